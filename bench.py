@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 group-quantized decode matvec path on one MI355X.
+
+A step is one pass over every call of the hot path, each on its own weights:
+  split4   x[4096] . W[6656, 4096]  -> 4096/1024/1024/512 routed outputs (gs 128)
+  gated    silu(x . Wg) * (x . Wu), Wg, Wu [14336, 4096]                (gs 128)
+  down     h[14336] . Wd[4096, 14336]  (h = the gated output)           (gs 128)
+  norm     RMSNorm(a_a + a_b) * w_norm . W[151936, 4096]  (LM head)     (gs 128)
+  lanes    X[M, 5120] . W[25600, 5120] for M = 1, 2, 4, 8, a weight copy each (gs 64)
+The step is captured once in a HIP graph and replayed; weights are re-read
+from HBM every step (a step streams ~0.8 GB, far beyond the 256 MB MALL).
+
+value = effective GB/s of the step = algorithmic bytes per step / time per step,
+where algorithmic bytes = packed codes N*K/2 + fp32 scales and zeros
+N*(K/gs)*8 + fp32 activations in + fp32 outputs out (what the method must move).
+
+Per-call durations: each call is also timed alone, in a graph of back-to-back
+calls cycling over >= 1 GiB of device copies of its buffers, with HIP events
+on the stream the kernels run on.  The norm LM head call is the dominant
+kernel; its roofline entry uses that measured duration.
+
+cpu_baseline: the CPU oracle (plain C, one thread) timed on a bounded sample
+of the same step (the first fraction f of every call's columns), converted to
+GB/s over the sampled algorithmic bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "int4 GEMV µs/call + effective HBM GB/s (% of MI355X peak), 1 GPU"
+PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MALL_ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "norm_lmhead_151936x4096_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "int4_group_quantized_quant_amd", "csrc", "kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(N, K, gs, in_floats, out_floats):
+    return N * K // 2 + N * (K // gs) * 8 + 4 * in_floats + 4 * out_floats
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the norm kernel from the committed rocprofv3 PMC
+    summary, or None when the summary is missing or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+# ---------------------------------------------------------------- workload
+
+class Call:
+    """One library call with its buffers and algorithmic bytes."""
+
+    def __init__(self, name, nbytes, fn, sets_fn, weight_bytes):
+        self.name = name
+        self.nbytes = nbytes
+        self.fn = fn            # fn(buffer_set) enqueues the call
+        self.sets_fn = sets_fn  # sets_fn(r) -> list of r buffer sets (device copies)
+        self.weight_bytes = weight_bytes
+
+
+def build_workload(q4, torch, dev):
+    c2, c3, c4, c5 = (synth.CONFIGS[k] for k in ("c2", "c3", "c4", "c5"))
+    calls = []
+    quant_times = []
+
+    def quantize(W, gs):
+        Wd = torch.from_numpy(W).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = q4.int4_quantize_pack(Wd, gs)
+        torch.cuda.synchronize()
+        quant_times.append((W.size, time.perf_counter() - t0))
+        del Wd
+        return out
+
+    def clones(tensors, r):
+        sets = [tuple(tensors)]
+        for _ in range(r - 1):
+            sets.append(tuple(t.clone() for t in tensors))
+        return sets
+
+    # split4
+    log("generating and quantizing split4 weights 6656x4096")
+    i2 = synth.c2_inputs()
+    w2 = quantize(i2["W"], c2["gs"])
+    x2 = torch.from_numpy(i2["x"]).to(dev)
+    outs2 = tuple(torch.empty(n, device=dev) for n in (4096, 1024, 1024, 512))
+    b2 = alg_bytes(c2["N"], c2["K"], c2["gs"], c2["K"], c2["N"])
+
+    def f2(s):
+        q4.int4_matvec_split4(s[0], s[1], s[2], s[3], c2["n0"], c2["n1"], c2["n2"], outs=outs2)
+    calls.append(Call("split4 6656x4096", b2, f2, lambda r: clones((x2, *w2), r),
+                      sum(t.numel() * 4 for t in w2)))
+
+    # gated + down
+    log("generating and quantizing gated MLP weights 2x14336x4096 and down 4096x14336")
+    i3 = synth.c3_inputs()
+    wg = quantize(i3["Wg"], c3["gs"])
+    wu = quantize(i3["Wu"], c3["gs"])
+    wd = quantize(i3["Wd"], c3["gs"])
+    x3 = torch.from_numpy(i3["x"]).to(dev)
+    h3 = torch.empty(c3["N"], device=dev)
+    y3 = torch.empty(c3["Nd"], device=dev)
+    b3g = 2 * alg_bytes(c3["N"], c3["K"], c3["gs"], 0, 0) + 4 * c3["K"] + 4 * c3["N"]
+    b3d = alg_bytes(c3["Nd"], c3["Kd"], c3["gs"], c3["Kd"], c3["Nd"])
+
+    def f3g(s):
+        q4.int4_matvec_gated(s[0], *s[1:7], h=s[7])
+
+    def f3d(s):
+        q4.int4_matvec(s[0], s[1], s[2], s[3], Y=s[4])
+    calls.append(Call("gated 2x14336x4096", b3g, f3g,
+                      lambda r: [(x3, *c[:6], h3) for c in clones((*wg, *wu), r)],
+                      sum(t.numel() * 4 for t in (*wg, *wu))))
+    calls.append(Call("down 4096x14336", b3d, f3d,
+                      lambda r: [(h3, *c, y3) for c in clones(wd, r)],
+                      sum(t.numel() * 4 for t in wd)))
+
+    # norm LM head
+    log("generating and quantizing the LM head 151936x4096 (the largest call)")
+    i4 = synth.c4_inputs()
+    w4 = quantize(i4["W"], c4["gs"])
+    del i4["W"]
+    a4 = [torch.from_numpy(i4[k]).to(dev) for k in ("a_a", "a_b", "w_norm")]
+    y4 = torch.empty(c4["N"], device=dev)
+    r4 = torch.empty(c4["K"], device=dev)
+    n4 = torch.empty(c4["K"], device=dev)
+    b4 = alg_bytes(c4["N"], c4["K"], c4["gs"], 3 * c4["K"], c4["N"] + 2 * c4["K"])
+
+    def f4(s):
+        q4.int4_matvec_norm(*a4, c4["eps"], s[0], s[1], s[2], y=y4, residual_out=r4, norm_out=n4)
+    calls.append(Call("norm LM head 151936x4096", b4, f4, lambda r: clones(w4, r),
+                      sum(t.numel() * 4 for t in w4)))
+
+    # lanes: one weight copy per M so no call re-reads another's weights from cache
+    log("generating and quantizing lane weights 25600x5120 gs=64")
+    i5 = synth.c5_inputs(8)
+    w5 = quantize(i5["W"], c5["gs"])
+    X5 = torch.from_numpy(i5["X"]).to(dev)
+    for M in c5["Ms"]:
+        wM = tuple(t.clone() for t in w5)
+        XM = X5[:M].contiguous()
+        YM = torch.empty((M, c5["N"]), device=dev)
+        bM = alg_bytes(c5["N"], c5["K"], c5["gs"], M * c5["K"], M * c5["N"])
+
+        def f5(s, YM=YM):
+            q4.int4_matvec(s[0], s[1], s[2], s[3], Y=YM)
+        calls.append(Call(f"lanes M={M} 25600x5120", bM, f5,
+                          lambda r, XM=XM, wM=wM: [(XM, *c) for c in clones(wM, r)],
+                          sum(t.numel() * 4 for t in wM)))
+    del w5
+    quant = {"elements": int(sum(n for n, _ in quant_times)),
+             "seconds": float(sum(t for _, t in quant_times))}
+    return calls, quant, {"y4": y4, "a4": a4, "w4": w4}
+
+
+# ---------------------------------------------------------------- timing
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager warm-up on the capture stream (device queries, attributes)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_call(torch, call, replays=6):
+    """Average duration of one call, from back-to-back calls over rotating copies."""
+    r = max(2, min(64, -(-MALL_ROTATE_BYTES // max(call.weight_bytes, 1))))
+    sets = call.sets_fn(r)
+    g = capture(torch, lambda: [call.fn(s) for s in sets])
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * r)
+    del g, sets
+    return us, r
+
+
+def cpu_baseline(calls_meta, budget_s=12.0):
+    """Time the oracle on the first fraction f of every call's columns."""
+    import oracle
+    c2, c3, c4, c5 = (synth.CONFIGS[k] for k in ("c2", "c3", "c4", "c5"))
+
+    def prep(frac):
+        items = []
+        W = synth.weights(0x202, max(1, int(c2["N"] * frac)), c2["K"])
+        items.append(("matvec", synth.normal_f32(0x201, c2["K"]), oracle.quantize_pack(W, 128),
+                      c2["K"], 128, 1))
+        for seed in (0x302, 0x303):
+            W = synth.weights(seed, max(1, int(c3["N"] * frac)), c3["K"])
+            items.append(("matvec", synth.normal_f32(0x301, c3["K"]), oracle.quantize_pack(W, 128),
+                          c3["K"], 128, 1))
+        W = synth.weights(0x304, max(1, int(c3["Nd"] * frac)), c3["Kd"])
+        items.append(("matvec", synth.normal_f32(0x30A, c3["Kd"]), oracle.quantize_pack(W, 128),
+                      c3["Kd"], 128, 1))
+        W = synth.weights(0x404, max(1, int(c4["N"] * frac)), c4["K"])
+        items.append(("norm", None, oracle.quantize_pack(W, 128), c4["K"], 128, 1))
+        W = synth.weights(0x502, max(1, int(c5["N"] * frac)), c5["K"])
+        w5 = oracle.quantize_pack(W, 64)
+        for M in c5["Ms"]:
+            items.append(("matvec", synth.lanes(0x501, M, c5["K"]), w5, c5["K"], 64, M))
+        return items
+
+    i4 = synth.c4_inputs(N=1)
+
+    def run(items):
+        nbytes = 0
+        t0 = time.perf_counter()
+        for kind, x, (q, s, z), K, gs, M in items:
+            N = q.shape[0]
+            if kind == "norm":
+                oracle.norm(i4["a_a"], i4["a_b"], i4["w_norm"], 1e-6, q, s, z, K, gs)
+                nbytes += alg_bytes(N, K, gs, 3 * K, N + 2 * K)
+            else:
+                oracle.matvec(x, q, s, z, K, gs)
+                nbytes += alg_bytes(N, K, gs, M * K, M * N)
+        return nbytes, time.perf_counter() - t0
+
+    probe = 0.002
+    nb, dt = run(prep(probe))
+    frac = min(1.0, probe * budget_s / max(dt, 1e-6))
+    log(f"cpu baseline: probe f={probe} took {dt:.2f}s, timing the oracle on f={frac:.4f}")
+    nb, dt = run(prep(frac))
+    return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"first {frac:.4f} of the columns of every call of the step "
+                       f"({nb / 1e6:.1f} MB algorithmic), one thread, plain C oracle with fp64 "
+                       f"dot products; {dt:.1f} s"),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (the JSON then carries cpu_baseline null)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the int4 matvec path here has no multi-GPU "
+              "mode (column sharding is described in DESIGN.md); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_group_quantized_quant_amd as q4
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '?')} CUs={props.multi_processor_count}")
+
+    calls, quant, keep = build_workload(q4, torch, dev)
+    step_bytes = sum(c.nbytes for c in calls)
+
+    # Per-call durations (rotating copies, graphs of back-to-back calls).
+    per_call = {}
+    for c in calls:
+        us, r = time_call(torch, c)
+        per_call[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
+                            "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
+                            "alg_bytes": c.nbytes, "rotating_copies": r}
+        log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
+            f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)")
+
+    # The step graph.
+    sets = [c.sets_fn(1)[0] for c in calls]
+    step = capture(torch, lambda: [c.fn(s) for c, s in zip(calls, sets)])
+    # Graph replays must reproduce the eager result bit for bit.
+    y_graph_ref = keep["y4"].clone()
+    for _ in range(args.warmup):
+        step.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(keep["y4"], y_graph_ref), "graph replay differs from the eager call"
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"step: {ms_per_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB, wall {wall:.3f}s")
+    assert torch.equal(keep["y4"], y_graph_ref), "graph replay differs from the eager call"
+
+    dom = per_call["norm LM head 151936x4096"]
+    traffic = read_traffic()
+    roofline = {"bound": "hbm", "achieved": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3, 1),
+                "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3 / PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "gemv_int4_kernel<1,4,kNorm> (int4_matvec_norm)",
+                "alg_bytes_per_launch": dom["alg_bytes"], "us_per_launch": dom["us_per_call"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(calls)
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": ("decode step: split4 6656x4096 + gated MLP 2x14336x4096 + "
+                                "down 4096x14336 + norm LM head 151936x4096 (gs 128) + "
+                                "lanes M=1,2,4,8 25600x5120 (gs 64)"),
+                   "alg_bytes_per_step": step_bytes, "pct_of_8TBps": round(100 * value / PEAK_GBS, 1),
+                   "weights": "int4 codes + fp32 scale/zero per group, N(0,0.02) seeded"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_call": per_call,
+        "quantize_pack": {"elements": quant["elements"], "seconds": round(quant["seconds"], 4),
+                          "GBps_fp32_in": round(4 * quant["elements"] / quant["seconds"] / 1e9, 1)},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "cus": props.multi_processor_count, "hip": torch.version.hip},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

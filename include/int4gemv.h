@@ -1,0 +1,145 @@
+/*
+ * int4gemv.h -- C ABI of the int4 group-quantized matrix-vector library for
+ * MI355X (gfx950).
+ *
+ * Sources (four gerbil diff pages; every entry point cites the passage that
+ * defines its operation):
+ *   [P1] gerbil 1.11.4 -> 1.13.0, page 9   (index type declarations: Executor docs)
+ *   [P2] gerbil 1.12.0 -> 1.13.0, page 8   (gpu module: Gepard backbone graph, addLinearOp)
+ *   [P3] gerbil 1.0.0-rc.9 -> 1.0.0, page 17 (gpu module: dequantizeMLXProjection)
+ *   [P4] gerbil 1.12.0 -> 1.13.0, page 12  (kernel registry: WGSL_QUAD_MATVEC_INT4,
+ *        WGSL_NORM_MATVEC_INT4 and their dispatch specs; Executor fusion passes)
+ *
+ * Quantized weight matrix with N output columns over K inputs, group size gs
+ * ([P2] addLinearOp: the {w}.q / {w}.scales / {w}.zeros triplet; [P4]
+ * fuseMambaFrontDecodeEntries doc: column-major, one column contiguous):
+ *   q      uint32 [N][K/8]   eight 4-bit codes per word; the code of input k of
+ *                            column n sits at bits 4*(k%8) of q[n*K/8 + k/8]
+ *                            (low nibble first: [P1]/[P3] dequantizeMLXProjection)
+ *   scales float  [N][K/gs]  scale of group g = k/gs of column n at [n*K/gs + g]
+ *   zeros  float  [N][K/gs]  zero point, an integer value in [0, 15]
+ *   w[n][k] = (code - zero) * scale            ([P4] WGSL_QUAD_MATVEC_INT4 dequant)
+ * Activations and outputs are fp32, row-major: X[m][k] at X[m*K + k],
+ * Y[m][n] at Y[m*N + n].
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller.  The library allocates nothing, keeps no pointer after
+ *     the call returns and holds no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; the call never synchronizes.  A kernel fault surfaces at
+ *     the caller's next synchronization.
+ *   - Shapes: K >= gs, K % gs == 0, gs % 32 == 0 (a 32-code, 16-byte load
+ *     never straddles a group).  N >= 0; N == 0 writes nothing (see norm).
+ *   - Alignment: q, X (and a_a, a_b, w_norm, W) must be 16-byte aligned;
+ *     scales, zeros and outputs 4-byte aligned.
+ *   - Outputs must not overlap any input or each other ([P4]
+ *     fuseNormMatVecDecodeEntries / fuseMambaFrontDecodeEntries alias rules).
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing is written and no kernel is launched.  int4_last_error()
+ *     returns a message for the last failed call on the calling thread.
+ *   - Calls are reentrant; concurrent calls on different streams are allowed.
+ */
+#ifndef INT4GEMV_H
+#define INT4GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum int4_status {
+    INT4_OK = 0,
+    INT4_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    INT4_ERR_SHAPE = 2,  /* K / gs / M / N outside the supported set            */
+    INT4_ERR_ALIGN = 3,  /* a pointer is not aligned as required                */
+    INT4_ERR_ALIAS = 4,  /* an output overlaps an input or another output       */
+    INT4_ERR_ARG = 5,    /* split points out of order, eps negative or not finite */
+    INT4_ERR_HIP = 6     /* the HIP runtime refused a query or a launch         */
+} int4_status;
+
+/* Static, human-readable name of a status code. */
+const char* int4_status_str(int status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* int4_last_error(void);
+
+/*
+ * Asymmetric per-group min/max quantization and packing of W (fp32 [N][K],
+ * row n = output column n).  The pages import the quantizer but do not show
+ * its body ([P4] module imports of quantizeInt4; [P1] quantizeKaniBackbone
+ * doc); the reading implemented, per group of gs inputs of one column, in
+ * IEEE binary32 with round-to-nearest-even and no flushing of subnormals:
+ *   scale = (max - min) / 15            (a constant group c != 0: |c| / 15)
+ *   zero  = clamp(rint(-min / scale), 0, 15)
+ *   code  = clamp(rint(w / scale) + zero, 0, 15)
+ * A group whose scale is 0 (all zero, or the range underflows) stores
+ * scale = 0, zero = +0 and codes 0.  Inputs must be finite.
+ * Outputs: q [N][K/8], scales [N][K/gs], zeros [N][K/gs].
+ */
+int int4_quantize_pack(const float* W, int64_t N, int64_t K, int32_t group_size,
+                       uint32_t* q, float* scales, float* zeros, void* stream);
+
+/*
+ * Y[m][n] = sum_k X[m][k] * w[n][k] for M decode lanes, 0 <= M <= 8
+ * (M == 0 writes nothing).  The weights are read from memory once per call
+ * for all lanes; lanes never interact ([P1] lockstep batch decode: linear
+ * layers run the batched INT4 GEMM; [P4] MATVEC_INT4 K-parallel matvec for
+ * the single-lane case).  M * K * 4 bytes must fit the device's per-block
+ * local data share (160 KiB on gfx950), else INT4_ERR_SHAPE.
+ */
+int int4_matvec(const float* X, int32_t M, const uint32_t* q, const float* scales,
+                const float* zeros, int64_t N, int64_t K, int32_t group_size,
+                float* Y, void* stream);
+
+/*
+ * One matvec over N column-concatenated outputs, routed into up to four
+ * buffers ([P4] WGSL_QUAD_MATVEC_INT4 routing, QUAD_MATVEC_INT4_SPEC params
+ * [K, N, gs, n0, n1, n2], fuseMambaFrontDecodeEntries doc):
+ *   column n -> out0[n] (n < n0), out1[n-n0] (n < n1), out2[n-n1] (n < n2),
+ *               out3[n-n2] otherwise.
+ * Requires 0 <= n0 <= n1 <= n2 <= N (else INT4_ERR_ARG).  out_j may be NULL
+ * only when its range is empty.  Per-column arithmetic is the same as
+ * int4_matvec's, so the routed values equal int4_matvec over the same
+ * concatenated matrix bit for bit.
+ */
+int int4_matvec_split4(const float* x, const uint32_t* q, const float* scales,
+                       const float* zeros, int64_t N, int64_t K, int32_t group_size,
+                       int64_t n0, int64_t n1, int64_t n2,
+                       float* out0, float* out1, float* out2, float* out3, void* stream);
+
+/*
+ * SiLU-gated gate/up matvec ([P1] fuseSwiGLUDecodeEntries: gate_proj +
+ * up_proj + SwiGLU in one dispatch; the activation is silu(gate) * up):
+ *   g[n] = x . w_gate[n],  u[n] = x . w_up[n],  h[n] = g / (1 + exp(-g)) * u.
+ * Both matrices share N, K and gs.  g and u are bit-identical to
+ * int4_matvec's outputs for the same weights.
+ */
+int int4_matvec_gated(const float* x,
+                      const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                      const uint32_t* q_up, const float* s_up, const float* z_up,
+                      int64_t N, int64_t K, int32_t group_size, float* h, void* stream);
+
+/*
+ * Residual-add + RMSNorm prefixed matvec ([P4] WGSL_NORM_MATVEC_INT4,
+ * NORM_MATVEC_INT4_SPEC with params [K, N, gs, eps]):
+ *   r[k]   = a_a[k] + a_b[k]                          (binary32)
+ *   inv    = 1 / sqrt(sum_k r[k]^2 / K + eps)
+ *   x[k]   = r[k] * inv * w_norm[k]
+ *   y[n]   = sum_k x[k] * w[n][k]
+ * residual_out (r) and norm_out (x) are optional (NULL = not written) and are
+ * written once per call.  eps must be finite and >= 0 (the pages default to
+ * 1e-6).  N == 0 still writes residual_out / norm_out when they are given.
+ * K * 4 bytes must fit the per-block local data share.
+ */
+int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, float eps,
+                     const uint32_t* q, const float* scales, const float* zeros,
+                     int64_t N, int64_t K, int32_t group_size,
+                     float* y, float* residual_out, float* norm_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT4GEMV_H */

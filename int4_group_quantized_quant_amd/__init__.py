@@ -1,0 +1,197 @@
+"""Python binding of libint4gemv.so, the int4 group-quantized matvec library
+for MI355X (gfx950).  The C ABI is declared in include/int4gemv.h.
+
+This module only marshals arguments: it checks dtypes, devices and
+contiguity of torch tensors, allocates outputs with torch when the caller
+passes none, and calls the C entry point of the same name on torch's current
+HIP stream.  Every step of the computation runs in the library's HIP kernels;
+there is no CPU or PyTorch fallback.  If the library has not been built, the
+import fails.
+
+Weight layout (as in the header): q uint32 (or int32 with the same bits)
+[N, K/8], scales / zeros float32 [N, K/gs]; activations and outputs float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Int4Error", "int4_quantize_pack", "int4_matvec", "int4_matvec_split4",
+    "int4_matvec_gated", "int4_matvec_norm", "lib", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+lib = ctypes.CDLL(LIB_PATH)
+lib.int4_status_str.argtypes = [ctypes.c_int]
+lib.int4_status_str.restype = ctypes.c_char_p
+lib.int4_last_error.argtypes = []
+lib.int4_last_error.restype = ctypes.c_char_p
+lib.int4_quantize_pack.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp]
+lib.int4_matvec.argtypes = [_vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_split4.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _i64, _i64,
+                                   _vp, _vp, _vp, _vp, _vp]
+lib.int4_matvec_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_norm.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i64, _i64, _i32,
+                                 _vp, _vp, _vp, _vp]
+for _fn in (lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
+            lib.int4_matvec_gated, lib.int4_matvec_norm):
+    _fn.restype = ctypes.c_int
+
+
+class Int4Error(RuntimeError):
+    """A library call returned a status other than INT4_OK."""
+
+    def __init__(self, status: int):
+        self.status = status
+        msg = lib.int4_last_error().decode() or lib.int4_status_str(status).decode()
+        super().__init__(msg)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Int4Error(status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_F32 = (torch.float32,)
+_CODES = (torch.int32, torch.uint32)
+
+
+def _weights(q, scales, zeros, tag=""):
+    _dev(q, "q" + tag, _CODES)
+    _dev(scales, "scales" + tag, _F32)
+    _dev(zeros, "zeros" + tag, _F32)
+    if q.dim() != 2 or scales.dim() != 2 or scales.shape != zeros.shape:
+        raise ValueError("q must be [N, K/8] and scales/zeros [N, K/gs]")
+    if scales.shape[0] != q.shape[0]:
+        raise ValueError("q and scales disagree on N")
+    N, K = q.shape[0], q.shape[1] * 8
+    G = scales.shape[1]
+    if G == 0 or K % G:
+        raise ValueError(f"K={K} is not a multiple of the group count {G}")
+    return N, K, K // G
+
+
+def int4_quantize_pack(W: torch.Tensor, group_size: int, q=None, scales=None, zeros=None,
+                       stream=None):
+    """W float32 [N, K] -> (q int32 [N, K/8], scales [N, K/gs], zeros [N, K/gs])."""
+    _dev(W, "W", _F32)
+    N, K = W.shape
+    G = K // group_size if group_size > 0 else 0
+    q = torch.empty((N, K // 8), dtype=torch.int32, device=W.device) if q is None else q
+    scales = torch.empty((N, G), dtype=torch.float32, device=W.device) if scales is None else scales
+    zeros = torch.empty((N, G), dtype=torch.float32, device=W.device) if zeros is None else zeros
+    _dev(q, "q", _CODES)
+    _dev(scales, "scales", _F32)
+    _dev(zeros, "zeros", _F32)
+    _check(lib.int4_quantize_pack(_ptr(W), N, K, group_size, _ptr(q), _ptr(scales), _ptr(zeros),
+                                  _stream(stream)))
+    return q, scales, zeros
+
+
+def int4_matvec(X: torch.Tensor, q, scales, zeros, Y=None, stream=None) -> torch.Tensor:
+    """X float32 [M, K] (or [K]) -> Y float32 [M, N] (or [N]); 0 <= M <= 8."""
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(X, "X", _F32)
+    squeeze = X.dim() == 1
+    M = 1 if squeeze else X.shape[0]
+    if X.shape[-1] != K:
+        raise ValueError(f"X has {X.shape[-1]} inputs, the weights {K}")
+    if Y is None:
+        Y = torch.empty((N,) if squeeze else (M, N), dtype=torch.float32, device=X.device)
+    _dev(Y, "Y", _F32)
+    _check(lib.int4_matvec(_ptr(X), M, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
+                           _stream(stream)))
+    return Y
+
+
+def int4_matvec_split4(x: torch.Tensor, q, scales, zeros, n0: int, n1: int, n2: int,
+                       outs=None, stream=None):
+    """One matvec over N columns routed to (out0[n0], out1[n1-n0], out2[n2-n1], out3[N-n2])."""
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(x, "x", _F32)
+    if outs is None:
+        sizes = [n0, n1 - n0, n2 - n1, N - n2]
+        outs = [torch.empty(max(sz, 0), dtype=torch.float32, device=x.device) for sz in sizes]
+    ptrs = []
+    for i, o in enumerate(outs):
+        if o is None:
+            ptrs.append(None)
+        else:
+            _dev(o, f"out{i}", _F32)
+            ptrs.append(_ptr(o) if o.numel() else None)
+    _check(lib.int4_matvec_split4(_ptr(x), _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs,
+                                  n0, n1, n2, *ptrs, _stream(stream)))
+    return tuple(outs)
+
+
+def int4_matvec_gated(x: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, h=None,
+                      stream=None) -> torch.Tensor:
+    """h[n] = silu(x . w_gate[n]) * (x . w_up[n])."""
+    N, K, gs = _weights(q_gate, s_gate, z_gate, "_gate")
+    N2, K2, gs2 = _weights(q_up, s_up, z_up, "_up")
+    if (N, K, gs) != (N2, K2, gs2):
+        raise ValueError("gate and up weights must share N, K and group size")
+    _dev(x, "x", _F32)
+    h = torch.empty(N, dtype=torch.float32, device=x.device) if h is None else h
+    _dev(h, "h", _F32)
+    _check(lib.int4_matvec_gated(_ptr(x), _ptr(q_gate), _ptr(s_gate), _ptr(z_gate), _ptr(q_up),
+                                 _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(h), _stream(stream)))
+    return h
+
+
+def int4_matvec_norm(a_a: torch.Tensor, a_b: torch.Tensor, w_norm: torch.Tensor, eps: float,
+                     q, scales, zeros, y=None, residual_out=None, norm_out=None,
+                     want_residual: bool = True, want_norm: bool = True, stream=None):
+    """y = (RMSNorm(a_a + a_b) * w_norm) . w  -> (y, residual_out or None, norm_out or None)."""
+    N, K, gs = _weights(q, scales, zeros)
+    for t, name in ((a_a, "a_a"), (a_b, "a_b"), (w_norm, "w_norm")):
+        _dev(t, name, _F32)
+    dev = a_a.device
+    y = torch.empty(N, dtype=torch.float32, device=dev) if y is None else y
+    if residual_out is None and want_residual:
+        residual_out = torch.empty(K, dtype=torch.float32, device=dev)
+    if norm_out is None and want_norm:
+        norm_out = torch.empty(K, dtype=torch.float32, device=dev)
+    for t, name in ((y, "y"), (residual_out, "residual_out"), (norm_out, "norm_out")):
+        if t is not None:
+            _dev(t, name, _F32)
+    _check(lib.int4_matvec_norm(_ptr(a_a), _ptr(a_b), _ptr(w_norm), float(eps), _ptr(q),
+                                _ptr(scales), _ptr(zeros), N, K, gs,
+                                _ptr(y) if N else None, _ptr(residual_out), _ptr(norm_out),
+                                _stream(stream)))
+    return y, residual_out, norm_out

@@ -1,0 +1,374 @@
+// abi.hip -- the extern "C" entry points declared in include/int4gemv.h:
+// argument validation (pure host logic, done before any HIP call), launch
+// geometry, and dispatch to the kernels in kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <array>
+#include <mutex>
+#include <string>
+
+#include "int4gemv.h"
+#include "internal.h"
+
+namespace int4gemv {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(int4_status_str(status)) + ": " + buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return INT4_OK;
+}
+
+// ------------------------------------------------------------------ checks
+
+struct Span {
+  const void* p;
+  uint64_t bytes;
+  const char* name;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  if (a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Outputs must not overlap any input or each other.
+int check_alias(const Span* ins, int n_in, const Span* outs, int n_out) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(outs[i], ins[j]))
+        return fail(INT4_ERR_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(INT4_ERR_ALIAS, "output %s overlaps output %s", outs[i].name, outs[j].name);
+  }
+  return INT4_OK;
+}
+
+int check_align(const void* p, unsigned align, const char* name) {
+  if (p != nullptr && ((uintptr_t)p % align) != 0)
+    return fail(INT4_ERR_ALIGN, "%s must be %u-byte aligned", name, align);
+  return INT4_OK;
+}
+
+#define RETURN_IF(expr)          \
+  do {                           \
+    int _st = (expr);            \
+    if (_st != INT4_OK) return _st; \
+  } while (0)
+
+// K, group size: the kernels read 32 codes (16 bytes) at a time and a group
+// must hold whole 16-byte units ([P4] WGSL_QUAD_MATVEC_INT4 reads vec4u units
+// and indexes groups per unit).
+int check_kgs(int64_t K, int32_t gs) {
+  if (gs < 32 || gs % 32 != 0)
+    return fail(INT4_ERR_SHAPE, "group_size must be a positive multiple of 32 (got %d)", (int)gs);
+  if (K < gs || K % gs != 0)
+    return fail(INT4_ERR_SHAPE, "K must be a positive multiple of group_size (K=%lld, gs=%d)",
+                (long long)K, (int)gs);
+  if (K > (int64_t)1 << 30)
+    return fail(INT4_ERR_SHAPE, "K=%lld is larger than supported", (long long)K);
+  return INT4_OK;
+}
+
+// ------------------------------------------------------------------ device
+
+struct DeviceInfo {
+  int cus = 0;
+  size_t lds_block = 0;
+  size_t lds_cu = 0;
+  bool valid = false;
+};
+
+std::mutex g_dev_mu;
+std::array<DeviceInfo, 64> g_dev;
+
+int device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= (int)g_dev.size()) return fail(INT4_ERR_HIP, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.valid) {
+    int cus = 0, lds_block = 0, lds_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return fail(INT4_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    d.cus = cus > 0 ? cus : 1;
+    d.lds_block = (size_t)lds_block;
+    d.lds_cu = lds_cu > 0 ? (size_t)lds_cu : (size_t)lds_block;
+    d.valid = true;
+  }
+  *out = d;
+  return INT4_OK;
+}
+
+// Launch geometry of the streaming matvec: 256-thread blocks, about 16 waves
+// per CU in total (enough 1 KiB loads in flight to cover HBM latency), and
+// every wave owning at least one group of `ncol` columns.
+int gemv_shape(Mode mode, int M, int64_t N, int64_t K, size_t lds_extra, LaunchShape* s) {
+  DeviceInfo dev;
+  RETURN_IF(device_info(&dev));
+  const int rows = mode == kPlain ? M : 1;
+  const size_t lds = (size_t)rows * (size_t)K * sizeof(float) + lds_extra;
+  if (lds > dev.lds_block)
+    return fail(INT4_ERR_SHAPE, "activations need %zu bytes of LDS per block; the device allows %zu",
+                lds, dev.lds_block);
+  const int64_t target_waves = (int64_t)dev.cus * 16;
+  int ncol = max_ncol(mode, M);
+  while (ncol > 1 && (N + ncol - 1) / ncol < target_waves) ncol /= 2;
+  const int waves_per_block = 4;
+  const int64_t groups = N > 0 ? (N + ncol - 1) / ncol : 0;
+  int64_t waves = groups < target_waves ? groups : target_waves;
+  if (waves < 1) waves = 1;
+  const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
+  s->ncol = ncol;
+  s->block_threads = waves_per_block * 64;
+  s->grid = (int)grid;
+  s->lds_bytes = lds;
+  s->lds_max = dev.lds_block;
+  return INT4_OK;
+}
+
+uint64_t group_magic(int32_t gs) {
+  const uint64_t d = (uint64_t)(gs / 32);
+  return (((uint64_t)1 << 40) + d - 1) / d;
+}
+
+void fill_common(GemvArgs& a, int64_t N, int64_t K, int32_t gs) {
+  a.N = N;
+  a.K = (int32_t)K;
+  a.U = (int32_t)(K / 32);
+  a.G = (int32_t)(K / gs);
+  a.nch = (a.U + 63) / 64;
+  a.g_magic = group_magic(gs);
+}
+
+int run(Mode mode, GemvArgs& a, const LaunchShape& s, void* stream) {
+  a.total_waves = (int64_t)s.grid * (s.block_threads / 64);
+  hipError_t e = launch_gemv(mode, a, s, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+}  // namespace int4gemv
+
+using namespace int4gemv;
+
+extern "C" {
+
+const char* int4_status_str(int status) {
+  switch (status) {
+    case INT4_OK: return "INT4_OK";
+    case INT4_ERR_NULL: return "INT4_ERR_NULL";
+    case INT4_ERR_SHAPE: return "INT4_ERR_SHAPE";
+    case INT4_ERR_ALIGN: return "INT4_ERR_ALIGN";
+    case INT4_ERR_ALIAS: return "INT4_ERR_ALIAS";
+    case INT4_ERR_ARG: return "INT4_ERR_ARG";
+    case INT4_ERR_HIP: return "INT4_ERR_HIP";
+    default: return "INT4_ERR_UNKNOWN";
+  }
+}
+
+const char* int4_last_error(void) { return g_last_error.c_str(); }
+
+int int4_quantize_pack(const float* W, int64_t N, int64_t K, int32_t group_size, uint32_t* q,
+                       float* scales, float* zeros, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0) return ok();
+  if (!W || !q || !scales || !zeros) return fail(INT4_ERR_NULL, "W, q, scales and zeros are required");
+  RETURN_IF(check_align(W, 16, "W"));
+  RETURN_IF(check_align(q, 4, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{W, (uint64_t)N * K * 4, "W"}};
+  const Span outs[] = {{q, (uint64_t)N * K / 2, "q"}, {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  RETURN_IF(check_alias(ins, 1, outs, 3));
+  hipError_t e = launch_quantize(W, (int64_t)G, group_size, q, scales, zeros, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int int4_matvec(const float* X, int32_t M, const uint32_t* q, const float* scales, const float* zeros,
+                int64_t N, int64_t K, int32_t group_size, float* Y, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  if (M < 0 || M > 8) return fail(INT4_ERR_SHAPE, "M must be in [0, 8] (got %d)", (int)M);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0 || M == 0) return ok();
+  if (!X || !q || !scales || !zeros || !Y)
+    return fail(INT4_ERR_NULL, "X, q, scales, zeros and Y are required");
+  RETURN_IF(check_align(X, 16, "X"));
+  RETURN_IF(check_align(q, 16, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(Y, 4, "Y"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{X, (uint64_t)M * K * 4, "X"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{Y, (uint64_t)M * N * 4, "Y"}};
+  RETURN_IF(check_alias(ins, 4, outs, 1));
+  LaunchShape s;
+  RETURN_IF(gemv_shape(kPlain, M, N, K, 0, &s));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = X;
+  a.M = M;
+  a.q[0] = reinterpret_cast<const uint4*>(q);
+  a.s[0] = scales;
+  a.z[0] = zeros;
+  a.out[0] = Y;
+  return run(kPlain, a, s, stream);
+}
+
+int int4_matvec_split4(const float* x, const uint32_t* q, const float* scales, const float* zeros,
+                       int64_t N, int64_t K, int32_t group_size, int64_t n0, int64_t n1, int64_t n2,
+                       float* out0, float* out1, float* out2, float* out3, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (!(0 <= n0 && n0 <= n1 && n1 <= n2 && n2 <= N))
+    return fail(INT4_ERR_ARG, "split points must satisfy 0 <= n0 <= n1 <= n2 <= N (%lld %lld %lld, N=%lld)",
+                (long long)n0, (long long)n1, (long long)n2, (long long)N);
+  if (N == 0) return ok();
+  const int64_t len[4] = {n0, n1 - n0, n2 - n1, N - n2};
+  float* outs_p[4] = {out0, out1, out2, out3};
+  if (!x || !q || !scales || !zeros) return fail(INT4_ERR_NULL, "x, q, scales and zeros are required");
+  for (int j = 0; j < 4; ++j)
+    if (len[j] > 0 && !outs_p[j])
+      return fail(INT4_ERR_NULL, "out%d is NULL but its range holds %lld columns", j, (long long)len[j]);
+  RETURN_IF(check_align(x, 16, "x"));
+  RETURN_IF(check_align(q, 16, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  static const char* names[4] = {"out0", "out1", "out2", "out3"};
+  for (int j = 0; j < 4; ++j) RETURN_IF(check_align(outs_p[j], 4, names[j]));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{x, (uint64_t)K * 4, "x"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{out0, (uint64_t)len[0] * 4, "out0"}, {out1, (uint64_t)len[1] * 4, "out1"},
+                       {out2, (uint64_t)len[2] * 4, "out2"}, {out3, (uint64_t)len[3] * 4, "out3"}};
+  RETURN_IF(check_alias(ins, 4, outs, 4));
+  LaunchShape s;
+  RETURN_IF(gemv_shape(kSplit4, 1, N, K, 0, &s));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = x;
+  a.M = 1;
+  a.q[0] = reinterpret_cast<const uint4*>(q);
+  a.s[0] = scales;
+  a.z[0] = zeros;
+  for (int j = 0; j < 4; ++j) a.out[j] = outs_p[j];
+  a.n0 = n0;
+  a.n1 = n1;
+  a.n2 = n2;
+  return run(kSplit4, a, s, stream);
+}
+
+int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                      const uint32_t* q_up, const float* s_up, const float* z_up, int64_t N, int64_t K,
+                      int32_t group_size, float* h, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0) return ok();
+  if (!x || !q_gate || !s_gate || !z_gate || !q_up || !s_up || !z_up || !h)
+    return fail(INT4_ERR_NULL, "x, both weight triplets and h are required");
+  RETURN_IF(check_align(x, 16, "x"));
+  RETURN_IF(check_align(q_gate, 16, "q_gate"));
+  RETURN_IF(check_align(q_up, 16, "q_up"));
+  RETURN_IF(check_align(s_gate, 4, "s_gate"));
+  RETURN_IF(check_align(z_gate, 4, "z_gate"));
+  RETURN_IF(check_align(s_up, 4, "s_up"));
+  RETURN_IF(check_align(z_up, 4, "z_up"));
+  RETURN_IF(check_align(h, 4, "h"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{x, (uint64_t)K * 4, "x"},
+                      {q_gate, (uint64_t)N * K / 2, "q_gate"}, {s_gate, G * 4, "s_gate"},
+                      {z_gate, G * 4, "z_gate"},
+                      {q_up, (uint64_t)N * K / 2, "q_up"}, {s_up, G * 4, "s_up"}, {z_up, G * 4, "z_up"}};
+  const Span outs[] = {{h, (uint64_t)N * 4, "h"}};
+  RETURN_IF(check_alias(ins, 7, outs, 1));
+  LaunchShape s;
+  RETURN_IF(gemv_shape(kGated, 1, N, K, 0, &s));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = x;
+  a.M = 1;
+  a.q[0] = reinterpret_cast<const uint4*>(q_gate);
+  a.s[0] = s_gate;
+  a.z[0] = z_gate;
+  a.q[1] = reinterpret_cast<const uint4*>(q_up);
+  a.s[1] = s_up;
+  a.z[1] = z_up;
+  a.out[0] = h;
+  return run(kGated, a, s, stream);
+}
+
+int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, float eps,
+                     const uint32_t* q, const float* scales, const float* zeros, int64_t N, int64_t K,
+                     int32_t group_size, float* y, float* residual_out, float* norm_out, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (!(isfinite(eps) && eps >= 0.0f)) return fail(INT4_ERR_ARG, "eps must be finite and >= 0");
+  if (N == 0 && !residual_out && !norm_out) return ok();
+  if (!a_a || !a_b || !w_norm) return fail(INT4_ERR_NULL, "a_a, a_b and w_norm are required");
+  if (N > 0 && (!q || !scales || !zeros || !y))
+    return fail(INT4_ERR_NULL, "q, scales, zeros and y are required when N > 0");
+  RETURN_IF(check_align(a_a, 16, "a_a"));
+  RETURN_IF(check_align(a_b, 16, "a_b"));
+  RETURN_IF(check_align(w_norm, 16, "w_norm"));
+  RETURN_IF(check_align(q, 16, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(y, 4, "y"));
+  RETURN_IF(check_align(residual_out, 16, "residual_out"));
+  RETURN_IF(check_align(norm_out, 16, "norm_out"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{a_a, (uint64_t)K * 4, "a_a"}, {a_b, (uint64_t)K * 4, "a_b"},
+                      {w_norm, (uint64_t)K * 4, "w_norm"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{y, (uint64_t)N * 4, "y"},
+                       {residual_out, residual_out ? (uint64_t)K * 4 : 0, "residual_out"},
+                       {norm_out, norm_out ? (uint64_t)K * 4 : 0, "norm_out"}};
+  RETURN_IF(check_alias(ins, 6, outs, 3));
+  LaunchShape s;
+  RETURN_IF(gemv_shape(kNorm, 1, N, K, 16 * sizeof(float), &s));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = a_a;
+  a.x2 = a_b;
+  a.w_norm = w_norm;
+  a.eps = eps;
+  a.M = 1;
+  a.q[0] = reinterpret_cast<const uint4*>(q);
+  a.s[0] = scales;
+  a.z[0] = zeros;
+  a.out[0] = y;
+  a.residual_out = residual_out;
+  a.norm_out = norm_out;
+  return run(kNorm, a, s, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// internal.h -- launch interface between the C ABI layer (abi.hip) and the
+// kernels (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace int4gemv {
+
+// Epilogue / prologue variant of the streaming matvec kernel.
+enum Mode : int {
+  kPlain = 0,   // Y[m][n] for M lanes
+  kSplit4 = 1,  // one lane, columns routed into four buffers
+  kGated = 2,   // one lane, two weight streams, h = silu(g) * u
+  kNorm = 3,    // one lane, residual-add + RMSNorm prologue
+};
+
+// Everything a matvec launch needs; passed by value as the kernel argument.
+struct GemvArgs {
+  const float* x;       // kPlain/kSplit4/kGated: X [M][K]; kNorm: a_a [K]
+  const float* x2;      // kNorm: a_b [K]
+  const float* w_norm;  // kNorm: RMSNorm gain [K]
+  float eps;            // kNorm
+  const uint4* q[2];    // packed codes per weight stream, 16-byte units [N][K/32]
+  const float* s[2];    // scales per stream [N][K/gs]
+  const float* z[2];    // zero points per stream [N][K/gs]
+  float* out[4];        // kPlain: out[0] = Y [M][N]; kSplit4: four routed buffers;
+                        // kGated: out[0] = h; kNorm: out[0] = y
+  float* residual_out;  // kNorm, nullable
+  float* norm_out;      // kNorm, nullable
+  int64_t N;            // output columns
+  int64_t n0, n1, n2;   // kSplit4 split points
+  int64_t total_waves;  // waves in the grid; wave w owns columns [w*N/W, (w+1)*N/W)
+  uint64_t g_magic;     // ceil(2^40 / (gs/32)): unit u lies in group (u*g_magic) >> 40
+  int32_t K;            // inputs per column
+  int32_t U;            // 16-byte units per column = K/32
+  int32_t G;            // groups per column = K/gs
+  int32_t nch;          // 64-unit chunks per column = ceil(U/64)
+  int32_t M;            // lanes (kPlain)
+};
+
+struct LaunchShape {
+  int ncol;           // columns per wave step (1, 2 or 4)
+  int block_threads;  // threads per block (multiple of 64)
+  int grid;           // blocks
+  size_t lds_bytes;   // dynamic LDS per block
+  size_t lds_max;     // device limit of dynamic LDS per block
+};
+
+// Launches the matvec kernel for `mode` / `a.M` with `shape`; returns the
+// launch status (hipGetLastError after the launch).
+hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& shape, hipStream_t stream);
+
+// Largest `ncol` instantiated for (mode, M).
+int max_ncol(Mode mode, int M);
+
+// Quantize + pack launch: groups [0, total_groups), each gs consecutive floats.
+hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,
+                           float* scales, float* zeros, hipStream_t stream);
+
+}  // namespace int4gemv

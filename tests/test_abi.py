@@ -1,0 +1,147 @@
+"""The C-ABI library loads, exports every entry point the header declares, and
+rejects invalid arguments before touching the GPU (CPU only: no call here
+reaches a kernel launch or a device query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int4gemv.h")
+LIB = os.path.join(ROOT, "int4_group_quantized_quant_amd", "libint4gemv.so")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from int4_group_quantized_quant_amd import _build
+        _build.build()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    import int4_group_quantized_quant_amd as pkg
+    return pkg.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(int4_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("int4_quantize_pack", "int4_matvec", "int4_matvec_split4", "int4_matvec_gated",
+              "int4_matvec_norm", "int4_status_str", "int4_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    _ensure_built()
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in int4gemv.h but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.int4_status_str(0) == b"INT4_OK"
+    assert lib.int4_status_str(4) == b"INT4_ERR_ALIAS"
+    assert lib.int4_status_str(99) == b"INT4_ERR_UNKNOWN"
+
+
+# Fake, never-dereferenced addresses: every call below fails validation.
+A = 0x10000000
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+F = 0x60000000
+
+
+def _err(lib):
+    return lib.int4_last_error().decode()
+
+
+def test_matvec_shape_errors(lib):
+    assert lib.int4_matvec(A, 1, B, C, D, 16, 256, 48, E, None) == SHAPE      # gs % 32
+    assert lib.int4_matvec(A, 1, B, C, D, 16, 256, 0, E, None) == SHAPE       # gs 0
+    assert lib.int4_matvec(A, 1, B, C, D, 16, 96, 64, E, None) == SHAPE       # K % gs
+    assert lib.int4_matvec(A, 1, B, C, D, 16, 32, 64, E, None) == SHAPE       # K < gs
+    assert lib.int4_matvec(A, 9, B, C, D, 16, 256, 64, E, None) == SHAPE      # M > 8
+    assert lib.int4_matvec(A, -1, B, C, D, 16, 256, 64, E, None) == SHAPE     # M < 0
+    assert lib.int4_matvec(A, 1, B, C, D, -1, 256, 64, E, None) == SHAPE      # N < 0
+    assert "group_size" in _err(lib) or "N must" in _err(lib)
+
+
+def test_empty_calls_are_no_ops(lib):
+    # N == 0 or M == 0: nothing to do; pointers are not needed.
+    assert lib.int4_matvec(None, 1, None, None, None, 0, 256, 64, None, None) == OK
+    assert lib.int4_matvec(None, 0, None, None, None, 16, 256, 64, None, None) == OK
+    assert lib.int4_quantize_pack(None, 0, 256, 64, None, None, None, None) == OK
+    assert lib.int4_matvec_split4(None, None, None, None, 0, 256, 64, 0, 0, 0,
+                                  None, None, None, None, None) == OK
+    assert lib.int4_matvec_gated(None, None, None, None, None, None, None, 0, 256, 64,
+                                 None, None) == OK
+    assert lib.int4_matvec_norm(None, None, None, ctypes.c_float(1e-6), None, None, None, 0,
+                                256, 64, None, None, None, None) == OK
+
+
+def test_null_errors(lib):
+    assert lib.int4_matvec(None, 1, B, C, D, 16, 256, 64, E, None) == NULL
+    assert lib.int4_matvec(A, 1, B, C, D, 16, 256, 64, None, None) == NULL
+    assert lib.int4_quantize_pack(A, 4, 256, 64, None, C, D, None) == NULL
+    assert lib.int4_matvec_gated(A, B, C, D, None, E, F, 16, 256, 64, A + 0x1000000, None) == NULL
+    assert lib.int4_matvec_norm(A, None, C, ctypes.c_float(1e-6), D, E, F, 4, 256, 64, B,
+                                None, None, None) == NULL
+
+
+def test_alignment_errors(lib):
+    assert lib.int4_matvec(A + 4, 1, B, C, D, 16, 256, 64, E, None) == ALIGN   # X 16B
+    assert lib.int4_matvec(A, 1, B + 8, C, D, 16, 256, 64, E, None) == ALIGN   # q 16B
+    assert lib.int4_matvec(A, 1, B, C + 2, D, 16, 256, 64, E, None) == ALIGN   # scales 4B
+    assert lib.int4_matvec(A, 1, B, C, D, 16, 256, 64, E + 1, None) == ALIGN   # Y 4B
+    assert lib.int4_quantize_pack(A + 4, 4, 256, 64, B, C, D, None) == ALIGN   # W 16B
+
+
+def test_alias_errors(lib):
+    N, K, gs = 16, 256, 64
+    # Y overlapping X / q / scales.
+    assert lib.int4_matvec(A, 1, B, C, D, N, K, gs, A + 16, None) == ALIAS
+    assert lib.int4_matvec(A, 1, B, C, D, N, K, gs, B + N * K // 2 - 4, None) == ALIAS
+    assert lib.int4_matvec(A, 1, B, C, D, N, K, gs, C, None) == ALIAS
+    # Adjacent but not overlapping is fine only if nothing else is wrong: here Y
+    # ends exactly where q starts, so this passes validation -- not called.
+    # split4 outputs overlapping each other.
+    assert lib.int4_matvec_split4(A, B, C, D, N, K, gs, 4, 8, 12, E, E + 8, F, F + 64,
+                                  None) == ALIAS
+    # norm outputs overlapping each other / an input.
+    assert lib.int4_matvec_norm(A, A + 0x10000, A + 0x20000, ctypes.c_float(1e-6), B, C, D, N,
+                                K, gs, E, E, None, None) == ALIAS
+    assert lib.int4_matvec_norm(A, A + 0x10000, A + 0x20000, ctypes.c_float(1e-6), B, C, D, N,
+                                K, gs, E, A + 0x10000, None, None) == ALIAS
+    # quantize outputs overlapping the input.
+    assert lib.int4_quantize_pack(A, N, K, gs, A + 256, C, D, None) == ALIAS
+    assert "overlaps" in _err(lib)
+
+
+def test_split4_argument_errors(lib):
+    N, K, gs = 16, 256, 64
+    assert lib.int4_matvec_split4(A, B, C, D, N, K, gs, 8, 4, 12, E, F, E + 0x1000, F + 0x1000,
+                                  None) == ARG
+    assert lib.int4_matvec_split4(A, B, C, D, N, K, gs, 4, 8, 17, E, F, E + 0x1000, F + 0x1000,
+                                  None) == ARG
+    assert lib.int4_matvec_split4(A, B, C, D, N, K, gs, -1, 8, 12, E, F, E + 0x1000, F + 0x1000,
+                                  None) == ARG
+    # A NULL output is allowed only for an empty range.
+    assert lib.int4_matvec_split4(A, B, C, D, N, K, gs, 4, 8, 12, E, None, E + 0x1000,
+                                  F + 0x1000, None) == NULL
+
+
+def test_norm_eps_errors(lib):
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert lib.int4_matvec_norm(A, A + 0x10000, A + 0x20000, ctypes.c_float(eps), B, C, D, 16,
+                                    256, 64, E, None, None, None) == ARG
