@@ -261,11 +261,16 @@ def cpu_baseline(calls_meta, budget_s=12.0):
     nb, dt = run(prep(probe))
     frac = min(1.0, probe * budget_s / max(dt, 1e-6))
     log(f"cpu baseline: probe f={probe} took {dt:.2f}s, timing the oracle on f={frac:.4f}")
-    nb, dt = run(prep(frac))
+    items = prep(frac)
+    nb, dt, passes = 0, 0.0, 0
+    # The whole step may take less than the budget: then time repeated passes.
+    while passes == 0 or (frac >= 1.0 and dt < budget_s):
+        b, t = run(items)
+        nb, dt, passes = nb + b, dt + t, passes + 1
     return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"first {frac:.4f} of the columns of every call of the step "
-                       f"({nb / 1e6:.1f} MB algorithmic), one thread, plain C oracle with fp64 "
-                       f"dot products; {dt:.1f} s"),
+            "sample": (f"first {frac:.4f} of the columns of every call of the step, "
+                       f"{passes} pass(es) ({nb / 1e6:.1f} MB algorithmic), one thread, plain C "
+                       f"oracle with fp64 dot products; {dt:.1f} s"),
             "seconds": dt}
 
 
@@ -332,7 +337,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3, 1),
                 "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3 / PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "gemv_int4_kernel<1,4,kNorm> (int4_matvec_norm)",
+                "traffic": traffic, "kernel": "gemv_reg_kernel<M=1,NCOL=4,kNorm,DEPTH=1> (int4_matvec_norm)",
                 "alg_bytes_per_launch": dom["alg_bytes"], "us_per_launch": dom["us_per_call"]}
 
     cpu = None

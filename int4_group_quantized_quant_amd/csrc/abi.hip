@@ -9,8 +9,10 @@
 #include <stdio.h>
 
 #include <array>
+#include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 
 #include "int4gemv.h"
 #include "internal.h"
@@ -124,30 +126,115 @@ int device_info(DeviceInfo* out) {
   return INT4_OK;
 }
 
-// Launch geometry of the streaming matvec: 256-thread blocks, about 16 waves
-// per CU in total (enough 1 KiB loads in flight to cover HBM latency), and
-// every wave owning at least one group of `ncol` columns.
-int gemv_shape(Mode mode, int M, int64_t N, int64_t K, size_t lds_extra, LaunchShape* s) {
+// Blocks per CU for one launch shape, cached: the occupancy query is host
+// work that would otherwise run on every call.
+int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bpc) {
+  struct Key {
+    int dev, mode, variant, M, ncol, depth, threads;
+    size_t lds;
+    bool operator<(const Key& o) const {
+      return std::tie(dev, mode, variant, M, ncol, depth, threads, lds) <
+             std::tie(o.dev, o.mode, o.variant, o.M, o.ncol, o.depth, o.threads, o.lds);
+    }
+  };
+  static std::mutex mu;
+  static std::map<Key, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const Key key{dev, (int)mode, s.variant, a.M, s.ncol, s.depth, s.block_threads, s.lds_bytes};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *bpc = it->second;
+      return INT4_OK;
+    }
+  }
+  int v = 0;
+  e = gemv_occupancy(mode, a, s, &v);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  if (v < 1)
+    return fail(INT4_ERR_SHAPE, "kernel does not fit on a CU (%d threads, %zu bytes of LDS)",
+                s.block_threads, s.lds_bytes);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = v;
+  *bpc = v;
+  return INT4_OK;
+}
+
+// Launch geometry.  Both kernels run persistent grids: as many blocks as are
+// resident on the device at once, so no block waits for a second round.
+//
+// Register kernel (M <= 2, K <= 32768): nch = ceil(K/2048) chunks of cw units,
+// P = 8/nch rows of nch waves per block (about 8 waves: two per SIMD, which
+// streams best), columns split evenly over the B*P rows, one LDS partial per
+// (column, stream, lane, chunk).
+//
+// LDS kernel (M >= 3 or larger K): 256-thread blocks, the M activation rows
+// staged in LDS (M*K*4 bytes), columns split evenly over the waves.
+int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   DeviceInfo dev;
   RETURN_IF(device_info(&dev));
+  const int M = a.M;
+  const int64_t N = a.N;
+  const int nstream = mode == kGated ? 2 : 1;
+  s->lds_max = dev.lds_block;
+  if (M <= 2 && a.nch <= 16) {
+    const int nch = a.nch;
+    const int P = nch >= 8 ? 1 : 8 / nch;
+    a.rows_per_block = P;
+    s->variant = kVariantReg;
+    s->depth = 1;
+    s->block_threads = 64 * P * nch;
+    auto table = [&](int64_t blocks) {
+      return (int64_t)((N + blocks - 1) / blocks) * nstream * M * nch;
+    };
+    int ncol = max_ncol(mode, M, kVariantReg);
+    while (ncol > 1 && N / ((int64_t)dev.cus * P) < ncol) ncol /= 2;
+    s->ncol = ncol;
+    int64_t B = dev.cus;
+    s->lds_bytes = (size_t)(table(B) + 16) * sizeof(float);
+    if (s->lds_bytes > dev.lds_block)
+      return fail(INT4_ERR_SHAPE, "N=%lld needs %zu bytes of LDS per block for partial sums",
+                  (long long)N, s->lds_bytes);
+    int bpc = 1;
+    RETURN_IF(cached_occupancy(mode, a, *s, &bpc));
+    // One block of about 8 waves per CU; more resident waves per CU only
+    // add contention for the memory pipeline.
+    const int waves_per_block = P * nch;
+    if (bpc > 1 && waves_per_block * bpc > 8) bpc = waves_per_block >= 8 ? 1 : 8 / waves_per_block;
+    B = (int64_t)dev.cus * bpc;
+    const int64_t max_blocks = (N + P - 1) / P;  // at least one column per row
+    if (B > max_blocks) B = max_blocks;
+    if (B < 1) B = 1;
+    while (s->ncol > 1 && N / (B * P) < s->ncol) s->ncol /= 2;
+    a.part_floats = (int32_t)table(B);
+    s->lds_bytes = (size_t)(a.part_floats + 16) * sizeof(float);
+    s->grid = (int)B;
+    a.total_waves = B * P * nch;
+    return INT4_OK;
+  }
   const int rows = mode == kPlain ? M : 1;
-  const size_t lds = (size_t)rows * (size_t)K * sizeof(float) + lds_extra;
+  const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode == kNorm ? 64 : 0);
   if (lds > dev.lds_block)
     return fail(INT4_ERR_SHAPE, "activations need %zu bytes of LDS per block; the device allows %zu",
                 lds, dev.lds_block);
-  const int64_t target_waves = (int64_t)dev.cus * 16;
-  int ncol = max_ncol(mode, M);
-  while (ncol > 1 && (N + ncol - 1) / ncol < target_waves) ncol /= 2;
-  const int waves_per_block = 4;
-  const int64_t groups = N > 0 ? (N + ncol - 1) / ncol : 0;
-  int64_t waves = groups < target_waves ? groups : target_waves;
-  if (waves < 1) waves = 1;
-  const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
-  s->ncol = ncol;
-  s->block_threads = waves_per_block * 64;
-  s->grid = (int)grid;
+  s->variant = kVariantLds;
+  s->block_threads = 256;
   s->lds_bytes = lds;
-  s->lds_max = dev.lds_block;
+  int ncol = max_ncol(mode, M, kVariantLds);
+  const int64_t target_waves = (int64_t)dev.cus * 16;
+  while (ncol > 1 && (N + ncol - 1) / ncol < target_waves) ncol /= 2;
+  s->ncol = ncol;
+  int bpc = 1;
+  RETURN_IF(cached_occupancy(mode, a, *s, &bpc));
+  const int64_t groups = (N + ncol - 1) / ncol;
+  int64_t waves = (int64_t)dev.cus * bpc * 4;
+  if (waves > groups) waves = groups;
+  if (waves < 1) waves = 1;
+  s->grid = (int)((waves + 3) / 4);
+  a.total_waves = (int64_t)s->grid * 4;
   return INT4_OK;
 }
 
@@ -162,11 +249,13 @@ void fill_common(GemvArgs& a, int64_t N, int64_t K, int32_t gs) {
   a.U = (int32_t)(K / 32);
   a.G = (int32_t)(K / gs);
   a.nch = (a.U + 63) / 64;
+  a.cw = (a.U + a.nch - 1) / a.nch;
   a.g_magic = group_magic(gs);
 }
 
-int run(Mode mode, GemvArgs& a, const LaunchShape& s, void* stream) {
-  a.total_waves = (int64_t)s.grid * (s.block_threads / 64);
+int run(Mode mode, GemvArgs& a, void* stream) {
+  LaunchShape s{};
+  RETURN_IF(plan(mode, a, &s));
   hipError_t e = launch_gemv(mode, a, s, (hipStream_t)stream);
   if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
@@ -231,8 +320,6 @@ int int4_matvec(const float* X, int32_t M, const uint32_t* q, const float* scale
                       {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
   const Span outs[] = {{Y, (uint64_t)M * N * 4, "Y"}};
   RETURN_IF(check_alias(ins, 4, outs, 1));
-  LaunchShape s;
-  RETURN_IF(gemv_shape(kPlain, M, N, K, 0, &s));
   GemvArgs a{};
   fill_common(a, N, K, group_size);
   a.x = X;
@@ -241,7 +328,7 @@ int int4_matvec(const float* X, int32_t M, const uint32_t* q, const float* scale
   a.s[0] = scales;
   a.z[0] = zeros;
   a.out[0] = Y;
-  return run(kPlain, a, s, stream);
+  return run(kPlain, a, stream);
 }
 
 int int4_matvec_split4(const float* x, const uint32_t* q, const float* scales, const float* zeros,
@@ -271,8 +358,6 @@ int int4_matvec_split4(const float* x, const uint32_t* q, const float* scales, c
   const Span outs[] = {{out0, (uint64_t)len[0] * 4, "out0"}, {out1, (uint64_t)len[1] * 4, "out1"},
                        {out2, (uint64_t)len[2] * 4, "out2"}, {out3, (uint64_t)len[3] * 4, "out3"}};
   RETURN_IF(check_alias(ins, 4, outs, 4));
-  LaunchShape s;
-  RETURN_IF(gemv_shape(kSplit4, 1, N, K, 0, &s));
   GemvArgs a{};
   fill_common(a, N, K, group_size);
   a.x = x;
@@ -284,7 +369,7 @@ int int4_matvec_split4(const float* x, const uint32_t* q, const float* scales, c
   a.n0 = n0;
   a.n1 = n1;
   a.n2 = n2;
-  return run(kSplit4, a, s, stream);
+  return run(kSplit4, a, stream);
 }
 
 int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gate, const float* z_gate,
@@ -310,8 +395,6 @@ int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gat
                       {q_up, (uint64_t)N * K / 2, "q_up"}, {s_up, G * 4, "s_up"}, {z_up, G * 4, "z_up"}};
   const Span outs[] = {{h, (uint64_t)N * 4, "h"}};
   RETURN_IF(check_alias(ins, 7, outs, 1));
-  LaunchShape s;
-  RETURN_IF(gemv_shape(kGated, 1, N, K, 0, &s));
   GemvArgs a{};
   fill_common(a, N, K, group_size);
   a.x = x;
@@ -323,7 +406,7 @@ int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gat
   a.s[1] = s_up;
   a.z[1] = z_up;
   a.out[0] = h;
-  return run(kGated, a, s, stream);
+  return run(kGated, a, stream);
 }
 
 int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, float eps,
@@ -353,8 +436,6 @@ int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, fl
                        {residual_out, residual_out ? (uint64_t)K * 4 : 0, "residual_out"},
                        {norm_out, norm_out ? (uint64_t)K * 4 : 0, "norm_out"}};
   RETURN_IF(check_alias(ins, 6, outs, 3));
-  LaunchShape s;
-  RETURN_IF(gemv_shape(kNorm, 1, N, K, 16 * sizeof(float), &s));
   GemvArgs a{};
   fill_common(a, N, K, group_size);
   a.x = a_a;
@@ -368,7 +449,7 @@ int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, fl
   a.out[0] = y;
   a.residual_out = residual_out;
   a.norm_out = norm_out;
-  return run(kNorm, a, s, stream);
+  return run(kNorm, a, stream);
 }
 
 }  // extern "C"

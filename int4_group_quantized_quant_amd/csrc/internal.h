@@ -35,24 +35,37 @@ struct GemvArgs {
   int32_t K;            // inputs per column
   int32_t U;            // 16-byte units per column = K/32
   int32_t G;            // groups per column = K/gs
-  int32_t nch;          // 64-unit chunks per column = ceil(U/64)
+  int32_t nch;          // chunks per column = ceil(U/64)
+  int32_t cw;           // units per chunk = ceil(U/nch) (register kernel)
+  int32_t rows_per_block;  // P: rows of nch waves per block (register kernel)
+  int32_t part_floats;  // floats of the per-block partial table (register kernel)
   int32_t M;            // lanes (kPlain)
 };
 
+enum Variant : int {
+  kVariantLds = 0,  // activations staged in LDS, one wave per column group
+  kVariantReg = 1,  // activations in registers, one wave per (row, K chunk)
+};
+
 struct LaunchShape {
+  int variant;        // Variant
   int ncol;           // columns per wave step (1, 2 or 4)
+  int depth;          // register kernel: steps of loads in flight ahead of compute (1 or 2)
   int block_threads;  // threads per block (multiple of 64)
   int grid;           // blocks
   size_t lds_bytes;   // dynamic LDS per block
   size_t lds_max;     // device limit of dynamic LDS per block
 };
 
-// Launches the matvec kernel for `mode` / `a.M` with `shape`; returns the
-// launch status (hipGetLastError after the launch).
+// Launches the matvec kernel for `mode` / `a.M` / `shape`; returns the launch
+// status (hipGetLastError after the launch).
 hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& shape, hipStream_t stream);
 
-// Largest `ncol` instantiated for (mode, M).
-int max_ncol(Mode mode, int M);
+// Resident blocks per CU of the kernel `launch_gemv` would run for this shape.
+hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& shape, int* blocks_per_cu);
+
+// Largest `ncol` instantiated for (mode, M, variant).
+int max_ncol(Mode mode, int M, int variant);
 
 // Quantize + pack launch: groups [0, total_groups), each gs consecutive floats.
 hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,

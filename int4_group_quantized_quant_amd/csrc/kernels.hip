@@ -5,28 +5,44 @@
 // WGSL_NORM_MATVEC_INT4: layout, dequant (code - zero) * scale, routing, norm
 // prologue); [P1] gerbil 1.11.4 -> 1.13.0, page 9 (SwiGLU fusion, batched INT4
 // GEMM for decode lanes).  The WGSL kernels give 16 lanes per column with a
-// shared-memory lane sum; the design here is CDNA-native instead:
+// shared-memory lane sum; the design here is CDNA-native instead.
 //
-//  * A column's K/32 sixteen-byte units are spread over the 64 lanes of a wave
-//    (lane l takes units l, l+64, ...), so every global_load_dwordx4 of a wave
-//    is one contiguous 1 KiB piece of one column.  A wave walks a contiguous
-//    range of columns NCOL at a time and prefetches the next step's units
-//    while it computes the current one.
-//  * The activation vector(s) are staged once per block into LDS, transposed
-//    so that lane l reads unit l's 32 inputs with conflict-free ds_read_b128.
-//  * Dequant-dot without zero-point folding and without int->float converts:
-//    a nibble masked into the low bits of an fp16 half is the subnormal
-//    code * 2^-24 (exactly); v_pk_add_f16 subtracts zero * 2^-24 exactly,
-//    and v_fma_mix_f32 multiplies the fp32 activation by that fp16 (q - zero).
-//    Odd inputs use the nibble 4 bits higher (value 16 * code * 2^-24), so
-//    their activations are pre-scaled by 2^-4 in LDS.  One unit costs 1 shift,
-//    16 AND, 16 packed-f16 subtractions and 32 mixed FMAs per 32 weights.
-//    Each unit's sum is rescaled by 2^24 and multiplied by its group's scale.
-//  * Cross-lane sums use DPP (quad perms, row mirrors, row broadcasts) in a
-//    fixed order, so a column's result depends only on K, its weights and x:
-//    split-4 routing, the gated streams and every lane count give the same
-//    bits as the plain matvec over the same column.
-//  * No MFMA: at one to eight lanes the work is a bandwidth-bound stream.
+// Shared by both matvec kernels:
+//  * A column's K/32 sixteen-byte code units are spread over the 64 lanes of
+//    a wave, so a wave's global_load_dwordx4 is one contiguous piece of one
+//    column (up to 1 KiB).  Loads of the next step are issued before the
+//    current step is computed.
+//  * Exact dequant-dot with no zero-point folding and no int->float
+//    converts: a nibble masked into the low bits of an fp16 half is the
+//    subnormal code * 2^-24; v_pk_add_f16 subtracts zero * 2^-24 exactly;
+//    v_fma_mix_f32 multiplies the fp32 activation by that fp16 (code - zero).
+//    Odd inputs use the nibble 4 bits higher (16 * code * 2^-24).  The
+//    activations are pre-scaled by 2^24 (even inputs) and 2^20 (odd inputs),
+//    exact power-of-two scalings, so a unit's sum is sum x * (code - zero)
+//    and only needs its group's scale.  Per 32 weights: 1 shift, 16 AND, 16
+//    packed-f16 subtractions, 32 mixed FMAs.
+//  * Cross-lane sums are butterflies in the fixed order xor 32, xor 16 (lane
+//    swaps across wave halves / row pairs), then xor 8, 4, 2, 1 (DPP row
+//    rotations).  Several values are reduced at once by pairing them in the
+//    swap steps; every value still sees exactly the single-value tree.
+//
+// gemv_reg_kernel (one or two lanes): K is cut into nch chunks of at most 64
+// units.  A block holds P rows of nch waves; wave (p, c) owns chunk c of the
+// columns of row p, keeps the activations of its chunk in registers for the
+// whole kernel (no LDS staging), streams its columns NCOL at a time with the
+// loads DEPTH steps ahead, and writes one partial per (column, chunk) to an
+// LDS table.  After one barrier the block sums each column's partials
+// in chunk order and runs the epilogue (routing, SiLU gate, plain store).
+// Blocks are persistent: as many as fit on the device at once.
+//
+// gemv_lds_kernel (three to eight lanes): the activation rows are staged in
+// LDS, transposed so lane l reads unit l's inputs with conflict-free
+// ds_read_b128; each wave walks whole columns chunk by chunk (the register
+// kernel's nch chunks of cw units), reducing every chunk across the wave and
+// summing the chunk totals in chunk order -- the register kernel's order, so
+// every lane count gives the same bits.
+//
+// No MFMA: at one to eight lanes the work is a bandwidth-bound stream.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -42,109 +58,119 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxBlockThreads = 256;
-constexpr float kTwo24 = 16777216.0f;  // undoes the 2^-24 of the fp16 subnormal codes
+constexpr float kEvenScale = 16777216.0f;  // 2^24: undoes the 2^-24 of even-input codes
+constexpr float kOddScale = 1048576.0f;    // 2^20: undoes the 2^-20 of odd-input codes
 
 __device__ __forceinline__ half2_t as_half2(uint32_t b) { return __builtin_bit_cast(half2_t, b); }
-
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A wave-uniform 64-bit value moved to scalar registers (the 64-bit division
+// that produces row bounds runs on the vector unit).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
-// Lane-shuffled copy of v through DPP; lanes in rows outside ROW_MASK read 0.
-template <int CTRL, int ROW_MASK>
+// ------------------------------------------------------------ reductions
+
+// DPP move within 16-lane rows (row_ror:N = 0x120 + N).
+template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+  return bitsf(__builtin_amdgcn_update_dpp(0u, fbits(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 64 lanes of a wave, returned as a wave-uniform value.  The
-// order of the additions is fixed: pairs, quads, half rows, rows (all DPP
-// within a 16-lane row), then row 0+1 and 2+3 via row_bcast15, then the two
-// halves via row_bcast31; lane 63 ends with the total.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_move<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v += dpp_move<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v += dpp_move<0x141, 0xF>(v);  // row_half_mirror
-  v += dpp_move<0x140, 0xF>(v);  // row_mirror
-  v += dpp_move<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_move<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
-// ------------------------------------------------------------ LDS staging
-
-// The activation row of lane m is stored as float4 xl[m][j][u] = inputs
-// 32u + 4j .. 32u + 4j + 3, with every odd input multiplied by 2^-4 (exact).
-__device__ __forceinline__ float4 lds_scale_odd(float4 v) {
-  v.y *= 0.0625f;
-  v.w *= 0.0625f;
+// Levels xor 8, 4, 2, 1 inside each row.  row_ror by 2^j pairs lane i with a
+// lane that differs from i ^ 2^j only in higher bits, whose value the
+// previous levels already made equal.
+__device__ __forceinline__ float row_allreduce(float v) {
+  v += dpp_move<0x128>(v);
+  v += dpp_move<0x124>(v);
+  v += dpp_move<0x122>(v);
+  v += dpp_move<0x121>(v);
   return v;
 }
 
-template <int M>
-__device__ __forceinline__ void stage_x(const float* __restrict__ X, int K, int U, float4* xl) {
-  const int n4 = K >> 2;
-  for (int m = 0; m < M; ++m) {
-    const float4* src = reinterpret_cast<const float4*>(X + (size_t)m * K);
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-      const float4 v = src[i];
-      xl[(m * 8 + (i & 7)) * U + (i >> 3)] = lds_scale_odd(v);
+// Level xor 32 for two values: lower half of the result = a[l] + a[l+32],
+// upper half = b[l-32] + b[l].
+__device__ __forceinline__ float add_swap32(float a, float b) {
+  auto r = __builtin_amdgcn_permlane32_swap(fbits(a), fbits(b), false, false);
+  return bitsf(r[0]) + bitsf(r[1]);
+}
+
+// Level xor 16 for two values: rows of the result = a0+a1, b0+b1, a2+a3, b2+b3.
+__device__ __forceinline__ float add_swap16(float a, float b) {
+  auto r = __builtin_amdgcn_permlane16_swap(fbits(a), fbits(b), false, false);
+  return bitsf(r[0]) + bitsf(r[1]);
+}
+
+// All-reduce of V values (V = 1, 2, 4 or 8).  Register j of z holds, in every
+// lane of row r, the total of value reduced_index<V>(j, r).
+template <int V>
+__device__ __forceinline__ void wave_reduce(const float (&v)[V], float (&z)[(V + 3) / 4]) {
+  static_assert(V == 1 || V == 2 || V == 4 || V == 8, "V must be 1, 2, 4 or 8");
+  if constexpr (V == 1) {
+    const float w = add_swap32(v[0], v[0]);
+    z[0] = row_allreduce(add_swap16(w, w));
+  } else if constexpr (V == 2) {
+    const float w = add_swap32(v[0], v[1]);
+    z[0] = row_allreduce(add_swap16(w, w));
+  } else {
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const float w0 = add_swap32(v[4 * j + 0], v[4 * j + 1]);
+      const float w1 = add_swap32(v[4 * j + 2], v[4 * j + 3]);
+      z[j] = row_allreduce(add_swap16(w0, w1));
     }
   }
 }
 
-// Residual add + RMSNorm prologue ([P4] WGSL_NORM_MATVEC_INT4): every block
-// computes the same inv_rms in the same order; block 0 writes residual_out
-// and norm_out.  `red` is LDS scratch of one float per wave.
-__device__ __forceinline__ void stage_norm(const GemvArgs& a, float4* xl, float* red) {
-  const int n4 = a.K >> 2;
-  const int U = a.U;
-  const float4* aa = reinterpret_cast<const float4*>(a.x);
-  const float4* ab = reinterpret_cast<const float4*>(a.x2);
-  const float4* wn = reinterpret_cast<const float4*>(a.w_norm);
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-    const float4 x1 = aa[i];
-    const float4 x2 = ab[i];
-    float4 r;
-    r.x = x1.x + x2.x;
-    r.y = x1.y + x2.y;
-    r.z = x1.z + x2.z;
-    r.w = x1.w + x2.w;
-    ss = fmaf(r.x, r.x, ss);
-    ss = fmaf(r.y, r.y, ss);
-    ss = fmaf(r.z, r.z, ss);
-    ss = fmaf(r.w, r.w, ss);
-    xl[(i & 7) * U + (i >> 3)] = r;  // unscaled residual for the second pass
-  }
-  const float wsum = wave_sum(ss);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = wsum;
-  __syncthreads();
-  float total = red[0];
-  const int nw = blockDim.x >> 6;
-  for (int w = 1; w < nw; ++w) total += red[w];
-  const float inv_rms = 1.0f / sqrtf(total / (float)a.K + a.eps);
-  const bool writer = blockIdx.x == 0;
-  float4* res_out = reinterpret_cast<float4*>(a.residual_out);
-  float4* nrm_out = reinterpret_cast<float4*>(a.norm_out);
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-    const int idx = (i & 7) * U + (i >> 3);
-    const float4 r = xl[idx];
-    const float4 g = wn[i];
-    float4 x;
-    x.x = r.x * inv_rms * g.x;
-    x.y = r.y * inv_rms * g.y;
-    x.z = r.z * inv_rms * g.z;
-    x.w = r.w * inv_rms * g.w;
-    if (writer) {
-      if (res_out) res_out[i] = r;
-      if (nrm_out) nrm_out[i] = x;
-    }
-    xl[idx] = lds_scale_odd(x);
-  }
+template <int V>
+__device__ __forceinline__ int reduced_index(int j, int row) {
+  if constexpr (V == 1) return 0;
+  if constexpr (V == 2) return row >> 1;
+  return 4 * j + (((row & 1) << 1) | (row >> 1));
 }
 
-// ------------------------------------------------------------ streaming core
+// Total over the wave, wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  const float one[1] = {v};
+  float z[1];
+  wave_reduce<1>(one, z);
+  return bitsf(__builtin_amdgcn_readfirstlane(fbits(z[0])));
+}
+
+// Wave-uniform totals of V values (any V): batches of 4, then 2, then 1, each
+// value reduced with the single-value butterfly tree.
+template <int V>
+__device__ __forceinline__ void wave_totals(const float (&v)[V], float (&t)[V]) {
+  auto lane_value = [](float z, int l) {
+    return bitsf(__builtin_amdgcn_readlane(fbits(z), l));
+  };
+#pragma unroll
+  for (int i = 0; i + 4 <= V; i += 4) {
+    const float b[4] = {v[i], v[i + 1], v[i + 2], v[i + 3]};
+    float z[1];
+    wave_reduce<4>(b, z);
+    t[i + 0] = lane_value(z[0], 0);
+    t[i + 2] = lane_value(z[0], 16);
+    t[i + 1] = lane_value(z[0], 32);
+    t[i + 3] = lane_value(z[0], 48);
+  }
+  constexpr int r = V % 4;
+  constexpr int i0 = V - r;
+  if constexpr (r >= 2) {
+    const float b[2] = {v[i0], v[i0 + 1]};
+    float z[1];
+    wave_reduce<2>(b, z);
+    t[i0] = lane_value(z[0], 0);
+    t[i0 + 1] = lane_value(z[0], 32);
+  }
+  if constexpr (r == 1 || r == 3) t[V - 1] = wave_sum(v[V - 1]);
+}
+
+// ------------------------------------------------------------ dequant-dot
 
 template <int NSLOT>
 struct Step {
@@ -153,52 +179,31 @@ struct Step {
   float z[NSLOT];
 };
 
-// Issue the loads of step (n, ch): for each slot, unit ch*64 + lane of column
-// n + slot/NSTREAM in weight stream slot%NSTREAM, with its scale and zero.
-template <int NCOL, int NSTREAM>
-__device__ __forceinline__ void load_step(const GemvArgs& a, int64_t n, int ch, int64_t c_end,
-                                          int lane, Step<NCOL * NSTREAM>& r) {
-  const int u = ch * kWave + lane;
-  const bool active = u < a.U;
-  const int g = (int)(((uint64_t)u * a.g_magic) >> 40);
-#pragma unroll
-  for (int c = 0; c < NCOL * NSTREAM; ++c) {
-    const int st = c % NSTREAM;
-    const int64_t col = n + c / NSTREAM;
-    if (col < c_end && active) {
-      r.q[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.q[st]) + col * a.U + u);
-      r.s[c] = a.s[st][col * a.G + g];
-      r.z[c] = a.z[st][col * a.G + g];
-    } else {
-      r.q[c] = u32x4{0u, 0u, 0u, 0u};
-      r.s[c] = 0.0f;
-      r.z[c] = 0.0f;
-    }
-  }
-}
-
-// (code - zero) for the 32 inputs of one unit as 16 fp16 pairs, scaled by
-// 2^-24 (even inputs) or 2^-20 (odd inputs).  Pair 4i+t holds inputs
-// 8i+t' and 8i+t'+4 with t' = (0, 1, 2, 3)[t].
-__device__ __forceinline__ void unit_codes(u32x4 w, float zero, half2_t (&d)[16]) {
-  const uint32_t zi = (uint32_t)zero;
-  const uint32_t zlo_bits = zi | (zi << 16);
-  const half2_t zlo = as_half2(zlo_bits);
-  const half2_t zhi = as_half2(zlo_bits << 4);
+// The codes of the 32 inputs of one unit as 16 fp16 pairs, scaled by 2^-24
+// (even inputs) or 2^-20 (odd inputs): each nibble is masked in place into
+// the mantissa of a subnormal half, so the value is exact with no
+// conversion.  Pair 4i+t holds inputs 8i+t and 8i+t+4.
+__device__ __forceinline__ void unit_codes(u32x4 w, half2_t (&d)[16]) {
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t lo = words[i];
     const uint32_t hi = words[i] >> 8;
-    d[4 * i + 0] = as_half2(lo & 0x000F000Fu) - zlo;
-    d[4 * i + 1] = as_half2(lo & 0x00F000F0u) - zhi;
-    d[4 * i + 2] = as_half2(hi & 0x000F000Fu) - zlo;
-    d[4 * i + 3] = as_half2(hi & 0x00F000F0u) - zhi;
+    d[4 * i + 0] = as_half2(lo & 0x000F000Fu);
+    d[4 * i + 1] = as_half2(lo & 0x00F000F0u);
+    d[4 * i + 2] = as_half2(hi & 0x000F000Fu);
+    d[4 * i + 3] = as_half2(hi & 0x00F000F0u);
   }
 }
 
-// 2^-24 * sum of x[k] * (code_k - zero) over one unit, k ascending.
-__device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&d)[16]) {
+// sum_k x[k] * (code_k - zero) over one unit (x pre-scaled, xs the unit's
+// activation sum from unit_xsum): the code products are accumulated k
+// ascending with one rounding each, then the zero point's term -zero * xs is
+// added with one fused rounding.  The zero point is constant over the unit
+// (a group spans whole units), so this is the dequantized dot product with
+// the subtraction moved out of the per-input work.
+__device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&d)[16], float xs,
+                                          float zero) {
   float t = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -211,82 +216,358 @@ __device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&
     t = fmaf(x[8 * i + 6], (float)d[4 * i + 2].y, t);
     t = fmaf(x[8 * i + 7], (float)d[4 * i + 3].y, t);
   }
+  return fmaf(-zero, xs, t);
+}
+
+// Sum of one unit's 32 activations, k ascending, from the pre-scaled values
+// (multiplying by 2^-24 or 2^-20 undoes the scaling exactly).
+__device__ __forceinline__ float unit_xsum(const float (&x)[32]) {
+  float t = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) t += x[k] * ((k & 1) ? (1.0f / kOddScale) : (1.0f / kEvenScale));
   return t;
 }
 
-template <int M, int NSLOT>
-__device__ __forceinline__ void compute_step(const float4* xl, int U, int ch, int lane,
-                                             const Step<NSLOT>& r, float (&acc)[M][NSLOT]) {
-  const int u = ch * kWave + lane;
-  const bool active = u < U;
-  half2_t d[NSLOT][16];
+// Activations of one unit: float4 v holds inputs 4j..4j+3.  Even inputs are
+// scaled by 2^24 and odd inputs by 2^20 (exact power-of-two scalings), so the
+// products with the fp16 codes code * 2^-24 / code * 2^-20 are plain
+// x * code and a unit's sum needs no rescaling.
+__device__ __forceinline__ float4 prescale4(float4 v) {
+  return make_float4(v.x * kEvenScale, v.y * kOddScale, v.z * kEvenScale, v.w * kOddScale);
+}
+
+__device__ __forceinline__ void put4(float (&x)[32], int j, float4 v) {
+  const float4 p = prescale4(v);
+  x[4 * j + 0] = p.x;
+  x[4 * j + 1] = p.y;
+  x[4 * j + 2] = p.z;
+  x[4 * j + 3] = p.w;
+}
+
+// Buffer resources of one wave's weight streams (scalar registers): each
+// starts at the wave's first column, so every offset below is 32-bit.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
+constexpr int kLoadNonTemporal = 2;       // cache policy: streamed, no reuse expected
+
+struct StreamBufs {
+  __amdgpu_buffer_rsrc_t q[2], s[2], z[2];
+};
+
+template <int NSTREAM>
+__device__ __forceinline__ StreamBufs make_stream_bufs(const GemvArgs& a, int64_t c_begin, int64_t c_end) {
+  StreamBufs b;
+  const int64_t ncols = c_end > c_begin ? c_end - c_begin : 0;
+  const int64_t qbytes = (int64_t)a.U * 16, gbytes = (int64_t)a.G * 4;
 #pragma unroll
-  for (int c = 0; c < NSLOT; ++c) unit_codes(r.q[c], r.z[c], d[c]);
+  for (int st = 0; st < NSTREAM; ++st) {
+    b.q[st] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.q[st]) + c_begin * qbytes), (short)0,
+        (int)(ncols * qbytes), kBufferWord3);
+    b.s[st] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.s[st]) + c_begin * gbytes), (short)0,
+        (int)(ncols * gbytes), kBufferWord3);
+    b.z[st] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.z[st]) + c_begin * gbytes), (short)0,
+        (int)(ncols * gbytes), kBufferWord3);
+  }
+  return b;
+}
+
+// Issue the loads of one step: for slot c, the unit at byte offset `qoff` of
+// column rel + c/NSTREAM (relative to the wave's first column) in weight
+// stream c%NSTREAM, and the scale and zero at byte offset `soff` of that
+// column's group table.  Column offsets are wave-uniform scalars and the lane
+// offsets 32-bit vector registers, so each load is one buffer instruction
+// with no 64-bit address arithmetic.  A column past the last one (`last`)
+// reads column `last`; its result is never stored.  An inactive lane reads
+// unit 0 of the column, and since its activations are 0 it adds exactly 0.
+// The loads are unconditional and nothing here uses a loaded value, so the
+// compiler's wait counts stay exact and the next step's loads overlap the
+// current step's arithmetic.
+template <int NCOL, int NSTREAM>
+__device__ __forceinline__ void load_units(const GemvArgs& a, const StreamBufs& b, uint32_t rel,
+                                           uint32_t last, uint32_t qoff, uint32_t soff,
+                                           Step<NCOL * NSTREAM>& r) {
+  const uint32_t qbytes = (uint32_t)a.U * 16u, gbytes = (uint32_t)a.G * 4u;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float x[32];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 v = active ? xl[(m * 8 + j) * U + u] : make_float4(0.f, 0.f, 0.f, 0.f);
-      x[4 * j + 0] = v.x;
-      x[4 * j + 1] = v.y;
-      x[4 * j + 2] = v.z;
-      x[4 * j + 3] = v.w;
-    }
-#pragma unroll
-    for (int c = 0; c < NSLOT; ++c) {
-      const float t = unit_dot(x, d[c]);
-      acc[m][c] = fmaf(r.s[c], t * kTwo24, acc[m][c]);
-    }
+  for (int c = 0; c < NCOL * NSTREAM; ++c) {
+    const int st = c % NSTREAM;
+    const uint32_t col0 = rel + (uint32_t)(c / NSTREAM);
+    const uint32_t col = col0 < last ? col0 : last;
+    r.q[c] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.q[st], qoff, col * qbytes, kLoadNonTemporal));
+    r.s[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.s[st], soff, col * gbytes, 0));
+    r.z[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.z[st], soff, col * gbytes, 0));
   }
 }
 
-template <int M, int NCOL, int MODE>
-__device__ __forceinline__ void finish_group(const GemvArgs& a, int64_t n, int64_t c_end, int lane,
-                                             float (&acc)[M][NCOL * (MODE == kGated ? 2 : 1)]) {
+__device__ __forceinline__ int unit_group(const GemvArgs& a, int u) {
+  return (int)(((uint64_t)u * a.g_magic) >> 40);
+}
+
+// ------------------------------------------------------------ RMSNorm prologue
+
+// inv_rms = 1 / sqrt(sum_k (a_a + a_b)^2 / K + eps) ([P4] WGSL_NORM_MATVEC_INT4),
+// identical in every block: per-thread strided partials, wave butterflies,
+// waves summed in index order.  `scratch` holds one float per wave.
+__device__ __forceinline__ float block_inv_rms(const GemvArgs& a, float* scratch) {
+  const int n4 = a.K >> 2;
+  const float4* aa = reinterpret_cast<const float4*>(a.x);
+  const float4* ab = reinterpret_cast<const float4*>(a.x2);
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+    const float4 x1 = aa[i];
+    const float4 x2 = ab[i];
+    const float r0 = x1.x + x2.x, r1 = x1.y + x2.y, r2 = x1.z + x2.z, r3 = x1.w + x2.w;
+    ss = fmaf(r0, r0, ss);
+    ss = fmaf(r1, r1, ss);
+    ss = fmaf(r2, r2, ss);
+    ss = fmaf(r3, r3, ss);
+  }
+  const float wsum = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = wsum;
+  __syncthreads();
+  float total = scratch[0];
+  const int nw = blockDim.x >> 6;
+  for (int w = 1; w < nw; ++w) total += scratch[w];
+  return 1.0f / sqrtf(total / (float)a.K + a.eps);
+}
+
+// r = a_a + a_b and x = r * inv_rms * w_norm for float4 i (binary32, left to right).
+__device__ __forceinline__ void norm4(const GemvArgs& a, int i, float inv, float4& r, float4& x) {
+  const float4 x1 = reinterpret_cast<const float4*>(a.x)[i];
+  const float4 x2 = reinterpret_cast<const float4*>(a.x2)[i];
+  const float4 g = reinterpret_cast<const float4*>(a.w_norm)[i];
+  r = make_float4(x1.x + x2.x, x1.y + x2.y, x1.z + x2.z, x1.w + x2.w);
+  x = make_float4(r.x * inv * g.x, r.y * inv * g.y, r.z * inv * g.z, r.w * inv * g.w);
+}
+
+// Block 0 writes residual_out and norm_out (optional outputs, once per call).
+__device__ __forceinline__ void write_norm_outputs(const GemvArgs& a, float inv) {
+  if (blockIdx.x != 0 || (a.residual_out == nullptr && a.norm_out == nullptr)) return;
+  float4* res = reinterpret_cast<float4*>(a.residual_out);
+  float4* nrm = reinterpret_cast<float4*>(a.norm_out);
+  for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
+    float4 r, x;
+    norm4(a, i, inv, r, x);
+    if (res) res[i] = r;
+    if (nrm) nrm[i] = x;
+  }
+}
+
+// Column epilogue shared by both kernels: `tot[st][m]` are the finished sums
+// of column `col` (stream st: 0 = the weights / gate, 1 = up).
+template <int M, int MODE>
+__device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
+                                             const float (&tot)[MODE == kGated ? 2 : 1][M]) {
+  if constexpr (MODE == kPlain) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) a.out[0][(int64_t)m * a.N + col] = tot[0][m];
+  } else if constexpr (MODE == kNorm) {
+    a.out[0][col] = tot[0][0];
+  } else if constexpr (MODE == kSplit4) {
+    const float v = tot[0][0];
+    if (col < a.n0) a.out[0][col] = v;
+    else if (col < a.n1) a.out[1][col - a.n0] = v;
+    else if (col < a.n2) a.out[2][col - a.n1] = v;
+    else a.out[3][col - a.n2] = v;
+  } else {
+    // silu(g) = g / (1 + e^-g), evaluated as g e / (1 + e) with e = e^g for
+    // negative g so that e^-g never overflows ([P1] SwiGLU: silu(gate) * up).
+    const float g = tot[0][0];
+    const float u = tot[1][0];
+    const float e = expf(-fabsf(g));
+    const float silu = g >= 0.0f ? g / (1.0f + e) : (g * e) / (1.0f + e);
+    a.out[0][col] = silu * u;
+  }
+}
+
+// ------------------------------------------------------------ register kernel
+
+template <int M, int NCOL, int MODE, int DEPTH>
+__global__ __launch_bounds__(1024) void gemv_reg_kernel(GemvArgs a) {
   constexpr int NSTREAM = MODE == kGated ? 2 : 1;
   constexpr int NSLOT = NCOL * NSTREAM;
-  float tot[M][NSLOT];
+  constexpr int V = M * NSLOT;
+  constexpr int NZ = (V + 3) / 4;
+  extern __shared__ float part[];  // [cols of the block][NSTREAM][M][nch], then one float per wave
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int nch = a.nch;
+  const int P = a.rows_per_block;
+  const int p = wave / nch;
+  const int c = wave - p * nch;
+  const int64_t R = (int64_t)gridDim.x * P;
+  const int64_t blk_begin = uniform_i64((int64_t)blockIdx.x * P * a.N / R);
+  const int64_t blk_end = uniform_i64(((int64_t)blockIdx.x * P + P) * a.N / R);
+  const int64_t row = (int64_t)blockIdx.x * P + p;
+  const int64_t c_begin = uniform_i64(row * a.N / R);
+  const int64_t c_end = uniform_i64((row + 1) * a.N / R);
+  const int u = c * a.cw + lane;
+  const bool active = lane < a.cw && u < a.U;
+  const uint32_t qoff = (uint32_t)(active ? u : 0) * 16u;
+  const uint32_t soff = (uint32_t)(active ? unit_group(a, u) : 0) * 4u;
+  float* scratch = part + a.part_floats;
+
+  // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
+  // before step i is computed.  The first loads go out before the activations
+  // are fetched.
+  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
+  const uint32_t last = c_end > c_begin ? (uint32_t)(c_end - c_begin - 1) : 0u;
+  Step<NSLOT> s0, s1, s2;
+  if (c_begin < c_end) load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+  if (DEPTH == 2 && c_begin + NCOL < c_end)
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)NCOL, last, qoff, soff, s1);
+
+  // Activations of this lane's unit, held in registers for the whole kernel.
+  float x[M][32];
+  if constexpr (MODE == kNorm) {
+    const float inv = block_inv_rms(a, scratch);
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int c = 0; c < NSLOT; ++c) {
-      tot[m][c] = wave_sum(acc[m][c]);
-      acc[m][c] = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+      float4 r, v;
+      if (active) {
+        norm4(a, 8 * u + j, inv, r, v);
+      } else {
+        v = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      put4(x[0], j, v);
     }
-  if (lane != 0) return;
+    write_norm_outputs(a, inv);
+  } else {
 #pragma unroll
-  for (int cc = 0; cc < NCOL; ++cc) {
-    const int64_t col = n + cc;
-    if (col >= c_end) break;
-    if (MODE == kPlain) {
+    for (int m = 0; m < M; ++m) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K) + 8 * u;
 #pragma unroll
-      for (int m = 0; m < M; ++m) a.out[0][(int64_t)m * a.N + col] = tot[m][cc];
-    } else if (MODE == kNorm) {
-      a.out[0][col] = tot[0][cc];
-    } else if (MODE == kSplit4) {
-      const float v = tot[0][cc];
-      if (col < a.n0) a.out[0][col] = v;
-      else if (col < a.n1) a.out[1][col - a.n0] = v;
-      else if (col < a.n2) a.out[2][col - a.n1] = v;
-      else a.out[3][col - a.n2] = v;
-    } else {  // kGated: slot 2cc is the gate column, 2cc+1 the up column
-      const float g = tot[0][2 * cc];
-      const float u = tot[0][2 * cc + 1];
-      a.out[0][col] = g / (1.0f + expf(-g)) * u;
+      for (int j = 0; j < 8; ++j) put4(x[m], j, active ? src[j] : make_float4(0.f, 0.f, 0.f, 0.f));
     }
+  }
+
+  float xs[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xs[m] = unit_xsum(x[m]);
+
+  const bool writer = V >= 4 ? (lane & 15) == 0 : (V == 2 ? (lane & 31) == 0 : lane == 0);
+  auto step = [&](int64_t n, const Step<NSLOT>& r) {
+    float vals[V];
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      half2_t d[16];
+      unit_codes(r.q[sl], d);
+#pragma unroll
+      for (int m = 0; m < M; ++m) vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x[m], d, xs[m], r.z[sl]);
+    }
+    float z[NZ];
+    wave_reduce<V>(vals, z);
+    if (writer) {
+      const int rrow = lane >> 4;
+#pragma unroll
+      for (int j = 0; j < NZ; ++j) {
+        const int vi = reduced_index<V>(j, rrow);
+        const int m = vi / NSLOT;
+        const int sl = vi - m * NSLOT;
+        const int64_t col = n + sl / NSTREAM;
+        if (col < c_end)
+          part[(((col - blk_begin) * NSTREAM + sl % NSTREAM) * M + m) * nch + c] = z[j];
+      }
+    }
+  };
+
+  // One pipeline stage: issue the loads DEPTH groups ahead into `far`, then
+  // compute `cur` (group n).  The steady-state loop runs only while every
+  // prefetch of an iteration is in range, so it has no branch around its
+  // loads and the compiler's wait counts stay exact; the last groups run
+  // through the guarded stage.
+  auto stage_ss = [&](int64_t n, const Step<NSLOT>& cur, Step<NSLOT>& far) {
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(n - c_begin) + DEPTH * NCOL, last, qoff, soff, far);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+    step(n, cur);
+  };
+  auto stage = [&](int64_t n, const Step<NSLOT>& cur, Step<NSLOT>& far) {
+    const int64_t nf = n + DEPTH * NCOL;
+    if (nf < c_end) load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(nf - c_begin), last, qoff, soff, far);
+    __builtin_amdgcn_sched_barrier(0);
+    step(n, cur);
+    return n + NCOL < c_end;
+  };
+  int64_t n = c_begin;
+  if constexpr (DEPTH == 1) {
+    while (n + 2 * NCOL < c_end) {
+      stage_ss(n, s0, s1);
+      stage_ss(n + NCOL, s1, s0);
+      n += 2 * NCOL;
+    }
+    while (n < c_end) {
+      if (!stage(n, s0, s1)) break;
+      n += NCOL;
+      if (!stage(n, s1, s0)) break;
+      n += NCOL;
+    }
+  } else {
+    while (n + 4 * NCOL < c_end) {
+      stage_ss(n, s0, s2);
+      stage_ss(n + NCOL, s1, s0);
+      stage_ss(n + 2 * NCOL, s2, s1);
+      n += 3 * NCOL;
+    }
+    while (n < c_end) {
+      if (!stage(n, s0, s2)) break;
+      n += NCOL;
+      if (!stage(n, s1, s0)) break;
+      n += NCOL;
+      if (!stage(n, s2, s1)) break;
+      n += NCOL;
+    }
+  }
+  __syncthreads();
+
+  // Each column's chunk partials, summed in chunk order.
+  const int64_t ncols = blk_end - blk_begin;
+  for (int64_t j = threadIdx.x; j < ncols; j += blockDim.x) {
+    float tot[NSTREAM][M];
+#pragma unroll
+    for (int st = 0; st < NSTREAM; ++st)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float* pp = part + ((j * NSTREAM + st) * M + m) * nch;
+        float s = pp[0];
+        for (int cc = 1; cc < nch; ++cc) s += pp[cc];
+        tot[st][m] = s;
+      }
+    store_column<M, MODE>(a, blk_begin + j, tot);
+  }
+}
+
+// ------------------------------------------------------------ LDS kernel
+
+// Activation row m is stored as float4 xl[m][j][u] = inputs 32u+4j .. 32u+4j+3,
+// pre-scaled like the register kernel's activations (prescale4).
+template <int M>
+__device__ __forceinline__ void stage_x(const float* __restrict__ X, int K, int U, float4* xl) {
+  const int n4 = K >> 2;
+  for (int m = 0; m < M; ++m) {
+    const float4* src = reinterpret_cast<const float4*>(X + (size_t)m * K);
+    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+      xl[(m * 8 + (i & 7)) * U + (i >> 3)] = prescale4(src[i]);
   }
 }
 
 template <int M, int NCOL, int MODE>
-__global__ __launch_bounds__(kMaxBlockThreads) void gemv_int4_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   constexpr int NSTREAM = MODE == kGated ? 2 : 1;
   constexpr int NSLOT = NCOL * NSTREAM;
   extern __shared__ float4 xl[];
 
-  if (MODE == kNorm) {
-    float* red = reinterpret_cast<float*>(xl + (size_t)8 * a.U);
-    stage_norm(a, xl, red);
+  if constexpr (MODE == kNorm) {
+    float* scratch = reinterpret_cast<float*>(xl + (size_t)8 * a.U);
+    const float inv = block_inv_rms(a, scratch);
+    for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
+      float4 r, v;
+      norm4(a, i, inv, r, v);
+      xl[(i & 7) * a.U + (i >> 3)] = prescale4(v);
+    }
+    write_norm_outputs(a, inv);
   } else {
     stage_x<M>(a.x, a.K, a.U, xl);
   }
@@ -295,31 +576,80 @@ __global__ __launch_bounds__(kMaxBlockThreads) void gemv_int4_kernel(GemvArgs a)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_int(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  const int64_t c_begin = gw * a.N / a.total_waves;
-  const int64_t c_end = (gw + 1) * a.N / a.total_waves;
+  const int64_t c_begin = uniform_i64(gw * a.N / a.total_waves);
+  const int64_t c_end = uniform_i64((gw + 1) * a.N / a.total_waves);
   if (c_begin >= c_end) return;
 
+  // acc[m][sl]: the column's chunk partials summed in chunk order, the same
+  // order as the register kernel's epilogue (wave-uniform values).
   float acc[M][NSLOT];
-#pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int c = 0; c < NSLOT; ++c) acc[m][c] = 0.0f;
-
   const int nch = a.nch;
+  auto compute = [&](int ch, const Step<NSLOT>& r) {
+    const int u = ch * a.cw + lane;
+    const bool active = lane < a.cw && u < a.U;
+    half2_t d[NSLOT][16];
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) unit_codes(r.q[sl], d[sl]);
+    float vals[M * NSLOT];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 v = active ? xl[(m * 8 + j) * a.U + u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[4 * j + 0] = v.x;
+        x[4 * j + 1] = v.y;
+        x[4 * j + 2] = v.z;
+        x[4 * j + 3] = v.w;
+      }
+      const float xs = unit_xsum(x);
+#pragma unroll
+      for (int sl = 0; sl < NSLOT; ++sl)
+        vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x, d[sl], xs, r.z[sl]);
+    }
+    float tot[M * NSLOT];
+    wave_totals<M * NSLOT>(vals, tot);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int sl = 0; sl < NSLOT; ++sl)
+        acc[m][sl] = ch == 0 ? tot[m * NSLOT + sl] : acc[m][sl] + tot[m * NSLOT + sl];
+  };
+  auto finish = [&](int64_t n) {
+    if (lane != 0) return;
+#pragma unroll
+    for (int cc = 0; cc < NCOL; ++cc) {
+      const int64_t col = n + cc;
+      if (col >= c_end) break;
+      float t[NSTREAM][M];
+#pragma unroll
+      for (int st = 0; st < NSTREAM; ++st)
+#pragma unroll
+        for (int m = 0; m < M; ++m) t[st][m] = acc[m][cc * NSTREAM + st];
+      store_column<M, MODE>(a, col, t);
+    }
+  };
+  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
+  const uint32_t last = (uint32_t)(c_end - c_begin - 1);
+  auto load = [&](int64_t n, int ch, Step<NSLOT>& r) {
+    const int u = ch * a.cw + lane;
+    const bool active = lane < a.cw && u < a.U;
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(n - c_begin), last, (uint32_t)(active ? u : 0) * 16u,
+                              (uint32_t)(active ? unit_group(a, u) : 0) * 4u, r);
+  };
+
   Step<NSLOT> ra, rb;
   int64_t n = c_begin;
   int ch = 0;
-  load_step<NCOL, NSTREAM>(a, n, ch, c_end, lane, ra);
-  // Two-stage software pipeline, unrolled twice so the register sets ping-pong
-  // instead of being copied.
+  load(n, ch, ra);
   while (true) {
     int ch2 = ch + 1;
     int64_t n2 = n;
     if (ch2 == nch) { ch2 = 0; n2 += NCOL; }
     bool more = n2 < c_end;
-    if (more) load_step<NCOL, NSTREAM>(a, n2, ch2, c_end, lane, rb);
-    compute_step<M, NSLOT>(xl, a.U, ch, lane, ra, acc);
-    if (ch == nch - 1) finish_group<M, NCOL, MODE>(a, n, c_end, lane, acc);
+    if (more) load(n2, ch2, rb);
+    compute(ch, ra);
+    if (ch == nch - 1) finish(n);
     if (!more) break;
     n = n2;
     ch = ch2;
@@ -328,9 +658,9 @@ __global__ __launch_bounds__(kMaxBlockThreads) void gemv_int4_kernel(GemvArgs a)
     n2 = n;
     if (ch2 == nch) { ch2 = 0; n2 += NCOL; }
     more = n2 < c_end;
-    if (more) load_step<NCOL, NSTREAM>(a, n2, ch2, c_end, lane, ra);
-    compute_step<M, NSLOT>(xl, a.U, ch, lane, rb, acc);
-    if (ch == nch - 1) finish_group<M, NCOL, MODE>(a, n, c_end, lane, acc);
+    if (more) load(n2, ch2, ra);
+    compute(ch, rb);
+    if (ch == nch - 1) finish(n);
     if (!more) break;
     n = n2;
     ch = ch2;
@@ -426,61 +756,114 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restr
   }
 }
 
-// ------------------------------------------------------------ dispatch tables
+// ------------------------------------------------------------ dispatch
 
-template <int MODE, int M, int NCOL>
-hipError_t launch_one(const GemvArgs& a, const LaunchShape& s, hipStream_t stream) {
-  auto kern = gemv_int4_kernel<M, NCOL, MODE>;
-  // Dynamic LDS beyond 64 KiB must be allowed per kernel; do it once, for the
+template <typename Kern>
+hipError_t raise_lds_once(Kern kern, std::atomic<bool>& done, const LaunchShape& s) {
+  // Dynamic LDS beyond 64 KiB must be allowed per kernel; once, for the
   // device maximum, before the first large launch of this instantiation.
-  static std::atomic<bool> lds_raised{false};
-  if (s.lds_bytes > 65536 && !lds_raised.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)s.lds_max);
-    if (e != hipSuccess) return e;
-    lds_raised.store(true, std::memory_order_release);
-  }
+  if (s.lds_bytes <= 65536 || done.load(std::memory_order_acquire)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)s.lds_max);
+  if (e == hipSuccess) done.store(true, std::memory_order_release);
+  return e;
+}
+
+template <typename Kern>
+hipError_t launch_or_query(Kern kern, std::atomic<bool>& raised, const GemvArgs& a,
+                           const LaunchShape& s, hipStream_t stream, int* occupancy) {
+  hipError_t e = raise_lds_once(kern, raised, s);
+  if (e != hipSuccess) return e;
+  if (occupancy)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, kern, s.block_threads, s.lds_bytes);
   hipLaunchKernelGGL(kern, dim3(s.grid), dim3(s.block_threads), s.lds_bytes, stream, a);
   return hipGetLastError();
 }
 
-template <int MODE, int M>
-hipError_t launch_ncol(const GemvArgs& a, const LaunchShape& s, hipStream_t stream) {
-  switch (s.ncol) {
-    case 1: return launch_one<MODE, M, 1>(a, s, stream);
-    case 2: return launch_one<MODE, M, 2>(a, s, stream);
-    default: return launch_one<MODE, M, (M <= 2 ? 4 : 2)>(a, s, stream);
+template <int MODE, int M, int NCOL>
+hipError_t launch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t stream, int* occupancy) {
+  static std::atomic<bool> raised1{false}, raised2{false};
+  if (s.depth == 2)
+    return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, 2>, raised2, a, s, stream, occupancy);
+  return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, 1>, raised1, a, s, stream, occupancy);
+}
+
+template <int MODE, int M, int NCOL>
+hipError_t launch_lds(const GemvArgs& a, const LaunchShape& s, hipStream_t stream, int* occupancy) {
+  static std::atomic<bool> raised{false};
+  return launch_or_query(gemv_lds_kernel<M, NCOL, MODE>, raised, a, s, stream, occupancy);
+}
+
+template <int MODE>
+hipError_t dispatch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if constexpr (MODE == kGated) {
+    return s.ncol == 1 ? launch_reg<MODE, 1, 1>(a, s, st, occ) : launch_reg<MODE, 1, 2>(a, s, st, occ);
+  } else if constexpr (MODE == kPlain) {
+    if (a.M == 2)
+      return s.ncol == 1 ? launch_reg<MODE, 2, 1>(a, s, st, occ) : launch_reg<MODE, 2, 2>(a, s, st, occ);
+    switch (s.ncol) {
+      case 1: return launch_reg<MODE, 1, 1>(a, s, st, occ);
+      case 2: return launch_reg<MODE, 1, 2>(a, s, st, occ);
+      default: return launch_reg<MODE, 1, 4>(a, s, st, occ);
+    }
+  } else {
+    switch (s.ncol) {
+      case 1: return launch_reg<MODE, 1, 1>(a, s, st, occ);
+      case 2: return launch_reg<MODE, 1, 2>(a, s, st, occ);
+      default: return launch_reg<MODE, 1, 4>(a, s, st, occ);
+    }
+  }
+}
+
+template <int M>
+hipError_t dispatch_lds_m(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  return s.ncol == 1 ? launch_lds<kPlain, M, 1>(a, s, st, occ) : launch_lds<kPlain, M, 2>(a, s, st, occ);
+}
+
+hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if (s.variant == kVariantReg) {
+    switch (mode) {
+      case kSplit4: return dispatch_reg<kSplit4>(a, s, st, occ);
+      case kGated: return dispatch_reg<kGated>(a, s, st, occ);
+      case kNorm: return dispatch_reg<kNorm>(a, s, st, occ);
+      default: return dispatch_reg<kPlain>(a, s, st, occ);
+    }
+  }
+  switch (mode) {
+    case kSplit4: return launch_lds<kSplit4, 1, 1>(a, s, st, occ);
+    case kGated: return launch_lds<kGated, 1, 1>(a, s, st, occ);
+    case kNorm: return launch_lds<kNorm, 1, 1>(a, s, st, occ);
+    default: break;
+  }
+  switch (a.M) {
+    case 1: return dispatch_lds_m<1>(a, s, st, occ);
+    case 2: return dispatch_lds_m<2>(a, s, st, occ);
+    case 3: return dispatch_lds_m<3>(a, s, st, occ);
+    case 4: return dispatch_lds_m<4>(a, s, st, occ);
+    case 5: return dispatch_lds_m<5>(a, s, st, occ);
+    case 6: return dispatch_lds_m<6>(a, s, st, occ);
+    case 7: return dispatch_lds_m<7>(a, s, st, occ);
+    default: return dispatch_lds_m<8>(a, s, st, occ);
   }
 }
 
 }  // namespace
 
-int max_ncol(Mode mode, int M) {
-  if (mode == kGated) return 2;
-  return M <= 2 ? 4 : 2;
+int max_ncol(Mode mode, int M, int variant) {
+  if (variant == kVariantReg) {
+    if (mode == kGated) return 2;
+    return M == 1 ? 4 : 2;
+  }
+  return mode == kPlain ? 2 : 1;
+}
+
+hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* blocks_per_cu) {
+  *blocks_per_cu = 0;
+  return dispatch(mode, a, s, nullptr, blocks_per_cu);
 }
 
 hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t stream) {
-  switch (mode) {
-    case kSplit4: return launch_ncol<kSplit4, 1>(a, s, stream);
-    case kNorm: return launch_ncol<kNorm, 1>(a, s, stream);
-    case kGated:
-      return s.ncol == 1 ? launch_one<kGated, 1, 1>(a, s, stream)
-                         : launch_one<kGated, 1, 2>(a, s, stream);
-    case kPlain:
-    default:
-      switch (a.M) {
-        case 1: return launch_ncol<kPlain, 1>(a, s, stream);
-        case 2: return launch_ncol<kPlain, 2>(a, s, stream);
-        case 3: return launch_ncol<kPlain, 3>(a, s, stream);
-        case 4: return launch_ncol<kPlain, 4>(a, s, stream);
-        case 5: return launch_ncol<kPlain, 5>(a, s, stream);
-        case 6: return launch_ncol<kPlain, 6>(a, s, stream);
-        case 7: return launch_ncol<kPlain, 7>(a, s, stream);
-        default: return launch_ncol<kPlain, 8>(a, s, stream);
-      }
-  }
+  return dispatch(mode, a, s, stream, nullptr);
 }
 
 hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,
