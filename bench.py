@@ -274,6 +274,35 @@ def cpu_baseline(calls_meta, budget_s=12.0):
             "seconds": dt}
 
 
+def counter_probe(q4, torch, dev):
+    """Launches for hardware-counter runs: the LM-head norm call on four
+    rotating weight copies (random codes and groups: the bytes a launch moves
+    do not depend on the values), then a plain device copy of 256 MiB whose
+    bytes are known, used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    c4 = synth.CONFIGS["c4"]
+    N, K, gs = c4["N"], c4["K"], c4["gs"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    sets = []
+    for _ in range(4):
+        q = torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, device=dev, generator=g)
+        s = torch.rand((N, K // gs), device=dev, generator=g) * 1e-2
+        z = torch.randint(0, 16, (N, K // gs), device=dev, generator=g).float()
+        sets.append((q, s, z))
+    a = [torch.randn(K, device=dev, generator=g) for _ in range(3)]
+    y, r, n = (torch.empty(m, device=dev) for m in (N, K, K))
+    for i in range(5):
+        q, s, z = sets[i % 4]
+        q4.int4_matvec_norm(*a, c4["eps"], q, s, z, y=y, residual_out=r, norm_out=n)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 26, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes 256 MiB
+    torch.cuda.synchronize()
+    log(f"counter probe: 5 norm launches {N}x{K} gs {gs}, 5 copies of {src.numel() * 4} bytes")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +310,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (the JSON then carries cpu_baseline null)")
+    ap.add_argument("--counter-probe", action="store_true",
+                    help="only launch the LM-head norm call and a plain 256 MiB device copy, "
+                         "5 times each, for rocprofv3 --pmc runs (prints no JSON)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the int4 matvec path here has no multi-GPU "
@@ -295,6 +327,10 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '?')} CUs={props.multi_processor_count}")
+
+    if args.counter_probe:
+        counter_probe(q4, torch, dev)
+        return
 
     calls, quant, keep = build_workload(q4, torch, dev)
     step_bytes = sum(c.nbytes for c in calls)
