@@ -128,8 +128,12 @@ int int4_matvec_gated(const float* x,
  *   inv    = 1 / sqrt(sum_k r[k]^2 / K + eps)
  *   x[k]   = r[k] * inv * w_norm[k]
  *   y[n]   = sum_k x[k] * w[n][k]
- * residual_out (r) and norm_out (x) are optional (NULL = not written) and are
- * written once per call.  eps must be finite and >= 0 (the pages default to
+ * inv is one factor of the whole input, so the library computes
+ * y[n] = inv * sum_k (r[k] * w_norm[k]) * w[n][k] and writes
+ * norm_out[k] = (r[k] * w_norm[k]) * inv, each product rounded to binary32
+ * (within the dot-product tolerance of the definition above; residual_out
+ * is exact).  residual_out (r) and norm_out (x) are optional (NULL = not
+ * written) and are written once per call.  eps must be finite and >= 0 (the pages default to
  * 1e-6).  N == 0 still writes residual_out / norm_out when they are given.
  * K * 4 bytes must fit the per-block local data share.
  */

@@ -166,10 +166,10 @@ int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bp
 // Launch geometry.  Both kernels run persistent grids: as many blocks as are
 // resident on the device at once, so no block waits for a second round.
 //
-// Register kernel (M <= 2, K <= 32768): nch = ceil(K/2048) chunks of cw units,
+// Register kernel (M <= 2, K <= 16384): nch = ceil(K/2048) chunks of cw units,
 // P = 8/nch rows of nch waves per block (about 8 waves: two per SIMD, which
 // streams best), columns split evenly over the B*P rows, one LDS partial per
-// (column, stream, lane, chunk).
+// (column, stream, lane, chunk), the activations staged once per block.
 //
 // LDS kernel (M >= 3 or larger K): 256-thread blocks, the M activation rows
 // staged in LDS (M*K*4 bytes), columns split evenly over the waves.
@@ -180,42 +180,50 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   const int64_t N = a.N;
   const int nstream = mode == kGated ? 2 : 1;
   s->lds_max = dev.lds_block;
-  if (M <= 2 && a.nch <= 16) {
+  const int rows = mode == kPlain ? M : 1;
+  if (M <= 2 && a.nch <= 8) {
     const int nch = a.nch;
     const int P = nch >= 8 ? 1 : 8 / nch;
-    a.rows_per_block = P;
-    s->variant = kVariantReg;
-    s->depth = 1;
-    s->block_threads = 64 * P * nch;
     auto table = [&](int64_t blocks) {
       return (int64_t)((N + blocks - 1) / blocks) * nstream * M * nch;
     };
-    int ncol = max_ncol(mode, M, kVariantReg);
-    while (ncol > 1 && N / ((int64_t)dev.cus * P) < ncol) ncol /= 2;
-    s->ncol = ncol;
-    int64_t B = dev.cus;
-    s->lds_bytes = (size_t)(table(B) + 16) * sizeof(float);
-    if (s->lds_bytes > dev.lds_block)
-      return fail(INT4_ERR_SHAPE, "N=%lld needs %zu bytes of LDS per block for partial sums",
-                  (long long)N, s->lds_bytes);
-    int bpc = 1;
-    RETURN_IF(cached_occupancy(mode, a, *s, &bpc));
-    // One block of about 8 waves per CU; more resident waves per CU only
-    // add contention for the memory pipeline.
-    const int waves_per_block = P * nch;
-    if (bpc > 1 && waves_per_block * bpc > 8) bpc = waves_per_block >= 8 ? 1 : 8 / waves_per_block;
-    B = (int64_t)dev.cus * bpc;
-    const int64_t max_blocks = (N + P - 1) / P;  // at least one column per row
-    if (B > max_blocks) B = max_blocks;
-    if (B < 1) B = 1;
-    while (s->ncol > 1 && N / (B * P) < s->ncol) s->ncol /= 2;
-    a.part_floats = (int32_t)table(B);
-    s->lds_bytes = (size_t)(a.part_floats + 16) * sizeof(float);
-    s->grid = (int)B;
-    a.total_waves = B * P * nch;
-    return INT4_OK;
+    // Partial table, wave slots and the staged activations.
+    auto lds_for = [&](int64_t blocks) -> size_t {
+      const int64_t t = table(blocks);
+      if (t > ((int64_t)1 << 28)) return (size_t)-1;
+      return ((size_t)x_lds_offset((int)t) + (size_t)rows * (size_t)a.K) * sizeof(float);
+    };
+    if (lds_for(dev.cus) <= dev.lds_block) {
+      a.rows_per_block = P;
+      s->variant = kVariantReg;
+      s->depth = 1;
+      s->block_threads = 64 * P * nch;
+      int ncol = max_ncol(mode, M, kVariantReg);
+      while (ncol > 1 && N / ((int64_t)dev.cus * P) < ncol) ncol /= 2;
+      s->ncol = ncol;
+      s->lds_bytes = lds_for(dev.cus);
+      int bpc = 1;
+      RETURN_IF(cached_occupancy(mode, a, *s, &bpc));
+      // One block of about 8 waves per CU; more resident waves per CU only
+      // add contention for the memory pipeline.
+      const int waves_per_block = P * nch;
+      if (bpc > 1 && waves_per_block * bpc > 8) bpc = waves_per_block >= 8 ? 1 : 8 / waves_per_block;
+      int64_t B = (int64_t)dev.cus * bpc;
+      const int64_t max_blocks = (N + P - 1) / P;  // at least one column per row
+      if (B > max_blocks) B = max_blocks;
+      if (B < 1) B = 1;
+      while (s->ncol > 1 && N / (B * P) < s->ncol) s->ncol /= 2;
+      if (lds_for(B) <= dev.lds_block) {
+        a.part_floats = (int32_t)table(B);
+        s->lds_bytes = lds_for(B);
+        s->grid = (int)B;
+        a.total_waves = B * P * nch;
+        return INT4_OK;
+      }
+    }
+    // Too little LDS for the partial table and the activations: the LDS
+    // kernel needs only the activations.
   }
-  const int rows = mode == kPlain ? M : 1;
   const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode == kNorm ? 64 : 0);
   if (lds > dev.lds_block)
     return fail(INT4_ERR_SHAPE, "activations need %zu bytes of LDS per block; the device allows %zu",

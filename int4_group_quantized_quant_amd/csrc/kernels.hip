@@ -333,38 +333,43 @@ __device__ __forceinline__ float block_inv_rms(const GemvArgs& a, float* scratch
   return 1.0f / sqrtf(total / (float)a.K + a.eps);
 }
 
-// r = a_a + a_b and x = r * inv_rms * w_norm for float4 i (binary32, left to right).
-__device__ __forceinline__ void norm4(const GemvArgs& a, int i, float inv, float4& r, float4& x) {
+// r = a_a + a_b and x = r * w_norm for float4 i (binary32).  The matvec runs
+// on x; inv_rms is a single factor of the whole input, applied to each
+// finished column sum, so the reduction over K never delays the weight stream.
+__device__ __forceinline__ void norm_in4(const GemvArgs& a, int i, float4& r, float4& x) {
   const float4 x1 = reinterpret_cast<const float4*>(a.x)[i];
   const float4 x2 = reinterpret_cast<const float4*>(a.x2)[i];
   const float4 g = reinterpret_cast<const float4*>(a.w_norm)[i];
   r = make_float4(x1.x + x2.x, x1.y + x2.y, x1.z + x2.z, x1.w + x2.w);
-  x = make_float4(r.x * inv * g.x, r.y * inv * g.y, r.z * inv * g.z, r.w * inv * g.w);
+  x = make_float4(r.x * g.x, r.y * g.y, r.z * g.z, r.w * g.w);
 }
 
-// Block 0 writes residual_out and norm_out (optional outputs, once per call).
+// Block 0 writes residual_out = r and norm_out = (r * w_norm) * inv_rms
+// (optional outputs, once per call).
 __device__ __forceinline__ void write_norm_outputs(const GemvArgs& a, float inv) {
   if (blockIdx.x != 0 || (a.residual_out == nullptr && a.norm_out == nullptr)) return;
   float4* res = reinterpret_cast<float4*>(a.residual_out);
   float4* nrm = reinterpret_cast<float4*>(a.norm_out);
   for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
     float4 r, x;
-    norm4(a, i, inv, r, x);
+    norm_in4(a, i, r, x);
     if (res) res[i] = r;
-    if (nrm) nrm[i] = x;
+    if (nrm) nrm[i] = make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv);
   }
 }
 
 // Column epilogue shared by both kernels: `tot[st][m]` are the finished sums
 // of column `col` (stream st: 0 = the weights / gate, 1 = up).
+// `inv` is inv_rms for kNorm and unused otherwise.
 template <int M, int MODE>
 __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
-                                             const float (&tot)[MODE == kGated ? 2 : 1][M]) {
+                                             const float (&tot)[MODE == kGated ? 2 : 1][M],
+                                             float inv) {
   if constexpr (MODE == kPlain) {
 #pragma unroll
     for (int m = 0; m < M; ++m) a.out[0][(int64_t)m * a.N + col] = tot[0][m];
   } else if constexpr (MODE == kNorm) {
-    a.out[0][col] = tot[0][0];
+    a.out[0][col] = tot[0][0] * inv;
   } else if constexpr (MODE == kSplit4) {
     const float v = tot[0][0];
     if (col < a.n0) a.out[0][col] = v;
@@ -384,13 +389,16 @@ __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
 
 // ------------------------------------------------------------ register kernel
 
+
 template <int M, int NCOL, int MODE, int DEPTH>
-__global__ __launch_bounds__(1024) void gemv_reg_kernel(GemvArgs a) {
+__global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   constexpr int NSTREAM = MODE == kGated ? 2 : 1;
   constexpr int NSLOT = NCOL * NSTREAM;
   constexpr int V = M * NSLOT;
   constexpr int NZ = (V + 3) / 4;
-  extern __shared__ float part[];  // [cols of the block][NSTREAM][M][nch], then one float per wave
+  // [cols of the block][NSTREAM][M][nch], one float per wave, then the
+  // staged activations (x_lds_offset)
+  extern __shared__ float part[];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_int(threadIdx.x >> 6);
@@ -420,29 +428,39 @@ __global__ __launch_bounds__(1024) void gemv_reg_kernel(GemvArgs a) {
   if (DEPTH == 2 && c_begin + NCOL < c_end)
     load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)NCOL, last, qoff, soff, s1);
 
-  // Activations of this lane's unit, held in registers for the whole kernel.
-  float x[M][32];
+  // Activations: the block stages the M rows once in LDS (coalesced; for
+  // the norm, x = (a_a + a_b) * w_norm and block 0 writes residual_out),
+  // then each lane keeps its unit's 32 inputs in registers for the sweep.
+  float4* xl = reinterpret_cast<float4*>(part + x_lds_offset(a.part_floats));
+  const int n4 = a.K >> 2;
   if constexpr (MODE == kNorm) {
-    const float inv = block_inv_rms(a, scratch);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    // Per-thread share of sum_k r_k^2, then the wave's total in its slot.
+    float ssq = 0.0f;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
       float4 r, v;
-      if (active) {
-        norm4(a, 8 * u + j, inv, r, v);
-      } else {
-        v = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      put4(x[0], j, v);
+      norm_in4(a, i, r, v);
+      ssq = fmaf(r.x, r.x, ssq);
+      ssq = fmaf(r.y, r.y, ssq);
+      ssq = fmaf(r.z, r.z, ssq);
+      ssq = fmaf(r.w, r.w, ssq);
+      if (blockIdx.x == 0 && a.residual_out) reinterpret_cast<float4*>(a.residual_out)[i] = r;
+      xl[(i & 7) * a.U + (i >> 3)] = v;
     }
-    write_norm_outputs(a, inv);
+    const float wsum = wave_sum(ssq);
+    if (lane == 0) scratch[wave] = wsum;
   } else {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K) + 8 * u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) put4(x[m], j, active ? src[j] : make_float4(0.f, 0.f, 0.f, 0.f));
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K);
+      for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(m * 8 + (i & 7)) * a.U + (i >> 3)] = src[i];
     }
   }
+  __syncthreads();
+  float x[M][32];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) put4(x[m], j, active ? xl[(m * 8 + j) * a.U + u] : make_float4(0.f, 0.f, 0.f, 0.f));
 
   float xs[M];
 #pragma unroll
@@ -522,6 +540,22 @@ __global__ __launch_bounds__(1024) void gemv_reg_kernel(GemvArgs a) {
   }
   __syncthreads();
 
+  // inv_rms = 1 / sqrt(sum_k r_k^2 / K + eps) ([P4] WGSL_NORM_MATVEC_INT4),
+  // from the wave totals in wave order: the same value in every block.
+  // Block 0 writes norm_out = x * inv_rms from the staged x.
+  float inv = 1.0f;
+  if constexpr (MODE == kNorm) {
+    float ss = scratch[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) ss += scratch[w];
+    inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    if (blockIdx.x == 0 && a.norm_out) {
+      for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+        const float4 v = xl[(i & 7) * a.U + (i >> 3)];
+        reinterpret_cast<float4*>(a.norm_out)[i] = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+      }
+    }
+  }
+
   // Each column's chunk partials, summed in chunk order.
   const int64_t ncols = blk_end - blk_begin;
   for (int64_t j = threadIdx.x; j < ncols; j += blockDim.x) {
@@ -535,7 +569,7 @@ __global__ __launch_bounds__(1024) void gemv_reg_kernel(GemvArgs a) {
         for (int cc = 1; cc < nch; ++cc) s += pp[cc];
         tot[st][m] = s;
       }
-    store_column<M, MODE>(a, blk_begin + j, tot);
+    store_column<M, MODE>(a, blk_begin + j, tot, inv);
   }
 }
 
@@ -558,13 +592,14 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   constexpr int NSTREAM = MODE == kGated ? 2 : 1;
   constexpr int NSLOT = NCOL * NSTREAM;
   extern __shared__ float4 xl[];
+  float inv = 1.0f;  // inv_rms (kNorm)
 
   if constexpr (MODE == kNorm) {
     float* scratch = reinterpret_cast<float*>(xl + (size_t)8 * a.U);
-    const float inv = block_inv_rms(a, scratch);
+    inv = block_inv_rms(a, scratch);
     for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
       float4 r, v;
-      norm4(a, i, inv, r, v);
+      norm_in4(a, i, r, v);
       xl[(i & 7) * a.U + (i >> 3)] = prescale4(v);
     }
     write_norm_outputs(a, inv);
@@ -626,7 +661,7 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
       for (int st = 0; st < NSTREAM; ++st)
 #pragma unroll
         for (int m = 0; m < M; ++m) t[st][m] = acc[m][cc * NSTREAM + st];
-      store_column<M, MODE>(a, col, t);
+      store_column<M, MODE>(a, col, t, inv);
     }
   };
   const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);

@@ -91,7 +91,7 @@ def test_split4_guards(q4):
 
 # ------------------------------------------------------------------ gated
 
-@pytest.mark.parametrize("N,K,gs", [(129, 1024, 128), (1000, 4096, 128), (33, 2080, 32)])
+@pytest.mark.parametrize("N,K,gs", [(129, 1024, 128), (1000, 4096, 128), (33, 2080, 32), (19, 16416, 32)])
 def test_gated(q4, N, K, gs):
     qg, sg, zg = quantized(0xD000 + N, N, K, gs)
     qu, su, zu = quantized(0xD001 + N, N, K, gs)
@@ -132,7 +132,7 @@ def norm_inputs(seed, K):
             synth.uniform_f32(seed + 2, K, 0.5, 1.5))
 
 
-@pytest.mark.parametrize("N,K,gs", [(257, 1024, 128), (3000, 4096, 128), (61, 2080, 32)])
+@pytest.mark.parametrize("N,K,gs", [(257, 1024, 128), (3000, 4096, 128), (61, 2080, 32), (17, 16416, 32)])
 def test_norm(q4, N, K, gs):
     q, s, z = quantized(0xE000 + N, N, K, gs)
     a_a, a_b, w = norm_inputs(0xE001, K)
@@ -143,9 +143,10 @@ def test_norm(q4, N, K, gs):
     np.testing.assert_array_equal(host(r).view(np.uint32), ref["residual"].view(np.uint32))
     nn = host(nrm).astype(np.float64)
     assert np.all(np.abs(nn - ref["normed"]) <= 1e-4 * np.abs(ref["normed"]) + 1e-6)
-    # The matvec part equals int4_matvec applied to the normed vector it wrote.
+    # int4_matvec applied to the normed vector the call wrote meets the same
+    # bound (the call itself applies inv_rms to each column sum instead).
     y2 = q4.int4_matvec(nrm, *dev[3:])
-    np.testing.assert_array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+    assert_dot_close(host(y2), ref["y"], ref["B"], "matvec of norm_out")
 
 
 def test_norm_power_of_two_is_exact(q4):

@@ -44,6 +44,9 @@ SHAPES = [
     (1, 32, 32), (3, 64, 32), (37, 96, 32), (64, 1024, 128), (1000, 1024, 128),
     (129, 2048, 64), (77, 2080, 32), (250, 4096, 128), (31, 5120, 64), (9, 14336, 128),
     (300, 3072, 256), (5, 8192, 2048),
+    # K past 16384 switches the single lane from the register kernel to the
+    # LDS kernel; 40960 floats fill the 160 KiB LDS.
+    (13, 16384, 128), (11, 16416, 32), (3, 40960, 64),
 ]
 
 
