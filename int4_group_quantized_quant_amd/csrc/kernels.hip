@@ -418,16 +418,6 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   const uint32_t soff = (uint32_t)(active ? unit_group(a, u) : 0) * 4u;
   float* scratch = part + a.part_floats;
 
-  // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
-  // before step i is computed.  The first loads go out before the activations
-  // are fetched.
-  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
-  const uint32_t last = c_end > c_begin ? (uint32_t)(c_end - c_begin - 1) : 0u;
-  Step<NSLOT> s0, s1, s2;
-  if (c_begin < c_end) load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
-  if (DEPTH == 2 && c_begin + NCOL < c_end)
-    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)NCOL, last, qoff, soff, s1);
-
   // Activations: the block stages the M rows once in LDS (coalesced; for
   // the norm, x = (a_a + a_b) * w_norm and block 0 writes residual_out),
   // then each lane keeps its unit's 32 inputs in registers for the sweep.
@@ -455,6 +445,18 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
       for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(m * 8 + (i & 7)) * a.U + (i >> 3)] = src[i];
     }
   }
+  // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
+  // before step i is computed.  The first weight loads go out once the
+  // activation loads have returned (the memory counter is in order, so the
+  // staging would otherwise wait for them) and overlap the barrier.
+  // Every load is unconditional: steps past the wave's last column re-read
+  // that column, and a wave without columns has an empty buffer range, whose
+  // loads return 0 without touching memory.
+  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
+  const uint32_t last = c_end > c_begin ? (uint32_t)(c_end - c_begin - 1) : 0u;
+  Step<NSLOT> s0, s1, s2;
+  load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+  if constexpr (DEPTH == 2) load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)NCOL, last, qoff, soff, s1);
   __syncthreads();
   float x[M][32];
 #pragma unroll
@@ -492,50 +494,33 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
     }
   };
 
-  // One pipeline stage: issue the loads DEPTH groups ahead into `far`, then
-  // compute `cur` (group n).  The steady-state loop runs only while every
-  // prefetch of an iteration is in range, so it has no branch around its
-  // loads and the compiler's wait counts stay exact; the last groups run
-  // through the guarded stage.
-  auto stage_ss = [&](int64_t n, const Step<NSLOT>& cur, Step<NSLOT>& far) {
+  // One pipeline stage: issue the loads DEPTH steps ahead into `far` (past
+  // the last column they re-read it), then compute `cur` (columns n..).  No
+  // load sits behind a branch, so the compiler's wait counts stay exact and
+  // every step, the last ones included, overlaps the next loads.
+  auto stage = [&](int64_t n, const Step<NSLOT>& cur, Step<NSLOT>& far) {
     load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(n - c_begin) + DEPTH * NCOL, last, qoff, soff, far);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
     step(n, cur);
   };
-  auto stage = [&](int64_t n, const Step<NSLOT>& cur, Step<NSLOT>& far) {
-    const int64_t nf = n + DEPTH * NCOL;
-    if (nf < c_end) load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(nf - c_begin), last, qoff, soff, far);
-    __builtin_amdgcn_sched_barrier(0);
-    step(n, cur);
-    return n + NCOL < c_end;
-  };
-  int64_t n = c_begin;
-  if constexpr (DEPTH == 1) {
-    while (n + 2 * NCOL < c_end) {
-      stage_ss(n, s0, s1);
-      stage_ss(n + NCOL, s1, s0);
-      n += 2 * NCOL;
-    }
-    while (n < c_end) {
-      if (!stage(n, s0, s1)) break;
-      n += NCOL;
-      if (!stage(n, s1, s0)) break;
-      n += NCOL;
-    }
-  } else {
-    while (n + 4 * NCOL < c_end) {
-      stage_ss(n, s0, s2);
-      stage_ss(n + NCOL, s1, s0);
-      stage_ss(n + 2 * NCOL, s2, s1);
-      n += 3 * NCOL;
-    }
-    while (n < c_end) {
-      if (!stage(n, s0, s2)) break;
-      n += NCOL;
-      if (!stage(n, s1, s0)) break;
-      n += NCOL;
-      if (!stage(n, s2, s1)) break;
-      n += NCOL;
+  if (c_begin < c_end) {
+    int64_t n = c_begin;
+    if constexpr (DEPTH == 1) {
+      while (true) {
+        stage(n, s0, s1);
+        if ((n += NCOL) >= c_end) break;
+        stage(n, s1, s0);
+        if ((n += NCOL) >= c_end) break;
+      }
+    } else {
+      while (true) {
+        stage(n, s0, s2);
+        if ((n += NCOL) >= c_end) break;
+        stage(n, s1, s0);
+        if ((n += NCOL) >= c_end) break;
+        stage(n, s2, s1);
+        if ((n += NCOL) >= c_end) break;
+      }
     }
   }
   __syncthreads();
