@@ -9,38 +9,40 @@
 //
 // Shared by both matvec kernels:
 //  * A column's K/32 sixteen-byte code units are spread over the 64 lanes of
-//    a wave, so a wave's global_load_dwordx4 is one contiguous piece of one
-//    column (up to 1 KiB).  Loads of the next step are issued before the
-//    current step is computed.
-//  * Exact dequant-dot with no zero-point folding and no int->float
-//    converts: a nibble masked into the low bits of an fp16 half is the
-//    subnormal code * 2^-24; v_pk_add_f16 subtracts zero * 2^-24 exactly;
-//    v_fma_mix_f32 multiplies the fp32 activation by that fp16 (code - zero).
-//    Odd inputs use the nibble 4 bits higher (16 * code * 2^-24).  The
-//    activations are pre-scaled by 2^24 (even inputs) and 2^20 (odd inputs),
-//    exact power-of-two scalings, so a unit's sum is sum x * (code - zero)
-//    and only needs its group's scale.  Per 32 weights: 1 shift, 16 AND, 16
-//    packed-f16 subtractions, 32 mixed FMAs.
+//    a wave, so one buffer_load_dwordx4 of a wave is one contiguous piece of
+//    one column (up to 1 KiB).  Each wave addresses its columns through
+//    buffer resources (scalar base, 32-bit lane offsets), and the loads of
+//    the next step are issued before the current step is computed.
+//  * Dequant-dot with no int->float converts: a nibble masked into the low
+//    bits of an fp16 half is the subnormal code * 2^-24 (exact), and
+//    v_fma_mix_f32 multiplies the fp32 activation by it.  Odd inputs use the
+//    nibble 4 bits higher (16 * code * 2^-24).  The activations are held
+//    pre-scaled by 2^24 (even inputs) and 2^20 (odd inputs), exact
+//    power-of-two scalings, so a unit's chain is sum x * code.  The zero
+//    point is constant over a unit, so sum x * (code - zero) is that chain
+//    minus zero * sum x, with the unit's activation sum computed once per
+//    lane.  Per 32 weights: 4 shifts, 16 AND, 32 mixed FMAs, then one FMA
+//    for the zero point and one multiply by the group's scale.
 //  * Cross-lane sums are butterflies in the fixed order xor 32, xor 16 (lane
 //    swaps across wave halves / row pairs), then xor 8, 4, 2, 1 (DPP row
 //    rotations).  Several values are reduced at once by pairing them in the
 //    swap steps; every value still sees exactly the single-value tree.
 //
-// gemv_reg_kernel (one or two lanes): K is cut into nch chunks of at most 64
-// units.  A block holds P rows of nch waves; wave (p, c) owns chunk c of the
-// columns of row p, keeps the activations of its chunk in registers for the
-// whole kernel (no LDS staging), streams its columns NCOL at a time with the
-// loads DEPTH steps ahead, and writes one partial per (column, chunk) to an
-// LDS table.  After one barrier the block sums each column's partials
-// in chunk order and runs the epilogue (routing, SiLU gate, plain store).
-// Blocks are persistent: as many as fit on the device at once.
+// gemv_reg_kernel (one or two lanes, K <= 16384): K is cut into nch chunks
+// of at most 64 units.  A block holds P rows of nch waves (about 8 waves);
+// the block stages the activations once in LDS, then wave (p, c) keeps the
+// inputs of chunk c in registers, streams the columns of row p NCOL at a
+// time with the loads DEPTH steps ahead, and writes one partial per (column,
+// chunk) to an LDS table.  After one barrier the block sums each column's
+// partials in chunk order and runs the epilogue (routing, SiLU gate, norm
+// scale, plain store).  Blocks are persistent: one per CU.
 //
-// gemv_lds_kernel (three to eight lanes): the activation rows are staged in
-// LDS, transposed so lane l reads unit l's inputs with conflict-free
-// ds_read_b128; each wave walks whole columns chunk by chunk (the register
-// kernel's nch chunks of cw units), reducing every chunk across the wave and
-// summing the chunk totals in chunk order -- the register kernel's order, so
-// every lane count gives the same bits.
+// gemv_lds_kernel (three to eight lanes, or longer K): the activation rows
+// are staged in LDS, transposed so lane l reads unit l's inputs with
+// conflict-free ds_read_b128; each wave walks whole columns chunk by chunk
+// (the register kernel's nch chunks of cw units), reducing every chunk
+// across the wave and summing the chunk totals in chunk order -- the
+// register kernel's order, so every lane count gives the same bits.
 //
 // No MFMA: at one to eight lanes the work is a bandwidth-bound stream.
 #include <hip/hip_runtime.h>
