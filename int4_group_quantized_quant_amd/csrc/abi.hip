@@ -171,8 +171,13 @@ int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bp
 // streams best), columns split evenly over the B*P rows, one LDS partial per
 // (column, stream, lane, chunk), the activations staged once per block.
 //
-// LDS kernel (M >= 3 or larger K): 256-thread blocks, the M activation rows
-// staged in LDS (M*K*4 bytes), columns split evenly over the waves.
+// MFMA kernel (plain, M >= 3): one 512-thread block per CU, the M activation
+// rows staged in LDS as fp16 hi/lo planes (about M*K*4 bytes), tiles of 16
+// columns dealt to the waves.
+//
+// LDS kernel (larger K for one or two lanes, or when the MFMA planes do not
+// fit): 256-thread blocks, the M activation rows staged in LDS (M*K*4 bytes),
+// columns split evenly over the waves.
 int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   DeviceInfo dev;
   RETURN_IF(device_info(&dev));
@@ -223,6 +228,21 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     }
     // Too little LDS for the partial table and the activations: the LDS
     // kernel needs only the activations.
+  }
+  if (mode == kPlain && M >= 3 && mfma_lds_bytes(M, a.U) <= dev.lds_block) {
+    // Matrix-core lanes: one 8-wave block per CU, tiles of 16 columns.
+    const int64_t tiles = (N + 15) / 16;
+    s->variant = kVariantMfma;
+    s->ncol = 16;
+    s->depth = 1;
+    s->block_threads = 512;
+    s->lds_bytes = mfma_lds_bytes(M, a.U);
+    int64_t B = dev.cus;
+    if (B > tiles) B = tiles;
+    if (B < 1) B = 1;
+    s->grid = (int)B;
+    a.total_waves = B * 8;
+    return INT4_OK;
   }
   const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode == kNorm ? 64 : 0);
   if (lds > dev.lds_block)

@@ -50,7 +50,12 @@ __host__ __device__ inline int x_lds_offset(int part_floats) { return (part_floa
 enum Variant : int {
   kVariantLds = 0,  // activations staged in LDS, one wave per column group
   kVariantReg = 1,  // activations in registers, one wave per (row, K chunk)
+  kVariantMfma = 2, // three to eight lanes on the matrix cores, 16-column tiles
 };
+
+// LDS bytes of the MFMA lane kernel: hi and lo fp16 planes of M rows over
+// the K/32 units padded to a multiple of 4.
+inline size_t mfma_lds_bytes(int M, int U) { return (size_t)((U + 3) & ~3) * 128u * (size_t)M; }
 
 struct LaunchShape {
   int variant;        // Variant

@@ -780,6 +780,292 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restr
 
 // ------------------------------------------------------------ dispatch
 
+// ------------------------------------------------------------ MFMA lane kernel
+
+// Three to eight decode lanes on the matrix cores: v_mfma_f32_16x16x32_f16
+// with D[m][col] = sum_k A[m][k] * B[k][col] over one 32-input unit, where
+//  * B[k][col] = (code - zero) * 2^-24, the nibble masked into an fp16
+//    subnormal and the zero point subtracted with v_pk_add_f16, both exact
+//    (the matrix cores keep fp16 subnormal inputs);
+//  * A[m][k] = x[m][k] * 2^e_m split into two fp16 parts hi + lo (hi the
+//    rounded value, lo the rounded remainder), e_m a power of two that puts
+//    the row's largest |x| just below 2^14; the two MFMAs accumulate the
+//    exact products hi*B and lo*B in fp32.
+// Lane l of a wave holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16]
+// and D[4*(l/16) .. +3][l%16].  A 16-column tile is streamed with one 16-byte
+// unit per lane: lane (col, g) loads unit 4s+g of column col, and a 4x4
+// transpose across the lane groups (two permlane32 and two permlane16
+// swaps) leaves word g of unit 4s+t in register t, so step t's MFMA covers
+// exactly unit 4s+t, which lies in one group.  Each unit's D is scaled by
+// its group's scale into the lane's four accumulators; at the end of a tile
+// the rows m < M are multiplied by 2^(24 - e_m) and stored.  Rows of A are
+// independent, so a lane's outputs never depend on the other lanes.
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaDepth = 3;  // quads of loads in flight ahead of the compute
+
+struct Quad {
+  u32x4 q;  // one 16-byte unit of the lane's column
+  u32x4 s;  // scales of the four groups from the quad's first group on
+  u32x4 z;  // zero points of the same groups
+};
+
+// Rows of 16 lanes x 4 registers, transposed: register t of lane group g
+// ends up holding what register g of lane group t held.
+__device__ __forceinline__ void transpose4x4(u32x4& w) {
+  auto a = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  w.x = c[0];
+  w.y = c[1];
+  w.z = d[0];
+  w.w = d[1];
+}
+
+__device__ __forceinline__ uint32_t pick4(u32x4 v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// 2^e as a float, e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) { return bitsf((uint32_t)(e + 127) << 23); }
+
+// e_m for a row whose largest magnitude is amax: amax * 2^e < 2^14.
+__device__ __forceinline__ int row_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int biased = (int)((fbits(amax) >> 23) & 0xFFu);
+  const int E = biased == 0 ? -126 : biased - 126;  // amax < 2^E
+  const int e = 14 - E;
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
+  extern __shared__ float4 lds4[];
+  const int M = a.M;
+  const int K = a.K;
+  const int U = a.U;
+  const int Up = (U + 3) & ~3;  // units padded to whole quads
+  const int S = Up >> 2;        // quads per column
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+
+  // 1. Largest |x| of every row, over the block.
+  float* red = reinterpret_cast<float*>(lds4);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    if (m >= M) break;
+    float mx = 0.0f;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) mx = fmaxf(mx, fabsf(a.x[(int64_t)m * K + k]));
+    mx = wave_max(mx);
+    if (lane == 0) red[m * nwaves + wave] = mx;
+  }
+  __syncthreads();
+  float p2[8];       // 2^e_m, the exact pre-scale of row m
+  float outf[4];     // 2^(24 - e_m) for this lane's output rows m = 4*(lane/16) + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) outf[r] = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    p2[m] = 1.0f;
+    if (m < M) {
+      float mx = red[m * nwaves];
+      for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, red[m * nwaves + w]);
+      const int e = row_exponent(mx);
+      p2[m] = pow2f(e);
+      const float f = pow2f(24 - e);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * (lane >> 4) + r == m) outf[r] = f;
+    }
+  }
+  __syncthreads();
+
+  // 2. Stage A: entry (u*4 + g)*M + m of the hi plane (lo plane after it)
+  // holds the 8 fp16 values of row m for MFMA k-slots 8g .. 8g+7 of unit u;
+  // slot 8g + 2v is input 32u + 8g + v and slot 8g + 2v + 1 is input
+  // 32u + 8g + v + 4 (the order the nibble masks produce).  Units past the
+  // end of K are zero.
+  const int plane = Up * 4 * M;
+  half8_t* hi_plane = reinterpret_cast<half8_t*>(lds4);
+  half8_t* lo_plane = hi_plane + plane;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    if (m >= M) break;
+    const float sc = p2[m];
+    for (int ug = threadIdx.x; ug < Up * 4; ug += blockDim.x) {
+      const int u = ug >> 2, g = ug & 3;
+      half8_t h, l;
+      if (u < U) {
+        const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * K + 32 * u + 8 * g);
+        const float4 v0 = src[0], v1 = src[1];
+        const float xv[8] = {v0.x, v1.x, v0.y, v1.y, v0.z, v1.z, v0.w, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xs = xv[e] * sc;
+          const _Float16 hh = (_Float16)xs;
+          h[e] = hh;
+          l[e] = (_Float16)(xs - (float)hh);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          h[e] = (_Float16)0.0f;
+          l[e] = (_Float16)0.0f;
+        }
+      }
+      hi_plane[ug * M + m] = h;
+      lo_plane[ug * M + m] = l;
+    }
+  }
+  __syncthreads();
+
+  // 3. Tiles of 16 columns: block b owns tiles [tb, te), wave w takes tiles
+  // tb + w, tb + w + nwaves, ...
+  const int64_t T = (a.N + 15) >> 4;
+  const int64_t tb = uniform_i64((int64_t)blockIdx.x * T / gridDim.x);
+  const int64_t te = uniform_i64(((int64_t)blockIdx.x + 1) * T / gridDim.x);
+  const int64_t ntiles = te - tb > wave ? (te - tb - wave + nwaves - 1) / nwaves : 0;
+  const int64_t nsteps = ntiles * S;
+  if (nsteps == 0) return;
+
+  const int col_l = lane & 15;
+  const int g = lane >> 4;
+  const int m_a = col_l;  // A row of this lane
+  const bool a_live = m_a < M;
+  const int m_c = a_live ? m_a : M - 1;
+  const uint32_t qcol = (uint32_t)a.U * 16u;
+  const uint32_t gcol = (uint32_t)a.G * 4u;
+
+  // Steps are (tile i, quad s) pairs walked in order; `Cursor` advances one
+  // step with no division.  Loads past the last step re-read it.
+  struct Cursor {
+    int64_t i;
+    int s;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.s == S) {
+      c.s = 0;
+      ++c.i;
+    }
+  };
+  auto load_step = [&](Cursor c, Quad& r) {
+    if (c.i >= ntiles) {
+      c.i = ntiles - 1;
+      c.s = S - 1;
+    }
+    const int64_t col0 = (tb + wave + c.i * nwaves) * 16;
+    const int64_t ncols = a.N - col0 < 16 ? a.N - col0 : 16;
+    const uint32_t cl = (uint32_t)(col_l < ncols ? col_l : ncols - 1);
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.q[0]) + col0 * qcol), (short)0, (int)(ncols * qcol), kBufferWord3);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.s[0]) + col0 * gcol), (short)0, (int)(ncols * gcol), kBufferWord3);
+    const auto rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.z[0]) + col0 * gcol), (short)0, (int)(ncols * gcol), kBufferWord3);
+    const uint32_t g0 = (uint32_t)unit_group(a, 4 * c.s);
+    r.q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rq, (cl * (uint32_t)a.U + 4u * c.s + g) * 16u, 0, kLoadNonTemporal));
+    r.s = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (cl * (uint32_t)a.G + g0) * 4u, 0, 0));
+    r.z = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (cl * (uint32_t)a.G + g0) * 4u, 0, 0));
+  };
+
+  // This lane's A entries: byte offset of row m_c, lane group g within a
+  // unit's block of 4*M entries; rows m >= M read row M-1 and are masked to 0.
+  const uint32_t a_lane = (uint32_t)(g * M + m_c) * 16u;
+  const uint32_t a_unit = (uint32_t)(4 * M) * 16u;
+  const uint32_t a_mask = a_live ? 0xFFFFFFFFu : 0u;
+  const char* hi_bytes = reinterpret_cast<const char*>(hi_plane);
+  const char* lo_bytes = reinterpret_cast<const char*>(lo_plane);
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](Cursor c, Quad r) {
+    const int s = c.s;
+    const int g0 = unit_group(a, 4 * s);
+    transpose4x4(r.q);
+    const uint32_t words[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int u = 4 * s + t;
+      const int j = uniform_int(unit_group(a, u) - g0);
+      const float sv = bitsf(pick4(r.s, j));
+      const uint32_t zi = (uint32_t)bitsf(pick4(r.z, j));
+      const half2_t zh = as_half2(zi | (zi << 16));
+      u32x4 bw;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        bw[v] = __builtin_bit_cast(uint32_t, as_half2((words[t] >> (4 * v)) & 0x000F000Fu) - zh);
+      const uint32_t off = (uint32_t)u * a_unit + a_lane;
+      const u32x4 ah = *reinterpret_cast<const u32x4*>(hi_bytes + off) & a_mask;
+      const u32x4 al = *reinterpret_cast<const u32x4*>(lo_bytes + off) & a_mask;
+      const half8_t b = __builtin_bit_cast(half8_t, bw);
+      const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah), b, z4, 0, 0, 0);
+      d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al), b, d4, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d4[rr], acc[rr]);
+    }
+    if (s == S - 1) {
+      const int64_t col = (tb + wave + c.i * nwaves) * 16 + col_l;
+      if (col < a.N) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int m = 4 * g + rr;
+          if (m < M) a.out[0][(int64_t)m * a.N + col] = acc[rr] * outf[rr];
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
+    }
+  };
+
+  // Ring of kMfmaDepth + 1 quads; every load is unconditional.
+  static_assert(kMfmaDepth == 3, "the ring below holds four quads");
+  Quad r0, r1, r2, r3;
+  Cursor lc = {0, 0}, cc = {0, 0};
+  load_step(lc, r0);
+  advance(lc);
+  load_step(lc, r1);
+  advance(lc);
+  load_step(lc, r2);
+  advance(lc);
+  int64_t n = 0;
+  while (true) {
+    load_step(lc, r3);
+    advance(lc);
+    __builtin_amdgcn_sched_barrier(0);
+    step(cc, r0);
+    advance(cc);
+    if (++n >= nsteps) break;
+    load_step(lc, r0);
+    advance(lc);
+    __builtin_amdgcn_sched_barrier(0);
+    step(cc, r1);
+    advance(cc);
+    if (++n >= nsteps) break;
+    load_step(lc, r1);
+    advance(lc);
+    __builtin_amdgcn_sched_barrier(0);
+    step(cc, r2);
+    advance(cc);
+    if (++n >= nsteps) break;
+    load_step(lc, r2);
+    advance(lc);
+    __builtin_amdgcn_sched_barrier(0);
+    step(cc, r3);
+    advance(cc);
+    if (++n >= nsteps) break;
+  }
+}
+
 template <typename Kern>
 hipError_t raise_lds_once(Kern kern, std::atomic<bool>& done, const LaunchShape& s) {
   // Dynamic LDS beyond 64 KiB must be allowed per kernel; once, for the
@@ -843,6 +1129,10 @@ hipError_t dispatch_lds_m(const GemvArgs& a, const LaunchShape& s, hipStream_t s
 }
 
 hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if (s.variant == kVariantMfma) {
+    static std::atomic<bool> raised{false};
+    return launch_or_query(gemv_mfma_kernel, raised, a, s, st, occ);
+  }
   if (s.variant == kVariantReg) {
     switch (mode) {
       case kSplit4: return dispatch_reg<kSplit4>(a, s, st, occ);

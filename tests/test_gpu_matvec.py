@@ -2,8 +2,10 @@
 
 Ragged shapes (N not a multiple of the column step, K not a multiple of the
 64-unit chunk), every group size the kernels accept, one-hot and
-integer-exact closed forms (bitwise), lane independence (bitwise against the
-single-lane call), and untouched memory around the outputs."""
+integer-exact closed forms (bitwise), lane independence (bitwise: against
+the single-lane call for one and two lanes, against calls with every other
+row replaced for the matrix-core lanes), and untouched memory around the
+outputs."""
 import numpy as np
 import pytest
 
@@ -60,7 +62,9 @@ def test_single_lane(q4, N, K, gs):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K,gs", [(203, 1024, 128), (65, 5120, 64)])
+@pytest.mark.parametrize("N,K,gs", [(203, 1024, 128), (65, 5120, 64),
+                                    (77, 2080, 32),    # K/32 not a multiple of 4
+                                    (50, 3072, 96)])   # three units per group
 def test_lanes(q4, M, N, K, gs):
     q, s, z = quantized(0xB100 + M, N, K, gs)
     X = synth.lanes(0xB101, M, K)
@@ -68,10 +72,20 @@ def test_lanes(q4, M, N, K, gs):
     Y = run_matvec(q4, X, q, s, z)
     assert Y.shape == (M, N)
     assert_dot_close(Y, Y_ref, B, f"lanes M={M}")
-    # Lanes never interact, and each lane's arithmetic is the single-lane one.
-    for m in range(M):
-        y1 = run_matvec(q4, X[m], q, s, z)
-        np.testing.assert_array_equal(Y[m].view(np.uint32), y1.view(np.uint32))
+    if M <= 2:
+        # One and two lanes share the register kernel's per-lane arithmetic:
+        # each lane's bits are the single-lane call's.
+        for m in range(M):
+            y1 = run_matvec(q4, X[m], q, s, z)
+            np.testing.assert_array_equal(Y[m].view(np.uint32), y1.view(np.uint32))
+    else:
+        # Matrix-core lanes never interact: replacing every other row leaves
+        # a row's outputs bit-identical.
+        for keep in (0, M - 1):
+            X2 = synth.lanes(0xB102 + keep, M, K)
+            X2[keep] = X[keep]
+            Y2 = run_matvec(q4, X2, q, s, z)
+            np.testing.assert_array_equal(Y2[keep].view(np.uint32), Y[keep].view(np.uint32))
 
 
 @pytest.mark.parametrize("K,gs", [(256, 32), (1024, 128), (2080, 32), (5120, 64)])
