@@ -229,7 +229,8 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // Too little LDS for the partial table and the activations: the LDS
     // kernel needs only the activations.
   }
-  if (mode == kPlain && M >= 3 && mfma_lds_bytes(M, a.U) <= dev.lds_block) {
+  if (mode == kPlain && M >= 3 && mfma_lds_bytes(M, a.U) <= dev.lds_block &&
+      (int64_t)((a.U + 3) & ~3) * 4 * M <= 5120) {
     // Matrix-core lanes: one 8-wave block per CU, tiles of 16 columns.
     const int64_t tiles = (N + 15) / 16;
     s->variant = kVariantMfma;

@@ -54,7 +54,9 @@ enum Variant : int {
 };
 
 // LDS bytes of the MFMA lane kernel: hi and lo fp16 planes of M rows over
-// the K/32 units padded to a multiple of 4.
+// the K/32 units padded to a multiple of 4.  The kernel stages at most 5120
+// (unit, lane group) row entries, (K/32 rounded up to 4) * 4 * M <= 5120,
+// which is exactly what 160 KiB of planes hold.
 inline size_t mfma_lds_bytes(int M, int U) { return (size_t)((U + 3) & ~3) * 128u * (size_t)M; }
 
 struct LaunchShape {

@@ -804,12 +804,56 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restr
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaDepth = 3;  // quads of loads in flight ahead of the compute
+constexpr int kMfmaDepth = 5;  // quads of loads in flight ahead of the compute
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pick4(u32x4 v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// Groups a quad of units can touch: 4 when a group is one unit (or of a
+// size that is not 2 or a multiple of 4), 2 for two-unit groups, 1 when the
+// group size is a multiple of 4 units.  Loading exactly these keeps every
+// loaded register live, so the register allocator never reuses one that a
+// load in flight will still write (which would force a full wait).
+template <int GSU>
+struct QuadGroups {
+  static constexpr int n = GSU == 2 ? 2 : (GSU == 4 ? 1 : 4);
+};
+
+template <int NG>
+struct GroupVals;
+template <>
+struct GroupVals<4> {
+  u32x4 v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
+  __device__ __forceinline__ uint32_t get(int j) const { return pick4(v, j); }
+};
+template <>
+struct GroupVals<2> {
+  u32x2 v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  }
+  __device__ __forceinline__ uint32_t get(int j) const { return j == 0 ? v.x : v.y; }
+};
+template <>
+struct GroupVals<1> {
+  uint32_t v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    v = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+  __device__ __forceinline__ uint32_t get(int) const { return v; }
+};
+
+template <int GSU>
 struct Quad {
-  u32x4 q;  // one 16-byte unit of the lane's column
-  u32x4 s;  // scales of the four groups from the quad's first group on
-  u32x4 z;  // zero points of the same groups
+  u32x4 q;                                   // one 16-byte unit of the lane's column
+  GroupVals<QuadGroups<GSU>::n> s;           // scales from the quad's first group on
+  GroupVals<QuadGroups<GSU>::n> z;           // zero points of the same groups
 };
 
 // Rows of 16 lanes x 4 registers, transposed: register t of lane group g
@@ -825,9 +869,6 @@ __device__ __forceinline__ void transpose4x4(u32x4& w) {
   w.w = d[1];
 }
 
-__device__ __forceinline__ uint32_t pick4(u32x4 v, int j) {
-  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
-}
 
 // 2^e as a float, e in [-126, 127].
 __device__ __forceinline__ float pow2f(int e) { return bitsf((uint32_t)(e + 127) << 23); }
@@ -841,89 +882,147 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return e < -100 ? -100 : (e > 100 ? 100 : e);
 }
 
+// Largest value over the wave (butterfly with the same swaps and DPP row
+// rotations as the sums).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  auto r32 = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+  v = fmaxf(bitsf(r32[0]), bitsf(r32[1]));
+  auto r16 = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  v = fmaxf(bitsf(r16[0]), bitsf(r16[1]));
+  v = fmaxf(v, dpp_move<0x128>(v));
+  v = fmaxf(v, dpp_move<0x124>(v));
+  v = fmaxf(v, dpp_move<0x122>(v));
+  v = fmaxf(v, dpp_move<0x121>(v));
+  return bitsf(__builtin_amdgcn_readfirstlane(fbits(v)));
 }
 
+// Group offset of unit t of a quad (t = 0..3) from the quad's first group.
+// GSU is the group size in units when it is 1 or 2, 4 when it is a multiple
+// of 4 (a quad then lies in one group), and 0 for any other size (the offset
+// is computed from the unit-in-group counter uig, uniform over the wave).
+template <int GSU>
+__device__ __forceinline__ int quad_group_offset(int t, int uig, int gsu) {
+  if constexpr (GSU == 1) return t;
+  if constexpr (GSU == 2) return t >> 1;
+  if constexpr (GSU == 4) return 0;
+  int j = 0;
+  j += (uig + t >= gsu) ? 1 : 0;
+  j += (uig + t >= 2 * gsu) ? 1 : 0;
+  j += (uig + t >= 3 * gsu) ? 1 : 0;
+  return j;
+}
+
+// Slot of row m of entry ug in an A plane (16-byte slots, M per entry).
+// For M = 4 and 8 the row is XOR-swizzled with bits of ug so that 16
+// consecutive entries written for one row, and the M rows of one entry read
+// by the MFMA lanes, both fall on distinct LDS banks; odd M needs no swizzle
+// (its stride is already odd), M = 6 keeps a two-way conflict.
+template <int M>
+__device__ __forceinline__ int a_slot(int ug, int m) {
+  if constexpr (M == 8) return ug * 8 + (m ^ ((ug >> 1) & 7));
+  if constexpr (M == 4) return ug * 4 + (m ^ ((ug >> 2) & 3));
+  return ug * M + m;
+}
+
+template <int MR, int GSU>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ float4 lds4[];
-  const int M = a.M;
+  constexpr int M = MR;
+  // Staging entries per thread: the LDS holds at most 160 KiB of planes,
+  // i.e. at most 5120 / M entries of (unit, lane group) for M rows.
+  constexpr int kEntries = (5120 / M + 511) / 512;
   const int K = a.K;
   const int U = a.U;
+  const int G = a.G;
+  const int gsu = U / G;        // units per group
   const int Up = (U + 3) & ~3;  // units padded to whole quads
   const int S = Up >> 2;        // quads per column
   const int lane = threadIdx.x & 63;
   const int wave = uniform_int(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
 
-  // 1. Largest |x| of every row, over the block.
+  // 1. One pass over the activations: each thread loads the M rows of its
+  // (unit, lane group) entries (8 inputs each) together, keeps them in
+  // registers, and the block reduces every row's largest magnitude.
+  // Entry ug = u*4 + g covers inputs 32u + 8g .. +7; units past K are zero.
+  const int nug = Up * 4;
+  float4 v0[kEntries][M], v1[kEntries][M];
+#pragma unroll
+  for (int e = 0; e < kEntries; ++e) {
+    const int ug = threadIdx.x + e * blockDim.x;
+    const int u = ug >> 2, g = ug & 3;
+    const bool live = ug < nug && u < U;
+    const int uc = live ? u : 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * K + 32 * uc + 8 * g);
+      v0[e][m] = src[0];
+      v1[e][m] = src[1];
+      if (!live) {
+        v0[e][m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        v1[e][m] = v0[e][m];
+      }
+    }
+  }
   float* red = reinterpret_cast<float*>(lds4);
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m >= M) break;
+  for (int m = 0; m < M; ++m) {
     float mx = 0.0f;
-    for (int k = threadIdx.x; k < K; k += blockDim.x) mx = fmaxf(mx, fabsf(a.x[(int64_t)m * K + k]));
-    mx = wave_max(mx);
-    if (lane == 0) red[m * nwaves + wave] = mx;
+#pragma unroll
+    for (int e = 0; e < kEntries; ++e) {
+      const float4 p = v0[e][m], q = v1[e][m];
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(p.x), fabsf(p.y)), fmaxf(fabsf(p.z), fabsf(p.w))));
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
+    }
+    const float w = wave_max(mx);
+    if (lane == 0) red[m * nwaves + wave] = w;
   }
   __syncthreads();
-  float p2[8];       // 2^e_m, the exact pre-scale of row m
-  float outf[4];     // 2^(24 - e_m) for this lane's output rows m = 4*(lane/16) + r
+  float rowmax[M];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) outf[r] = 0.0f;
+  for (int m = 0; m < M; ++m) {
+    rowmax[m] = red[m * nwaves];
+    for (int w = 1; w < nwaves; ++w) rowmax[m] = fmaxf(rowmax[m], red[m * nwaves + w]);
+  }
+  float outf[4];  // 2^(24 - e_m) for this lane's output rows m = 4*(lane/16) + r
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    p2[m] = 1.0f;
-    if (m < M) {
-      float mx = red[m * nwaves];
-      for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, red[m * nwaves + w]);
-      const int e = row_exponent(mx);
-      p2[m] = pow2f(e);
-      const float f = pow2f(24 - e);
+  for (int r = 0; r < 4; ++r) {
+    outf[r] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * (lane >> 4) + r == m) outf[r] = f;
-    }
+    for (int m = 0; m < M; ++m)
+      if (4 * (lane >> 4) + r == m) outf[r] = pow2f(24 - row_exponent(rowmax[m]));
   }
   __syncthreads();
 
-  // 2. Stage A: entry (u*4 + g)*M + m of the hi plane (lo plane after it)
-  // holds the 8 fp16 values of row m for MFMA k-slots 8g .. 8g+7 of unit u;
-  // slot 8g + 2v is input 32u + 8g + v and slot 8g + 2v + 1 is input
-  // 32u + 8g + v + 4 (the order the nibble masks produce).  Units past the
-  // end of K are zero.
+  // 2. Stage A from the registers: entry (u*4 + g)*M + m of the hi plane (lo
+  // plane after it) holds the 8 fp16 values of row m for MFMA k-slots
+  // 8g .. 8g+7 of unit u; slot 8g + 2v is input 32u + 8g + v and slot
+  // 8g + 2v + 1 is input 32u + 8g + v + 4 (the order the nibble masks
+  // produce).  x * 2^e_m is split into hi = fp16(x * 2^e_m) and
+  // lo = fp16(x * 2^e_m - hi).
   const int plane = Up * 4 * M;
   half8_t* hi_plane = reinterpret_cast<half8_t*>(lds4);
   half8_t* lo_plane = hi_plane + plane;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m >= M) break;
-    const float sc = p2[m];
-    for (int ug = threadIdx.x; ug < Up * 4; ug += blockDim.x) {
-      const int u = ug >> 2, g = ug & 3;
-      half8_t h, l;
-      if (u < U) {
-        const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * K + 32 * u + 8 * g);
-        const float4 v0 = src[0], v1 = src[1];
-        const float xv[8] = {v0.x, v1.x, v0.y, v1.y, v0.z, v1.z, v0.w, v1.w};
+  for (int e = 0; e < kEntries; ++e) {
+    const int ug = threadIdx.x + e * blockDim.x;
+    if (ug < nug) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xs = xv[e] * sc;
+      for (int m = 0; m < M; ++m) {
+        const float sc = pow2f(row_exponent(rowmax[m]));
+        const float4 p = v0[e][m], q = v1[e][m];
+        const float xv[8] = {p.x, q.x, p.y, q.y, p.z, q.z, p.w, q.w};
+        half8_t h, l;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float xs = xv[k] * sc;
           const _Float16 hh = (_Float16)xs;
-          h[e] = hh;
-          l[e] = (_Float16)(xs - (float)hh);
+          h[k] = hh;
+          l[k] = (_Float16)(xs - (float)hh);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          h[e] = (_Float16)0.0f;
-          l[e] = (_Float16)0.0f;
-        }
+        hi_plane[a_slot<M>(ug, m)] = h;
+        lo_plane[a_slot<M>(ug, m)] = l;
       }
-      hi_plane[ug * M + m] = h;
-      lo_plane[ug * M + m] = l;
     }
   }
   __syncthreads();
@@ -934,36 +1033,20 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
   const int64_t tb = uniform_i64((int64_t)blockIdx.x * T / gridDim.x);
   const int64_t te = uniform_i64(((int64_t)blockIdx.x + 1) * T / gridDim.x);
   const int64_t ntiles = te - tb > wave ? (te - tb - wave + nwaves - 1) / nwaves : 0;
-  const int64_t nsteps = ntiles * S;
-  if (nsteps == 0) return;
 
   const int col_l = lane & 15;
   const int g = lane >> 4;
   const int m_a = col_l;  // A row of this lane
-  const bool a_live = m_a < M;
-  const int m_c = a_live ? m_a : M - 1;
-  const uint32_t qcol = (uint32_t)a.U * 16u;
-  const uint32_t gcol = (uint32_t)a.G * 4u;
+  const uint32_t a_mask = m_a < M ? 0xFFFFFFFFu : 0u;
+  const int m_c = m_a < M ? m_a : M - 1;
+  const char* hi_bytes = reinterpret_cast<const char*>(hi_plane);
+  const char* lo_bytes = reinterpret_cast<const char*>(lo_plane);
+  const uint32_t qcol = (uint32_t)U * 16u;
+  const uint32_t gcol = (uint32_t)G * 4u;
 
-  // Steps are (tile i, quad s) pairs walked in order; `Cursor` advances one
-  // step with no division.  Loads past the last step re-read it.
-  struct Cursor {
-    int64_t i;
-    int s;
-  };
-  auto advance = [&](Cursor& c) {
-    if (++c.s == S) {
-      c.s = 0;
-      ++c.i;
-    }
-  };
-  auto load_step = [&](Cursor c, Quad& r) {
-    if (c.i >= ntiles) {
-      c.i = ntiles - 1;
-      c.s = S - 1;
-    }
-    const int64_t col0 = (tb + wave + c.i * nwaves) * 16;
-    const int64_t ncols = a.N - col0 < 16 ? a.N - col0 : 16;
+  for (int64_t i = 0; i < ntiles; ++i) {
+    const int64_t col0 = (tb + wave + i * nwaves) * 16;
+    const int ncols = a.N - col0 < 16 ? (int)(a.N - col0) : 16;
     const uint32_t cl = (uint32_t)(col_l < ncols ? col_l : ncols - 1);
     const auto rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(reinterpret_cast<const char*>(a.q[0]) + col0 * qcol), (short)0, (int)(ncols * qcol), kBufferWord3);
@@ -971,98 +1054,112 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
         (void*)(reinterpret_cast<const char*>(a.s[0]) + col0 * gcol), (short)0, (int)(ncols * gcol), kBufferWord3);
     const auto rz = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(reinterpret_cast<const char*>(a.z[0]) + col0 * gcol), (short)0, (int)(ncols * gcol), kBufferWord3);
-    const uint32_t g0 = (uint32_t)unit_group(a, 4 * c.s);
-    r.q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                        rq, (cl * (uint32_t)a.U + 4u * c.s + g) * 16u, 0, kLoadNonTemporal));
-    r.s = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (cl * (uint32_t)a.G + g0) * 4u, 0, 0));
-    r.z = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (cl * (uint32_t)a.G + g0) * 4u, 0, 0));
-  };
+    const uint32_t vq = (cl * (uint32_t)U + (uint32_t)g) * 16u;
+    const uint32_t vs = cl * (uint32_t)G * 4u;
 
-  // This lane's A entries: byte offset of row m_c, lane group g within a
-  // unit's block of 4*M entries; rows m >= M read row M-1 and are masked to 0.
-  const uint32_t a_lane = (uint32_t)(g * M + m_c) * 16u;
-  const uint32_t a_unit = (uint32_t)(4 * M) * 16u;
-  const uint32_t a_mask = a_live ? 0xFFFFFFFFu : 0u;
-  const char* hi_bytes = reinterpret_cast<const char*>(hi_plane);
-  const char* lo_bytes = reinterpret_cast<const char*>(lo_plane);
-
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto step = [&](Cursor c, Quad r) {
-    const int s = c.s;
-    const int g0 = unit_group(a, 4 * s);
-    transpose4x4(r.q);
-    const uint32_t words[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+    // Load cursor: quad ls and its first group lg (uniform).  Loads past the
+    // column's last quad re-read it.
+    int ls = 0, lg = 0, luig = 0;
+    auto load = [&](Quad<GSU>& r) {
+      r.q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq, 64u * (uint32_t)ls,
+                                                                            kLoadNonTemporal));
+      r.s.load(rs, vs, 4u * (uint32_t)lg);
+      r.z.load(rz, vs, 4u * (uint32_t)lg);
+      // Advance one quad (none past the last), branch-free.
+      const int adv = ls + 1 < S ? 1 : 0;
+      const int t4 = luig + 4 * adv;
+      const int inc = (t4 >= gsu ? 1 : 0) + (t4 >= 2 * gsu ? 1 : 0) + (t4 >= 3 * gsu ? 1 : 0) +
+                      (t4 >= 4 * gsu ? 1 : 0);
+      ls += adv;
+      lg += inc;
+      luig = t4 - inc * gsu;
+    };
+    // Compute cursor: quad cs, first group's unit-in-group counter cuig.
+    int cs = 0, cuig = 0;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](Quad<GSU> r) {
+      // The quad's A operands first: eight LDS reads in flight together.
+      u32x4 ah[4], al[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int u = 4 * s + t;
-      const int j = uniform_int(unit_group(a, u) - g0);
-      const float sv = bitsf(pick4(r.s, j));
-      const uint32_t zi = (uint32_t)bitsf(pick4(r.z, j));
-      const half2_t zh = as_half2(zi | (zi << 16));
-      u32x4 bw;
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        bw[v] = __builtin_bit_cast(uint32_t, as_half2((words[t] >> (4 * v)) & 0x000F000Fu) - zh);
-      const uint32_t off = (uint32_t)u * a_unit + a_lane;
-      const u32x4 ah = *reinterpret_cast<const u32x4*>(hi_bytes + off) & a_mask;
-      const u32x4 al = *reinterpret_cast<const u32x4*>(lo_bytes + off) & a_mask;
-      const half8_t b = __builtin_bit_cast(half8_t, bw);
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t off = (uint32_t)a_slot<M>(4 * (4 * cs + t) + g, m_c) * 16u;
+        ah[t] = *reinterpret_cast<const u32x4*>(hi_bytes + off) & a_mask;
+        al[t] = *reinterpret_cast<const u32x4*>(lo_bytes + off) & a_mask;
+      }
+      transpose4x4(r.q);
+      const uint32_t words[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
       const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-      f32x4_t d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah), b, z4, 0, 0, 0);
-      d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al), b, d4, 0, 0, 0);
+      f32x4_t d4 = z4;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d4[rr], acc[rr]);
-    }
-    if (s == S - 1) {
-      const int64_t col = (tb + wave + c.i * nwaves) * 16 + col_l;
-      if (col < a.N) {
+      for (int t = 0; t < 4; ++t) {
+        const int j = quad_group_offset<GSU>(t, cuig, gsu);
+        const uint32_t zi = (uint32_t)bitsf(r.z.get(j));
+        const half2_t zh = as_half2(zi | (zi << 16));
+        u32x4 bw;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int m = 4 * g + rr;
-          if (m < M) a.out[0][(int64_t)m * a.N + col] = acc[rr] * outf[rr];
+        for (int v = 0; v < 4; ++v)
+          bw[v] = __builtin_bit_cast(uint32_t, as_half2((words[t] >> (4 * v)) & 0x000F000Fu) - zh);
+        const half8_t b = __builtin_bit_cast(half8_t, bw);
+        // Units of one group accumulate in the matrix core; the group's
+        // scale is applied once its last unit of the quad is in.
+        const bool first = GSU == 0 || GSU == 1 || (GSU == 2 && (t & 1) == 0) || (GSU == 4 && t == 0);
+        const bool last = GSU == 0 || GSU == 1 || (GSU == 2 && (t & 1) == 1) || (GSU == 4 && t == 3);
+        d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[t]), b, first ? z4 : d4, 0, 0, 0);
+        d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[t]), b, d4, 0, 0, 0);
+        if (last) {
+          const float sv = bitsf(r.s.get(j));
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d4[rr], acc[rr]);
         }
       }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
-    }
-  };
+      ++cs;
+      const int t4 = cuig + 4;
+      cuig = t4 - gsu * ((t4 >= gsu ? 1 : 0) + (t4 >= 2 * gsu ? 1 : 0) + (t4 >= 3 * gsu ? 1 : 0) +
+                         (t4 >= 4 * gsu ? 1 : 0));
+    };
 
-  // Ring of kMfmaDepth + 1 quads; every load is unconditional.
-  static_assert(kMfmaDepth == 3, "the ring below holds four quads");
-  Quad r0, r1, r2, r3;
-  Cursor lc = {0, 0}, cc = {0, 0};
-  load_step(lc, r0);
-  advance(lc);
-  load_step(lc, r1);
-  advance(lc);
-  load_step(lc, r2);
-  advance(lc);
-  int64_t n = 0;
-  while (true) {
-    load_step(lc, r3);
-    advance(lc);
-    __builtin_amdgcn_sched_barrier(0);
-    step(cc, r0);
-    advance(cc);
-    if (++n >= nsteps) break;
-    load_step(lc, r0);
-    advance(lc);
-    __builtin_amdgcn_sched_barrier(0);
-    step(cc, r1);
-    advance(cc);
-    if (++n >= nsteps) break;
-    load_step(lc, r1);
-    advance(lc);
-    __builtin_amdgcn_sched_barrier(0);
-    step(cc, r2);
-    advance(cc);
-    if (++n >= nsteps) break;
-    load_step(lc, r2);
-    advance(lc);
-    __builtin_amdgcn_sched_barrier(0);
-    step(cc, r3);
-    advance(cc);
-    if (++n >= nsteps) break;
+    // Ring of kMfmaDepth + 1 quads; every load is unconditional.
+    static_assert(kMfmaDepth == 5, "the ring below holds six quads");
+    Quad<GSU> r0, r1, r2, r3, r4, r5;
+    load(r0);
+    load(r1);
+    load(r2);
+    load(r3);
+    load(r4);
+    while (true) {
+      load(r5);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r0);
+      if (cs >= S) break;
+      load(r0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r1);
+      if (cs >= S) break;
+      load(r1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r2);
+      if (cs >= S) break;
+      load(r2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r3);
+      if (cs >= S) break;
+      load(r3);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r4);
+      if (cs >= S) break;
+      load(r4);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(r5);
+      if (cs >= S) break;
+    }
+
+    if (col_l < ncols) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int m = 4 * g + rr;
+        if (m < M) a.out[0][(int64_t)m * a.N + col0 + col_l] = acc[rr] * outf[rr];
+      }
+    }
   }
 }
 
@@ -1128,10 +1225,26 @@ hipError_t dispatch_lds_m(const GemvArgs& a, const LaunchShape& s, hipStream_t s
   return s.ncol == 1 ? launch_lds<kPlain, M, 1>(a, s, st, occ) : launch_lds<kPlain, M, 2>(a, s, st, occ);
 }
 
+template <int M>
+hipError_t dispatch_mfma(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised0{false};
+  const int gsu = a.U / a.G;
+  if (gsu == 1) return launch_or_query(gemv_mfma_kernel<M, 1>, raised1, a, s, st, occ);
+  if (gsu == 2) return launch_or_query(gemv_mfma_kernel<M, 2>, raised2, a, s, st, occ);
+  if (gsu % 4 == 0) return launch_or_query(gemv_mfma_kernel<M, 4>, raised4, a, s, st, occ);
+  return launch_or_query(gemv_mfma_kernel<M, 0>, raised0, a, s, st, occ);
+}
+
 hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
   if (s.variant == kVariantMfma) {
-    static std::atomic<bool> raised{false};
-    return launch_or_query(gemv_mfma_kernel, raised, a, s, st, occ);
+    switch (a.M) {
+      case 3: return dispatch_mfma<3>(a, s, st, occ);
+      case 4: return dispatch_mfma<4>(a, s, st, occ);
+      case 5: return dispatch_mfma<5>(a, s, st, occ);
+      case 6: return dispatch_mfma<6>(a, s, st, occ);
+      case 7: return dispatch_mfma<7>(a, s, st, occ);
+      default: return dispatch_mfma<8>(a, s, st, occ);
+    }
   }
   if (s.variant == kVariantReg) {
     switch (mode) {
