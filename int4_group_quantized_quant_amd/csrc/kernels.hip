@@ -998,8 +998,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
   // plane after it) holds the 8 fp16 values of row m for MFMA k-slots
   // 8g .. 8g+7 of unit u; slot 8g + 2v is input 32u + 8g + v and slot
   // 8g + 2v + 1 is input 32u + 8g + v + 4 (the order the nibble masks
-  // produce).  x * 2^e_m is split into hi = fp16(x * 2^e_m) and
-  // lo = fp16(x * 2^e_m - hi).
+  // produce).  y = x * 2^e_m is split into hi = fp16(y) and
+  // lo = fp16(y - hi), both rounded toward zero two at a time
+  // (v_cvt_pkrtz_f16_f32): y - hi is exact in fp32, so hi + lo carries y to
+  // 2^-20 relative, or 2^-24 absolute below the fp16 normal range.
   const int plane = Up * 4 * M;
   half8_t* hi_plane = reinterpret_cast<half8_t*>(lds4);
   half8_t* lo_plane = hi_plane + plane;
@@ -1012,16 +1014,17 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
         const float sc = pow2f(row_exponent(rowmax[m]));
         const float4 p = v0[e][m], q = v1[e][m];
         const float xv[8] = {p.x, q.x, p.y, q.y, p.z, q.z, p.w, q.w};
-        half8_t h, l;
+        u32x4 h, l;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float xs = xv[k] * sc;
-          const _Float16 hh = (_Float16)xs;
-          h[k] = hh;
-          l[k] = (_Float16)(xs - (float)hh);
+        for (int k = 0; k < 4; ++k) {
+          const float y0 = xv[2 * k] * sc, y1 = xv[2 * k + 1] * sc;
+          const auto hh = __builtin_amdgcn_cvt_pkrtz(y0, y1);
+          const auto ll = __builtin_amdgcn_cvt_pkrtz(y0 - (float)hh[0], y1 - (float)hh[1]);
+          h[k] = __builtin_bit_cast(uint32_t, hh);
+          l[k] = __builtin_bit_cast(uint32_t, ll);
         }
-        hi_plane[a_slot<M>(ug, m)] = h;
-        lo_plane[a_slot<M>(ug, m)] = l;
+        hi_plane[a_slot<M>(ug, m)] = __builtin_bit_cast(half8_t, h);
+        lo_plane[a_slot<M>(ug, m)] = __builtin_bit_cast(half8_t, l);
       }
     }
   }
