@@ -701,6 +701,88 @@ __device__ __forceinline__ float clamp_code(float v) {
 // One block handles `gpb` groups of gs consecutive floats; `tpg` threads share
 // a group, each thread owning whole 8-code words.  Min/max meet in LDS, one
 // thread per group derives scale and zero, then every thread packs its words.
+// Wave-level quantizer: a group of gs inputs (gs/8 words) lives on TPG
+// consecutive lanes of one wave (TPG the power of two >= gs/8, at most 64),
+// each lane holding WPT words (8 inputs each) in registers; min and max are
+// all-reduced across the group's lanes with xor shuffles, so the group is
+// read once and no LDS or barrier is involved.  The arithmetic is the same
+// binary32 sequence as quantize_pack_kernel (min/max are exact in any
+// order; a +0/-0 tie cannot change scale or zero).
+template <int WPT>
+__global__ __launch_bounds__(256) void quantize_pack_wave_kernel(const float* __restrict__ W,
+                                                                 int64_t total_groups, int gs, int tpg,
+                                                                 uint32_t* __restrict__ q,
+                                                                 float* __restrict__ scales,
+                                                                 float* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int gpw = 64 / tpg;  // groups per wave
+  const int64_t grp = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * gpw + lane / tpg;
+  const int part = lane & (tpg - 1);
+  const int wpg = gs >> 3;
+  const bool live = grp < total_groups;
+  const float* wg = W + (live ? grp : 0) * gs;
+
+  float v[WPT][8];
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int wi = part + j * tpg;
+    const bool has = live && wi < wpg;
+    const int wc = has ? wi : 0;
+    const float4 a0 = reinterpret_cast<const float4*>(wg)[2 * wc];
+    const float4 a1 = reinterpret_cast<const float4*>(wg)[2 * wc + 1];
+    v[j][0] = a0.x; v[j][1] = a0.y; v[j][2] = a0.z; v[j][3] = a0.w;
+    v[j][4] = a1.x; v[j][5] = a1.y; v[j][6] = a1.z; v[j][7] = a1.w;
+    if (has) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (v[j][e] < lo) lo = v[j][e];
+        if (v[j][e] > hi) hi = v[j][e];
+      }
+    }
+  }
+  for (int o = tpg >> 1; o >= 1; o >>= 1) {
+    const float lo2 = __shfl_xor(lo, o, 64);
+    const float hi2 = __shfl_xor(hi, o, 64);
+    if (lo2 < lo) lo = lo2;
+    if (hi2 > hi) hi = hi2;
+  }
+  if (!live) return;
+  float scale;
+  if (hi > lo) {
+    const float range = hi - lo;
+    scale = range / 15.0f;
+  } else {
+    scale = fabsf(hi) / 15.0f;
+  }
+  float zero = 0.0f;
+  if (scale == 0.0f) {
+    scale = 0.0f;
+  } else {
+    const float neg_lo = -lo;
+    zero = clamp_code(rintf(neg_lo / scale));
+  }
+  if (part == 0) {
+    scales[grp] = scale;
+    zeros[grp] = zero;
+  }
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int wi = part + j * tpg;
+    if (wi < wpg) {
+      uint32_t word = 0u;
+      if (scale != 0.0f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float code = clamp_code(rintf(v[j][e] / scale) + zero);
+          word |= (uint32_t)code << (4 * e);
+        }
+      }
+      q[grp * wpg + wi] = word;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restrict__ W,
                                                             int64_t total_groups, int gs, int tpg,
                                                             int gpb, uint32_t* __restrict__ q,
@@ -1297,6 +1379,24 @@ hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& s, hipSt
 hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,
                            float* scales, float* zeros, hipStream_t stream) {
   const int wpg = gs / 8;
+  if (wpg <= 512) {
+    // Wave kernel: tpg = next power of two >= words per group (<= 64 lanes),
+    // WPT words per lane.
+    int tpg = 1;
+    while (tpg < wpg && tpg < 64) tpg <<= 1;
+    const int wpt = (wpg + tpg - 1) / tpg;
+    const int64_t groups_per_block = 4 * (64 / tpg);
+    const int64_t grid = (total_groups + groups_per_block - 1) / groups_per_block;
+    if (wpt == 1)
+      hipLaunchKernelGGL(quantize_pack_wave_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+    else if (wpt == 2)
+      hipLaunchKernelGGL(quantize_pack_wave_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+    else if (wpt <= 4)
+      hipLaunchKernelGGL(quantize_pack_wave_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+    else
+      hipLaunchKernelGGL(quantize_pack_wave_kernel<8>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+    return hipGetLastError();
+  }
   const int tpg = wpg < 256 ? wpg : 256;
   const int gpb = 256 / tpg < 64 ? 256 / tpg : 64;
   const int64_t grid = (total_groups + gpb - 1) / gpb;

@@ -53,7 +53,7 @@ def test_worked_examples(q4):
         np.testing.assert_array_equal(got[0][i], words)
 
 
-@pytest.mark.parametrize("gs", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("gs", [32, 64, 96, 128, 256, 544])
 def test_adversarial_groups(q4, gs):
     rng = np.random.default_rng(100 + gs)
     G = adversarial_groups(rng, 400, gs)
@@ -62,7 +62,9 @@ def test_adversarial_groups(q4, gs):
 
 
 @pytest.mark.parametrize("N,K,gs", [(1, 32, 32), (7, 96, 32), (333, 1024, 128), (64, 5120, 64),
-                                    (17, 14336, 128), (5, 4096, 4096)])
+                                    (17, 14336, 128), (5, 4096, 4096),
+                                    (3, 8192, 8192),  # groups wider than the wave kernel takes
+                                    (9, 2880, 160)])  # 20 words per group: lanes padded to 32
 def test_random_shapes(q4, N, K, gs):
     W = synth.weights(0xA000 + N + K + gs, N, K)
     assert_bits_equal(W, gs, gpu_quantize(q4, W, gs), f"N={N} K={K} gs={gs}")
