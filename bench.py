@@ -100,6 +100,7 @@ def build_workload(q4, torch, dev):
 
     def quantize(W, gs):
         Wd = torch.from_numpy(W).to(dev)
+        q4.int4_quantize_pack(Wd[:1], gs)  # first launch of this kernel: code loading, not timed
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         out = q4.int4_quantize_pack(Wd, gs)
