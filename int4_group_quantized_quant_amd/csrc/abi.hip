@@ -171,13 +171,13 @@ int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bp
 // streams best), columns split evenly over the B*P rows, one LDS partial per
 // (column, stream, lane, chunk), the activations staged once per block.
 //
-// MFMA kernel (plain, M >= 3): one 512-thread block per CU, the M activation
-// rows staged in LDS as fp16 hi/lo planes (about M*K*4 bytes), tiles of 16
-// columns dealt to the waves.
+// Matrix-core kernel (plain, M >= 3): blocks of W <= 12 waves, each wave one
+// 16-unit slice of K per pass, 12 / W blocks per CU, the block's tiles of 16
+// columns in rounds that fit the partial table in LDS.
 //
-// LDS kernel (larger K for one or two lanes, or when the MFMA planes do not
-// fit): 256-thread blocks, the M activation rows staged in LDS (M*K*4 bytes),
-// columns split evenly over the waves.
+// LDS kernel (larger K for one or two lanes): 256-thread blocks, the M
+// activation rows staged in LDS (M*K*4 bytes), columns split evenly over the
+// waves.
 int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   DeviceInfo dev;
   RETURN_IF(device_info(&dev));
@@ -229,20 +229,36 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // Too little LDS for the partial table and the activations: the LDS
     // kernel needs only the activations.
   }
-  if (mode == kPlain && M >= 3 && mfma_lds_bytes(M, a.U) <= dev.lds_block &&
-      (int64_t)((a.U + 3) & ~3) * 4 * M <= 5120) {
-    // Matrix-core lanes: one 8-wave block per CU, tiles of 16 columns.
+  if (mode == kPlain && M >= 3) {
+    // Matrix-core lanes: W waves per block split K into slices of 16 units
+    // (P passes when there are more than 12 slices), about 12 waves per CU,
+    // one block's columns in rounds of RT tiles whose partials fit the LDS.
+    const int cls = slice_class(a.U / a.G);
+    const int nsl = (a.U + kSliceUnits - 1) / kSliceUnits;
+    const int P = (nsl + kSliceMaxWaves - 1) / kSliceMaxWaves;
+    const int W = (nsl + P - 1) / P;
+    int bpc = kSliceMaxWaves / W;
     const int64_t tiles = (N + 15) / 16;
-    s->variant = kVariantMfma;
-    s->ncol = 16;
-    s->depth = 1;
-    s->block_threads = 512;
-    s->lds_bytes = mfma_lds_bytes(M, a.U);
-    int64_t B = dev.cus;
+    int64_t B = (int64_t)dev.cus * bpc;
     if (B > tiles) B = tiles;
     if (B < 1) B = 1;
+    const int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
+    const size_t budget = dev.lds_cu / (size_t)bpc < dev.lds_block ? dev.lds_cu / (size_t)bpc : dev.lds_block;
+    const size_t fixed = slice_lds_bytes(cls, W, 0);
+    const size_t per_tile = slice_lds_bytes(cls, W, 1) - fixed;
+    if (fixed + per_tile > budget)
+      return fail(INT4_ERR_SHAPE, "matrix-core lanes need %zu bytes of LDS per block; %zu available",
+                  fixed + per_tile, budget);
+    int64_t rt = (int64_t)((budget - fixed) / per_tile);
+    if (rt > tiles_per_block) rt = tiles_per_block;
+    a.rt = (int32_t)rt;
+    s->variant = kVariantSlice;
+    s->ncol = 16;
+    s->depth = 1;
+    s->block_threads = 64 * W;
+    s->lds_bytes = slice_lds_bytes(cls, W, (int)rt);
     s->grid = (int)B;
-    a.total_waves = B * 8;
+    a.total_waves = B * W;
     return INT4_OK;
   }
   const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode == kNorm ? 64 : 0);

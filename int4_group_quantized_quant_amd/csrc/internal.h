@@ -40,6 +40,7 @@ struct GemvArgs {
   int32_t rows_per_block;  // P: rows of nch waves per block (register kernel)
   int32_t part_floats;  // floats of the per-block partial table (register kernel)
   int32_t M;            // lanes (kPlain)
+  int32_t rt;           // tiles of 16 columns per round (matrix-core kernel)
 };
 
 // Float offset of the staged activations in the register kernel's LDS: after
@@ -48,16 +49,44 @@ struct GemvArgs {
 __host__ __device__ inline int x_lds_offset(int part_floats) { return (part_floats + 16 + 3) & ~3; }
 
 enum Variant : int {
-  kVariantLds = 0,  // activations staged in LDS, one wave per column group
-  kVariantReg = 1,  // activations in registers, one wave per (row, K chunk)
-  kVariantMfma = 2, // three to eight lanes on the matrix cores, 16-column tiles
+  kVariantLds = 0,   // activations staged in LDS, one wave per column group
+  kVariantReg = 1,   // activations in registers, one wave per (row, K chunk)
+  kVariantSlice = 2, // three to eight lanes on the matrix cores, K sliced over the waves
 };
 
-// LDS bytes of the MFMA lane kernel: hi and lo fp16 planes of M rows over
-// the K/32 units padded to a multiple of 4.  The kernel stages at most 5120
-// (unit, lane group) row entries, (K/32 rounded up to 4) * 4 * M <= 5120,
-// which is exactly what 160 KiB of planes hold.
-inline size_t mfma_lds_bytes(int M, int U) { return (size_t)((U + 3) & ~3) * 128u * (size_t)M; }
+// Matrix-core lanes kernel.  A slice is 16 units (512 inputs) of K; each
+// wave holds one slice's activations and streams the block's tiles of 16
+// columns over it.  Its LDS holds, per wave, a stage of one tile (codes:
+// 16 columns of kSliceCodeStride dwords; scales and zero points: 16 columns
+// of slice_sz_stride dwords) and, per block, the partial sums of a round of
+// tiles: 8 rows x 16 columns per (tile, wave).
+constexpr int kSliceUnits = 16;
+constexpr int kSliceMaxWaves = 12;
+constexpr int kSliceCodeStride = 68;  // 64 dwords of codes + 4: conflict-free column reads
+
+// Group-size class of gsu = gs/32 units per group: 1, 2, 4 or 8 when gsu is
+// exactly that, 16 when gsu is a multiple of 16 (a slice lies in one group),
+// 0 for any other size.
+__host__ __device__ constexpr int slice_class(int gsu) {
+  return gsu == 1 || gsu == 2 || gsu == 4 || gsu == 8 ? gsu : (gsu % 16 == 0 ? 16 : 0);
+}
+// Scale (and zero-point) words each lane loads per tile: its quarter of the
+// slice's groups, which number at most 16 / gsu + 1.
+__host__ __device__ constexpr int slice_sz_words(int cls) {
+  return cls == 1 ? 4 : (cls == 2 || cls == 0 ? 2 : 1);
+}
+// Dwords per column of the scale/zero stage: 4 words per lane group for the
+// scales, the same for the zero points, padded so that the 16 columns fall
+// on distinct banks and vector writes stay aligned.
+__host__ __device__ constexpr int slice_sz_stride(int cls) {
+  return slice_sz_words(cls) == 4 ? 36 : (slice_sz_words(cls) == 2 ? 18 : 9);
+}
+__host__ __device__ constexpr int slice_stage_words(int cls) {
+  return 16 * kSliceCodeStride + 16 * slice_sz_stride(cls);
+}
+inline size_t slice_lds_bytes(int cls, int waves, int rt) {
+  return ((size_t)waves * slice_stage_words(cls) + (size_t)rt * waves * 128) * sizeof(float);
+}
 
 struct LaunchShape {
   int variant;        // Variant

@@ -862,100 +862,45 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restr
 
 // ------------------------------------------------------------ dispatch
 
-// ------------------------------------------------------------ MFMA lane kernel
+// ------------------------------------------------------------ matrix-core lanes kernel
 
-// Three to eight decode lanes on the matrix cores: v_mfma_f32_16x16x32_f16
-// with D[m][col] = sum_k A[m][k] * B[k][col] over one 32-input unit, where
-//  * B[k][col] = (code - zero) * 2^-24, the nibble masked into an fp16
-//    subnormal and the zero point subtracted with v_pk_add_f16, both exact
-//    (the matrix cores keep fp16 subnormal inputs);
-//  * A[m][k] = x[m][k] * 2^e_m split into two fp16 parts hi + lo (hi the
-//    rounded value, lo the rounded remainder), e_m a power of two that puts
-//    the row's largest |x| just below 2^14; the two MFMAs accumulate the
-//    exact products hi*B and lo*B in fp32.
-// Lane l of a wave holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16]
-// and D[4*(l/16) .. +3][l%16].  A 16-column tile is streamed with one 16-byte
-// unit per lane: lane (col, g) loads unit 4s+g of column col, and a 4x4
-// transpose across the lane groups (two permlane32 and two permlane16
-// swaps) leaves word g of unit 4s+t in register t, so step t's MFMA covers
-// exactly unit 4s+t, which lies in one group.  Each unit's D is scaled by
-// its group's scale into the lane's four accumulators; at the end of a tile
-// the rows m < M are multiplied by 2^(24 - e_m) and stored.  Rows of A are
-// independent, so a lane's outputs never depend on the other lanes.
+// Three to eight decode lanes on the matrix cores, v_mfma_f32_16x16x32_f16:
+// D[i][col] = sum_k A[i][k] * B[k][col] over the 32 inputs of one unit.
+//  * B[k][col] = (code - zero) * 2^-24: the nibble masked into an fp16
+//    subnormal minus the zero point, exact (the matrix cores keep fp16
+//    subnormal inputs).
+//  * A row i < 8 holds hi and row 8 + i holds lo for activation row m = i,
+//    where x[m][k] * 2^e = hi + lo, hi = fp16(y) and lo = fp16(y - hi), both
+//    rounded toward zero; e is a power of two per (row, slice) that puts the
+//    slice's largest |x| just below 2^14.  One MFMA yields the hi and the lo
+//    products of every row; they are added once per tile.
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// D[4*(l/16) .. +3][l%16].  Slot 8g + 2v of a unit is input 8g + v and slot
+// 8g + 2v + 1 is input 8g + v + 4, the order the nibble masks produce.
+//
+// Work split.  Block b owns columns [b*N/B, (b+1)*N/B) in tiles of 16
+// columns.  Its W waves split K into slices of 16 units: wave w takes slices
+// w, w + W, ..., keeps the A operand of its slice in 64 registers and streams
+// every tile of the block over that slice.  Per tile, one load instruction
+// covers 4 columns x 16 units (lanes 16c .. 16c+15 read 256 contiguous bytes
+// of one column), and each lane loads 1, 2 or 4 scale and zero-point words of
+// its column.  The tile passes through the wave's LDS stage to reach the
+// matrix layout (lane (g, col) reads word g of every unit of column col).
+// Each unit's D is scaled by its group's scale into four accumulators; at the
+// end of the tile the lo rows are added to the hi rows, multiplied by
+// 2^(24 - e) and written to the block's partial table.  After a round of
+// tiles, the block adds the waves' partials in wave order and stores Y.
+// Every row's arithmetic reads only that row's activations, so a lane's
+// outputs never depend on the other lanes.
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kMfmaDepth = 5;  // quads of loads in flight ahead of the compute
-
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pick4(u32x4 v, int j) {
-  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
-}
-
-// Groups a quad of units can touch: 4 when a group is one unit (or of a
-// size that is not 2 or a multiple of 4), 2 for two-unit groups, 1 when the
-// group size is a multiple of 4 units.  Loading exactly these keeps every
-// loaded register live, so the register allocator never reuses one that a
-// load in flight will still write (which would force a full wait).
-template <int GSU>
-struct QuadGroups {
-  static constexpr int n = GSU == 2 ? 2 : (GSU == 4 ? 1 : 4);
-};
-
-template <int NG>
-struct GroupVals;
-template <>
-struct GroupVals<4> {
-  u32x4 v;
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-  }
-  __device__ __forceinline__ uint32_t get(int j) const { return pick4(v, j); }
-};
-template <>
-struct GroupVals<2> {
-  u32x2 v;
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-  }
-  __device__ __forceinline__ uint32_t get(int j) const { return j == 0 ? v.x : v.y; }
-};
-template <>
-struct GroupVals<1> {
-  uint32_t v;
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    v = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-  }
-  __device__ __forceinline__ uint32_t get(int) const { return v; }
-};
-
-template <int GSU>
-struct Quad {
-  u32x4 q;                                   // one 16-byte unit of the lane's column
-  GroupVals<QuadGroups<GSU>::n> s;           // scales from the quad's first group on
-  GroupVals<QuadGroups<GSU>::n> z;           // zero points of the same groups
-};
-
-// Rows of 16 lanes x 4 registers, transposed: register t of lane group g
-// ends up holding what register g of lane group t held.
-__device__ __forceinline__ void transpose4x4(u32x4& w) {
-  auto a = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
-  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  w.x = c[0];
-  w.y = c[1];
-  w.z = d[0];
-  w.w = d[1];
-}
-
 
 // 2^e as a float, e in [-126, 127].
 __device__ __forceinline__ float pow2f(int e) { return bitsf((uint32_t)(e + 127) << 23); }
 
-// e_m for a row whose largest magnitude is amax: amax * 2^e < 2^14.
+// e for a row slice whose largest magnitude is amax: amax * 2^e < 2^14.
 __device__ __forceinline__ int row_exponent(float amax) {
   if (!(amax > 0.0f)) return 0;
   const int biased = (int)((fbits(amax) >> 23) & 0xFFu);
@@ -964,287 +909,309 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return e < -100 ? -100 : (e > 100 ? 100 : e);
 }
 
-// Largest value over the wave (butterfly with the same swaps and DPP row
-// rotations as the sums).
-__device__ __forceinline__ float wave_max(float v) {
-  auto r32 = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
-  v = fmaxf(bitsf(r32[0]), bitsf(r32[1]));
-  auto r16 = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
-  v = fmaxf(bitsf(r16[0]), bitsf(r16[1]));
-  v = fmaxf(v, dpp_move<0x128>(v));
-  v = fmaxf(v, dpp_move<0x124>(v));
-  v = fmaxf(v, dpp_move<0x122>(v));
-  v = fmaxf(v, dpp_move<0x121>(v));
-  return bitsf(__builtin_amdgcn_readfirstlane(fbits(v)));
+template <int SZW>
+struct SzWords {
+  uint32_t w[SZW];
+};
+
+template <int SZW>
+__device__ __forceinline__ SzWords<SZW> load_sz(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  SzWords<SZW> o;
+  if constexpr (SZW == 4) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadNonTemporal));
+    o.w[0] = v.x;
+    o.w[1] = v.y;
+    o.w[2] = v.z;
+    o.w[3] = v.w;
+  } else if constexpr (SZW == 2) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kLoadNonTemporal));
+    o.w[0] = v.x;
+    o.w[1] = v.y;
+  } else {
+    o.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kLoadNonTemporal);
+  }
+  return o;
 }
 
-// Group offset of unit t of a quad (t = 0..3) from the quad's first group.
-// GSU is the group size in units when it is 1 or 2, 4 when it is a multiple
-// of 4 (a quad then lies in one group), and 0 for any other size (the offset
-// is computed from the unit-in-group counter uig, uniform over the wave).
-template <int GSU>
-__device__ __forceinline__ int quad_group_offset(int t, int uig, int gsu) {
-  if constexpr (GSU == 1) return t;
-  if constexpr (GSU == 2) return t >> 1;
-  if constexpr (GSU == 4) return 0;
-  int j = 0;
-  j += (uig + t >= gsu) ? 1 : 0;
-  j += (uig + t >= 2 * gsu) ? 1 : 0;
-  j += (uig + t >= 3 * gsu) ? 1 : 0;
-  return j;
+template <int SZW>
+__device__ __forceinline__ void store_sz(uint32_t* p, const uint32_t (&v)[SZW]) {
+  if constexpr (SZW == 4) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{v[0], v[1], v[2], v[3]};
+  } else if constexpr (SZW == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{v[0], v[1]};
+  } else {
+    p[0] = v[0];
+  }
 }
 
-// Slot of row m of entry ug in an A plane (16-byte slots, M per entry).
-// For M = 4 and 8 the row is XOR-swizzled with bits of ug so that 16
-// consecutive entries written for one row, and the M rows of one entry read
-// by the MFMA lanes, both fall on distinct LDS banks; odd M needs no swizzle
-// (its stride is already odd), M = 6 keeps a two-way conflict.
-template <int M>
-__device__ __forceinline__ int a_slot(int ug, int m) {
-  if constexpr (M == 8) return ug * 8 + (m ^ ((ug >> 1) & 7));
-  if constexpr (M == 4) return ug * 4 + (m ^ ((ug >> 2) & 3));
-  return ug * M + m;
-}
+// One tile of one slice in flight: 4 x 16 bytes of codes, the lane's scale
+// and zero-point words.
+template <int SZW>
+struct SliceTile {
+  u32x4 c[4];
+  SzWords<SZW> s, z;
+};
 
-template <int MR, int GSU>
-__global__ __launch_bounds__(512) void gemv_mfma_kernel(GemvArgs a) {
-  extern __shared__ float4 lds4[];
-  constexpr int M = MR;
-  // Staging entries per thread: the LDS holds at most 160 KiB of planes,
-  // i.e. at most 5120 / M entries of (unit, lane group) for M rows.
-  constexpr int kEntries = (5120 / M + 511) / 512;
-  const int K = a.K;
-  const int U = a.U;
-  const int G = a.G;
-  const int gsu = U / G;        // units per group
-  const int Up = (U + 3) & ~3;  // units padded to whole quads
-  const int S = Up >> 2;        // quads per column
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform_int(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-
-  // 1. One pass over the activations: each thread loads the M rows of its
-  // (unit, lane group) entries (8 inputs each) together, keeps them in
-  // registers, and the block reduces every row's largest magnitude.
-  // Entry ug = u*4 + g covers inputs 32u + 8g .. +7; units past K are zero.
-  const int nug = Up * 4;
-  float4 v0[kEntries][M], v1[kEntries][M];
+// The A operand of slice `sl` (16 units from unit 16*sl) for lane (g, i):
+// A[t] holds, for unit t, row i of the k-slots 8g .. 8g+7.  Lanes i < 8 take
+// the hi parts of row i, lanes i >= 8 the lo parts of row i - 8.  Each lane
+// loads 8 units of its row (lanes i < 8 units 0..7, lanes i >= 8 units
+// 8..15), the slice's row maximum is reduced over the 8 lanes of the row,
+// and the partner lane (i ^ 8) sends the parts this lane needs for the
+// other 8 units.  f[r] receives 2^(24 - e) of output row 4*(g & 1) + r.
+__device__ __forceinline__ void slice_operand(const GemvArgs& a, int sl, int lane, u32x4 (&A)[16],
+                                              float (&f)[4]) {
+  const int K = a.K, U = a.U, M = a.M;
+  const int g = lane >> 4;
+  const int i = lane & 15;
+  const int m = i & 7;
+  const int half = i >> 3;
+  const bool row_live = m < M;
+  const int mc = row_live ? m : 0;
+  float4 p[8], q[8];
 #pragma unroll
-  for (int e = 0; e < kEntries; ++e) {
-    const int ug = threadIdx.x + e * blockDim.x;
-    const int u = ug >> 2, g = ug & 3;
-    const bool live = ug < nug && u < U;
-    const int uc = live ? u : 0;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * K + 32 * uc + 8 * g);
-      v0[e][m] = src[0];
-      v1[e][m] = src[1];
-      if (!live) {
-        v0[e][m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        v1[e][m] = v0[e][m];
-      }
+  for (int tt = 0; tt < 8; ++tt) {
+    const int u = 16 * sl + 8 * half + tt;
+    const bool live = row_live && u < U;
+    const int uc = u < U ? u : U - 1;
+    const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)mc * K + 32 * uc + 8 * g);
+    p[tt] = src[0];
+    q[tt] = src[1];
+    if (!live) {
+      p[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+      q[tt] = p[tt];
     }
   }
-  float* red = reinterpret_cast<float*>(lds4);
+  float mx = 0.0f;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float mx = 0.0f;
+  for (int tt = 0; tt < 8; ++tt) {
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(p[tt].x), fabsf(p[tt].y)), fmaxf(fabsf(p[tt].z), fabsf(p[tt].w))));
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q[tt].x), fabsf(q[tt].y)), fmaxf(fabsf(q[tt].z), fabsf(q[tt].w))));
+  }
+  {
+    auto r32 = __builtin_amdgcn_permlane32_swap(fbits(mx), fbits(mx), false, false);
+    mx = fmaxf(bitsf(r32[0]), bitsf(r32[1]));
+    auto r16 = __builtin_amdgcn_permlane16_swap(fbits(mx), fbits(mx), false, false);
+    mx = fmaxf(bitsf(r16[0]), bitsf(r16[1]));
+    mx = fmaxf(mx, dpp_move<0x128>(mx));
+  }
+  const int e = row_exponent(mx);
+  const float sc = pow2f(e);
 #pragma unroll
-    for (int e = 0; e < kEntries; ++e) {
-      const float4 p = v0[e][m], q = v1[e][m];
-      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(p.x), fabsf(p.y)), fmaxf(fabsf(p.z), fabsf(p.w))));
-      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
+  for (int tt = 0; tt < 8; ++tt) {
+    const float xv[8] = {p[tt].x, q[tt].x, p[tt].y, q[tt].y, p[tt].z, q[tt].z, p[tt].w, q[tt].w};
+    u32x4 h, l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float y0 = xv[2 * k] * sc, y1 = xv[2 * k + 1] * sc;
+      const auto hh = __builtin_amdgcn_cvt_pkrtz(y0, y1);
+      const auto ll = __builtin_amdgcn_cvt_pkrtz(y0 - (float)hh[0], y1 - (float)hh[1]);
+      h[k] = __builtin_bit_cast(uint32_t, hh);
+      l[k] = __builtin_bit_cast(uint32_t, ll);
     }
-    const float w = wave_max(mx);
-    if (lane == 0) red[m * nwaves + wave] = w;
-  }
-  __syncthreads();
-  float rowmax[M];
+    // Lanes i < 8 keep hi and send lo; lanes i >= 8 keep lo and send hi.
+    u32x4 keep = half ? l : h;
+    u32x4 send = half ? h : l;
+    u32x4 recv;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    rowmax[m] = red[m * nwaves];
-    for (int w = 1; w < nwaves; ++w) rowmax[m] = fmaxf(rowmax[m], red[m * nwaves + w]);
+    for (int k = 0; k < 4; ++k) recv[k] = fbits(dpp_move<0x128>(bitsf(send[k])));
+    A[tt] = half ? recv : keep;
+    A[8 + tt] = half ? keep : recv;
   }
-  float outf[4];  // 2^(24 - e_m) for this lane's output rows m = 4*(lane/16) + r
+  const int r0 = 4 * (g & 1);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    outf[r] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (4 * (lane >> 4) + r == m) outf[r] = pow2f(24 - row_exponent(rowmax[m]));
+    const int e_lo = __builtin_amdgcn_readlane(e, r);
+    const int e_hi = __builtin_amdgcn_readlane(e, 4 + r);
+    f[r] = pow2f(24 - (r0 ? e_hi : e_lo));
   }
-  __syncthreads();
+}
 
-  // 2. Stage A from the registers: entry (u*4 + g)*M + m of the hi plane (lo
-  // plane after it) holds the 8 fp16 values of row m for MFMA k-slots
-  // 8g .. 8g+7 of unit u; slot 8g + 2v is input 32u + 8g + v and slot
-  // 8g + 2v + 1 is input 32u + 8g + v + 4 (the order the nibble masks
-  // produce).  y = x * 2^e_m is split into hi = fp16(y) and
-  // lo = fp16(y - hi), both rounded toward zero two at a time
-  // (v_cvt_pkrtz_f16_f32): y - hi is exact in fp32, so hi + lo carries y to
-  // 2^-20 relative, or 2^-24 absolute below the fp16 normal range.
-  const int plane = Up * 4 * M;
-  half8_t* hi_plane = reinterpret_cast<half8_t*>(lds4);
-  half8_t* lo_plane = hi_plane + plane;
+template <int GS>
+__global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
+  extern __shared__ float4 lds4[];
+  constexpr int SZW = slice_sz_words(GS);
+  constexpr int SS = slice_sz_stride(GS);
+  constexpr int kStage = slice_stage_words(GS);
+  const int M = a.M;
+  const int U = a.U;
+  const int G = a.G;
+  const int gsu = U / G;
+  const int64_t N = a.N;
+  const int lane = threadIdx.x & 63;
+  const int hi4 = lane >> 4;   // load: column quarter; matrix: k group / D row group
+  const int lo16 = lane & 15;  // load: unit; matrix: column
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int nsl = (U + kSliceUnits - 1) / kSliceUnits;
+  const int64_t cb = uniform_i64((int64_t)blockIdx.x * N / gridDim.x);
+  const int64_t ce = uniform_i64(((int64_t)blockIdx.x + 1) * N / gridDim.x);
+  const int ntile = (int)((ce - cb + 15) >> 4);
+  const int RT = a.rt;
+
+  uint32_t* lds = reinterpret_cast<uint32_t*>(lds4);
+  uint32_t* stage = lds + wave * kStage;
+  float* part = reinterpret_cast<float*>(lds + W * kStage);
+  const char* qbase = reinterpret_cast<const char*>(a.q[0]);
+  const char* sbase = reinterpret_cast<const char*>(a.s[0]);
+  const char* zbase = reinterpret_cast<const char*>(a.z[0]);
+
+  for (int r0 = 0; r0 < ntile; r0 += RT) {
+    const int rn = ntile - r0 < RT ? ntile - r0 : RT;
+    bool first_pass = true;
+    for (int sl = wave; sl < nsl; sl += W) {
+      const int u0 = kSliceUnits * sl;
+      const int h0 = u0 / gsu;
+
+      // Tile ti of the block in flight; tiles past the round read nothing
+      // (an empty buffer range), so every load is unconditional.
+      auto load = [&](int ti, SliceTile<SZW>& r) {
+        const bool live = ti < r0 + rn;
+        const int64_t col0 = cb + 16 * (int64_t)(live ? ti : r0);
+        const int ncols = live ? (ce - col0 < 16 ? (int)(ce - col0) : 16) : 0;
+        const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + col0 * (int64_t)U * 16), (short)0,
+                                                          ncols * U * 16, kBufferWord3);
+        const uint32_t vq = ((uint32_t)hi4 * (uint32_t)U + (uint32_t)(u0 + lo16)) * 16u;
 #pragma unroll
-  for (int e = 0; e < kEntries; ++e) {
-    const int ug = threadIdx.x + e * blockDim.x;
-    if (ug < nug) {
+        for (int j = 0; j < 4; ++j)
+          r.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rq, vq, (uint32_t)j * 64u * (uint32_t)U, kLoadNonTemporal));
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(sbase + col0 * (int64_t)G * 4), (short)0,
+                                                          ncols * G * 4, kBufferWord3);
+        const auto rz = __builtin_amdgcn_make_buffer_rsrc((void*)(zbase + col0 * (int64_t)G * 4), (short)0,
+                                                          ncols * G * 4, kBufferWord3);
+        const int colc = lo16 < ncols ? lo16 : (ncols > 0 ? ncols - 1 : 0);
+        const uint32_t vs = ((uint32_t)colc * (uint32_t)G + (uint32_t)(h0 + hi4 * SZW)) * 4u;
+        r.s = load_sz<SZW>(rs, vs);
+        r.z = load_sz<SZW>(rz, vs);
+      };
+
+      // Codes to [col][unit][word] (column stride kSliceCodeStride dwords);
+      // scales and zero points (as fp16 subnormal pairs) to [col][group],
+      // groups past the column's last set to zero: they hold only units
+      // past K, whose activations are zero.
+      auto write_stage = [&](const SliceTile<SZW>& r) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float sc = pow2f(row_exponent(rowmax[m]));
-        const float4 p = v0[e][m], q = v1[e][m];
-        const float xv[8] = {p.x, q.x, p.y, q.y, p.z, q.z, p.w, q.w};
-        u32x4 h, l;
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x4*>(stage + (4 * j + hi4) * kSliceCodeStride + 4 * lo16) = r.c[j];
+        uint32_t sv[SZW], zv[SZW];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float y0 = xv[2 * k] * sc, y1 = xv[2 * k + 1] * sc;
-          const auto hh = __builtin_amdgcn_cvt_pkrtz(y0, y1);
-          const auto ll = __builtin_amdgcn_cvt_pkrtz(y0 - (float)hh[0], y1 - (float)hh[1]);
-          h[k] = __builtin_bit_cast(uint32_t, hh);
-          l[k] = __builtin_bit_cast(uint32_t, ll);
+        for (int c = 0; c < SZW; ++c) {
+          const bool ok = h0 + hi4 * SZW + c < G;
+          const uint32_t zi = (uint32_t)bitsf(r.z.w[c]);
+          sv[c] = ok ? r.s.w[c] : 0u;
+          zv[c] = ok ? (zi | (zi << 16)) : 0u;
         }
-        hi_plane[a_slot<M>(ug, m)] = __builtin_bit_cast(half8_t, h);
-        lo_plane[a_slot<M>(ug, m)] = __builtin_bit_cast(half8_t, l);
-      }
-    }
-  }
-  __syncthreads();
+        uint32_t* zs = stage + 16 * kSliceCodeStride + lo16 * SS + hi4 * SZW;
+        store_sz<SZW>(zs, sv);
+        store_sz<SZW>(zs + 4 * SZW, zv);
+      };
 
-  // 3. Tiles of 16 columns: block b owns tiles [tb, te), wave w takes tiles
-  // tb + w, tb + w + nwaves, ...
-  const int64_t T = (a.N + 15) >> 4;
-  const int64_t tb = uniform_i64((int64_t)blockIdx.x * T / gridDim.x);
-  const int64_t te = uniform_i64(((int64_t)blockIdx.x + 1) * T / gridDim.x);
-  const int64_t ntiles = te - tb > wave ? (te - tb - wave + nwaves - 1) / nwaves : 0;
+      SliceTile<SZW> ra, rb;
+      load(r0, ra);
+      load(r0 + 1, rb);
+      __builtin_amdgcn_sched_barrier(0);
 
-  const int col_l = lane & 15;
-  const int g = lane >> 4;
-  const int m_a = col_l;  // A row of this lane
-  const uint32_t a_mask = m_a < M ? 0xFFFFFFFFu : 0u;
-  const int m_c = m_a < M ? m_a : M - 1;
-  const char* hi_bytes = reinterpret_cast<const char*>(hi_plane);
-  const char* lo_bytes = reinterpret_cast<const char*>(lo_plane);
-  const uint32_t qcol = (uint32_t)U * 16u;
-  const uint32_t gcol = (uint32_t)G * 4u;
+      u32x4 A[16];
+      float f[4];
+      slice_operand(a, sl, lane, A, f);
 
-  for (int64_t i = 0; i < ntiles; ++i) {
-    const int64_t col0 = (tb + wave + i * nwaves) * 16;
-    const int ncols = a.N - col0 < 16 ? (int)(a.N - col0) : 16;
-    const uint32_t cl = (uint32_t)(col_l < ncols ? col_l : ncols - 1);
-    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const char*>(a.q[0]) + col0 * qcol), (short)0, (int)(ncols * qcol), kBufferWord3);
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const char*>(a.s[0]) + col0 * gcol), (short)0, (int)(ncols * gcol), kBufferWord3);
-    const auto rz = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const char*>(a.z[0]) + col0 * gcol), (short)0, (int)(ncols * gcol), kBufferWord3);
-    const uint32_t vq = (cl * (uint32_t)U + (uint32_t)g) * 16u;
-    const uint32_t vs = cl * (uint32_t)G * 4u;
-
-    // Load cursor: quad ls and its first group lg (uniform).  Loads past the
-    // column's last quad re-read it.
-    int ls = 0, lg = 0, luig = 0;
-    auto load = [&](Quad<GSU>& r) {
-      r.q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq, 64u * (uint32_t)ls,
-                                                                            kLoadNonTemporal));
-      r.s.load(rs, vs, 4u * (uint32_t)lg);
-      r.z.load(rz, vs, 4u * (uint32_t)lg);
-      // Advance one quad (none past the last), branch-free.
-      const int adv = ls + 1 < S ? 1 : 0;
-      const int t4 = luig + 4 * adv;
-      const int inc = (t4 >= gsu ? 1 : 0) + (t4 >= 2 * gsu ? 1 : 0) + (t4 >= 3 * gsu ? 1 : 0) +
-                      (t4 >= 4 * gsu ? 1 : 0);
-      ls += adv;
-      lg += inc;
-      luig = t4 - inc * gsu;
-    };
-    // Compute cursor: quad cs, first group's unit-in-group counter cuig.
-    int cs = 0, cuig = 0;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](Quad<GSU> r) {
-      // The quad's A operands first: eight LDS reads in flight together.
-      u32x4 ah[4], al[4];
+      // Group structure of the slice (wave-uniform): unit t lies in group
+      // h0 + h(t); first(t) / last(t) mark the slice's part of a group.
+      uint64_t hpack = 0;
+      uint32_t fmask = 0, lmask = 0;
+      if constexpr (GS == 0) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t off = (uint32_t)a_slot<M>(4 * (4 * cs + t) + g, m_c) * 16u;
-        ah[t] = *reinterpret_cast<const u32x4*>(hi_bytes + off) & a_mask;
-        al[t] = *reinterpret_cast<const u32x4*>(lo_bytes + off) & a_mask;
-      }
-      transpose4x4(r.q);
-      const uint32_t words[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-      const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-      f32x4_t d4 = z4;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = quad_group_offset<GSU>(t, cuig, gsu);
-        const uint32_t zi = (uint32_t)bitsf(r.z.get(j));
-        const half2_t zh = as_half2(zi | (zi << 16));
-        u32x4 bw;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          bw[v] = __builtin_bit_cast(uint32_t, as_half2((words[t] >> (4 * v)) & 0x000F000Fu) - zh);
-        const half8_t b = __builtin_bit_cast(half8_t, bw);
-        // Units of one group accumulate in the matrix core; the group's
-        // scale is applied once its last unit of the quad is in.
-        const bool first = GSU == 0 || GSU == 1 || (GSU == 2 && (t & 1) == 0) || (GSU == 4 && t == 0);
-        const bool last = GSU == 0 || GSU == 1 || (GSU == 2 && (t & 1) == 1) || (GSU == 4 && t == 3);
-        d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[t]), b, first ? z4 : d4, 0, 0, 0);
-        d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[t]), b, d4, 0, 0, 0);
-        if (last) {
-          const float sv = bitsf(r.s.get(j));
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d4[rr], acc[rr]);
+        for (int t = 0; t < kSliceUnits; ++t) {
+          const int u = u0 + t;
+          const int gq = u / gsu;
+          const int rem = u - gq * gsu;
+          hpack |= (uint64_t)(gq - h0) << (4 * t);
+          if (rem == 0 || t == 0) fmask |= 1u << t;
+          if (rem == gsu - 1 || t == kSliceUnits - 1) lmask |= 1u << t;
         }
       }
-      ++cs;
-      const int t4 = cuig + 4;
-      cuig = t4 - gsu * ((t4 >= gsu ? 1 : 0) + (t4 >= 2 * gsu ? 1 : 0) + (t4 >= 3 * gsu ? 1 : 0) +
-                         (t4 >= 4 * gsu ? 1 : 0));
-    };
 
-    // Ring of kMfmaDepth + 1 quads; every load is unconditional.
-    static_assert(kMfmaDepth == 5, "the ring below holds six quads");
-    Quad<GSU> r0, r1, r2, r3, r4, r5;
-    load(r0);
-    load(r1);
-    load(r2);
-    load(r3);
-    load(r4);
-    while (true) {
-      load(r5);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(r0);
-      if (cs >= S) break;
-      load(r0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(r1);
-      if (cs >= S) break;
-      load(r1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(r2);
-      if (cs >= S) break;
-      load(r2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(r3);
-      if (cs >= S) break;
-      load(r3);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(r4);
-      if (cs >= S) break;
-      load(r4);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(r5);
-      if (cs >= S) break;
-    }
-
-    if (col_l < ncols) {
+      auto compute = [&](int i) {
+        const uint32_t* cs = stage + lo16 * kSliceCodeStride + hi4;
+        const uint32_t* zs = stage + 16 * kSliceCodeStride + lo16 * SS;
+        uint32_t wd[kSliceUnits];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = 4 * g + rr;
-        if (m < M) a.out[0][(int64_t)m * a.N + col0 + col_l] = acc[rr] * outf[rr];
+        for (int t = 0; t < kSliceUnits; ++t) wd[t] = cs[4 * t];
+        const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc = z4, d = z4;
+#pragma unroll
+        for (int t = 0; t < kSliceUnits; ++t) {
+          int h;
+          bool first, last;
+          if constexpr (GS == 0) {
+            h = (int)((hpack >> (4 * t)) & 15u);
+            first = (fmask >> t) & 1u;
+            last = (lmask >> t) & 1u;
+          } else if constexpr (GS == 16) {
+            h = 0;
+            first = t == 0;
+            last = t == kSliceUnits - 1;
+          } else {
+            h = t / GS;
+            first = t % GS == 0;
+            last = t % GS == GS - 1;
+          }
+          const half2_t zh = as_half2(zs[4 * SZW + h]);
+          u32x4 bw;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            bw[v] = __builtin_bit_cast(uint32_t, as_half2((wd[t] >> (4 * v)) & 0x000F000Fu) - zh);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]),
+                                                     __builtin_bit_cast(half8_t, bw), first ? z4 : d, 0, 0, 0);
+          if (last) {
+            const float sv = bitsf(zs[h]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d[rr], acc[rr]);
+          }
+        }
+        // Lanes 0..31 hold the hi rows, lanes 32..63 the lo rows.
+        float v[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v[rr] = add_swap32(acc[rr], acc[rr]) * f[rr];
+        if (hi4 < 2) {
+          float* pp = part + ((size_t)(i * W + wave) * 8 + 4 * hi4) * 16 + lo16;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) pp[16 * rr] = first_pass ? v[rr] : pp[16 * rr] + v[rr];
+        }
+      };
+
+      for (int i = 0;; i += 2) {
+        write_stage(ra);
+        load(r0 + i + 2, ra);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i);
+        if (i + 1 >= rn) break;
+        write_stage(rb);
+        load(r0 + i + 3, rb);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 1);
+        if (i + 2 >= rn) break;
+      }
+      first_pass = false;
+    }
+    __syncthreads();
+    // Y for the round's tiles: the waves' partials added in wave order.
+    const int nout = rn * M * 16;
+    for (int o = threadIdx.x; o < nout; o += blockDim.x) {
+      const int c = o & 15;
+      const int tm = o >> 4;
+      const int i = tm / M;
+      const int m = tm - i * M;
+      const int64_t col = cb + 16 * (int64_t)(r0 + i) + c;
+      if (col < ce) {
+        const float* pp = part + ((size_t)(i * W) * 8 + m) * 16 + c;
+        float y = pp[0];
+        for (int w = 1; w < W; ++w) y += pp[(size_t)w * 128];
+        a.out[0][(int64_t)m * N + col] = y;
       }
     }
+    __syncthreads();
   }
 }
 
@@ -1310,27 +1277,21 @@ hipError_t dispatch_lds_m(const GemvArgs& a, const LaunchShape& s, hipStream_t s
   return s.ncol == 1 ? launch_lds<kPlain, M, 1>(a, s, st, occ) : launch_lds<kPlain, M, 2>(a, s, st, occ);
 }
 
-template <int M>
-hipError_t dispatch_mfma(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
-  static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised0{false};
-  const int gsu = a.U / a.G;
-  if (gsu == 1) return launch_or_query(gemv_mfma_kernel<M, 1>, raised1, a, s, st, occ);
-  if (gsu == 2) return launch_or_query(gemv_mfma_kernel<M, 2>, raised2, a, s, st, occ);
-  if (gsu % 4 == 0) return launch_or_query(gemv_mfma_kernel<M, 4>, raised4, a, s, st, occ);
-  return launch_or_query(gemv_mfma_kernel<M, 0>, raised0, a, s, st, occ);
+hipError_t dispatch_slice(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised8{false}, raised16{false},
+      raised0{false};
+  switch (slice_class(a.U / a.G)) {
+    case 1: return launch_or_query(gemv_slice_kernel<1>, raised1, a, s, st, occ);
+    case 2: return launch_or_query(gemv_slice_kernel<2>, raised2, a, s, st, occ);
+    case 4: return launch_or_query(gemv_slice_kernel<4>, raised4, a, s, st, occ);
+    case 8: return launch_or_query(gemv_slice_kernel<8>, raised8, a, s, st, occ);
+    case 16: return launch_or_query(gemv_slice_kernel<16>, raised16, a, s, st, occ);
+    default: return launch_or_query(gemv_slice_kernel<0>, raised0, a, s, st, occ);
+  }
 }
 
 hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
-  if (s.variant == kVariantMfma) {
-    switch (a.M) {
-      case 3: return dispatch_mfma<3>(a, s, st, occ);
-      case 4: return dispatch_mfma<4>(a, s, st, occ);
-      case 5: return dispatch_mfma<5>(a, s, st, occ);
-      case 6: return dispatch_mfma<6>(a, s, st, occ);
-      case 7: return dispatch_mfma<7>(a, s, st, occ);
-      default: return dispatch_mfma<8>(a, s, st, occ);
-    }
-  }
+  if (s.variant == kVariantSlice) return dispatch_slice(a, s, st, occ);
   if (s.variant == kVariantReg) {
     switch (mode) {
       case kSplit4: return dispatch_reg<kSplit4>(a, s, st, occ);

@@ -88,6 +88,46 @@ def test_lanes(q4, M, N, K, gs):
             np.testing.assert_array_equal(Y2[keep].view(np.uint32), Y[keep].view(np.uint32))
 
 
+def check_lanes(q4, X, q, s, z, K, gs, seed):
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    Y = run_matvec(q4, X, q, s, z)
+    assert_dot_close(Y, Y_ref, B, f"lanes M={X.shape[0]} K={K} gs={gs}")
+    M = X.shape[0]
+    for keep in (0, M - 1):
+        X2 = synth.lanes(seed + keep, M, K)
+        X2[keep] = X[keep]
+        Y2 = run_matvec(q4, X2, q, s, z)
+        np.testing.assert_array_equal(Y2[keep].view(np.uint32), Y[keep].view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [3, 8])
+@pytest.mark.parametrize("N,K,gs", [(37, 16416, 32),   # 33 slices of 16 units: three passes of 11
+                                    (29, 8256, 96),    # 17 slices, three units per group
+                                    (23, 9216, 256),   # 18 slices, eight units per group
+                                    (40, 7168, 1024)]) # every slice inside one group
+def test_lanes_long_k(q4, M, N, K, gs):
+    q, s, z = quantized(0xB180 + M + K, N, K, gs)
+    check_lanes(q4, synth.lanes(0xB181 + K, M, K), q, s, z, K, gs, 0xB182)
+
+
+def test_lanes_many_rounds(q4):
+    """More tiles per block than the LDS partial table holds (70000 columns at
+    K = 16416: two rounds per block).  Random packed codes, integer zero
+    points; a contiguous run of columns across blocks and rounds, a random
+    sample and the last columns are checked."""
+    rng = np.random.default_rng(0xB700)
+    N, K, gs, M = 70000, 16416, 32, 3
+    q = rng.integers(0, 2**32, (N, K // 8), dtype=np.uint32)
+    s = (rng.random((N, K // gs), dtype=np.float32) * 0.01 + 1e-3).astype(np.float32)
+    z = rng.integers(0, 16, (N, K // gs)).astype(np.float32)
+    X = synth.lanes(0xB701, M, K)
+    Y = run_matvec(q4, X, q, s, z)
+    cols = np.unique(np.concatenate([np.arange(800), rng.choice(N, 300, replace=False),
+                                     np.arange(N - 8, N)]))
+    Y_ref, B = oracle.matvec(X, q[cols], s[cols], z[cols], K, gs)
+    assert_dot_close(Y[:, cols], Y_ref, B, "lanes, two rounds")
+
+
 @pytest.mark.parametrize("K,gs", [(256, 32), (1024, 128), (2080, 32), (5120, 64)])
 def test_one_hot_is_bit_exact(q4, K, gs):
     N = 70
