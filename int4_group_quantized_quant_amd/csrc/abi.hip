@@ -171,9 +171,9 @@ int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bp
 // streams best), columns split evenly over the B*P rows, one LDS partial per
 // (column, stream, lane, chunk), the activations staged once per block.
 //
-// Matrix-core kernel (plain, M >= 3): blocks of W <= 12 waves, each wave one
-// 16-unit slice of K per pass, 12 / W blocks per CU, the block's tiles of 16
-// columns in rounds that fit the partial table in LDS.
+// Matrix-core kernel (plain, M >= 3): blocks of W <= 8 waves, each wave one
+// slice of 16, 20 or 24 units of K per pass, 8 / W blocks per CU, the
+// block's tiles of 16 columns in rounds that fit the partial table in LDS.
 //
 // LDS kernel (larger K for one or two lanes): 256-thread blocks, the M
 // activation rows staged in LDS (M*K*4 bytes), columns split evenly over the
@@ -230,33 +230,40 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // kernel needs only the activations.
   }
   if (mode == kPlain && M >= 3) {
-    // Matrix-core lanes: W waves per block split K into slices of 16 units
-    // (P passes when there are more than 12 slices), about 12 waves per CU,
-    // one block's columns in rounds of RT tiles whose partials fit the LDS.
-    const int cls = slice_class(a.U / a.G);
-    const int nsl = (a.U + kSliceUnits - 1) / kSliceUnits;
-    const int P = (nsl + kSliceMaxWaves - 1) / kSliceMaxWaves;
-    const int W = (nsl + P - 1) / P;
-    int bpc = kSliceMaxWaves / W;
+    // Matrix-core lanes: slices of SU = 16, 20 or 24 units, at most 8 waves
+    // (two per SIMD) per block, P passes of the waves over the slices; one
+    // block's columns in rounds of RT tiles whose partials fit the LDS.
+    const int U = a.U;
+    int su = 16;
+    if (U > kSliceMaxWaves * 16) {
+      const int P = (U + kSliceMaxWaves * 24 - 1) / (kSliceMaxWaves * 24);
+      const int per_wave = ((U + P - 1) / P + kSliceMaxWaves - 1) / kSliceMaxWaves;
+      su = per_wave <= 16 ? 16 : (per_wave <= 20 ? 20 : 24);
+    }
+    const int cls = slice_class(U / a.G);
+    const int nsl = (U + su - 1) / su;
+    const int W = nsl < kSliceMaxWaves ? nsl : kSliceMaxWaves;
+    const int bpc = kSliceMaxWaves / W;
     const int64_t tiles = (N + 15) / 16;
     int64_t B = (int64_t)dev.cus * bpc;
     if (B > tiles) B = tiles;
     if (B < 1) B = 1;
     const int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
     const size_t budget = dev.lds_cu / (size_t)bpc < dev.lds_block ? dev.lds_cu / (size_t)bpc : dev.lds_block;
-    const size_t fixed = slice_lds_bytes(cls, W, 0);
-    const size_t per_tile = slice_lds_bytes(cls, W, 1) - fixed;
+    const size_t fixed = slice_lds_bytes(su, cls, W, 0);
+    const size_t per_tile = slice_lds_bytes(su, cls, W, 1) - fixed;
     if (fixed + per_tile > budget)
       return fail(INT4_ERR_SHAPE, "matrix-core lanes need %zu bytes of LDS per block; %zu available",
                   fixed + per_tile, budget);
     int64_t rt = (int64_t)((budget - fixed) / per_tile);
     if (rt > tiles_per_block) rt = tiles_per_block;
     a.rt = (int32_t)rt;
+    a.su = su;
     s->variant = kVariantSlice;
     s->ncol = 16;
     s->depth = 1;
     s->block_threads = 64 * W;
-    s->lds_bytes = slice_lds_bytes(cls, W, (int)rt);
+    s->lds_bytes = slice_lds_bytes(su, cls, W, (int)rt);
     s->grid = (int)B;
     a.total_waves = B * W;
     return INT4_OK;

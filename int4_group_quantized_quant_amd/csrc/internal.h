@@ -41,6 +41,7 @@ struct GemvArgs {
   int32_t part_floats;  // floats of the per-block partial table (register kernel)
   int32_t M;            // lanes (kPlain)
   int32_t rt;           // tiles of 16 columns per round (matrix-core kernel)
+  int32_t su;           // units per K slice (matrix-core kernel)
 };
 
 // Float offset of the staged activations in the register kernel's LDS: after
@@ -54,38 +55,35 @@ enum Variant : int {
   kVariantSlice = 2, // three to eight lanes on the matrix cores, K sliced over the waves
 };
 
-// Matrix-core lanes kernel.  A slice is 16 units (512 inputs) of K; each
-// wave holds one slice's activations and streams the block's tiles of 16
-// columns over it.  Its LDS holds, per wave, a stage of one tile (codes:
-// 16 columns of kSliceCodeStride dwords; scales and zero points: 16 columns
-// of slice_sz_stride dwords) and, per block, the partial sums of a round of
-// tiles: 8 rows x 16 columns per (tile, wave).
-constexpr int kSliceUnits = 16;
-constexpr int kSliceMaxWaves = 12;
-constexpr int kSliceCodeStride = 68;  // 64 dwords of codes + 4: conflict-free column reads
+// Matrix-core lanes kernel.  K is cut into slices of SU units (SU = 16, 20
+// or 24); each wave holds one slice's activations in registers and streams
+// the block's tiles of 16 columns over it.  Its LDS holds, per wave, a stage
+// of one tile (codes: 16 columns of 4*SU + 4 dwords; scales and zero points:
+// 16 columns of 8*SZW + 1 dwords) and, per block, the partial sums of a
+// round of tiles: 8 rows x 16 columns per (tile, wave).
+constexpr int kSliceMaxWaves = 8;  // two waves per SIMD
 
-// Group-size class of gsu = gs/32 units per group: 1, 2, 4 or 8 when gsu is
-// exactly that, 16 when gsu is a multiple of 16 (a slice lies in one group),
-// 0 for any other size.
-__host__ __device__ constexpr int slice_class(int gsu) {
-  return gsu == 1 || gsu == 2 || gsu == 4 || gsu == 8 ? gsu : (gsu % 16 == 0 ? 16 : 0);
+// Group-size class of gsu = gs/32 units per group: 1, 2 or 4 (slices start
+// on group boundaries and the group structure is fixed at compile time), or
+// 0 for any other size (worked out per unit at run time; gsu >= 3).
+__host__ __device__ constexpr int slice_class(int gsu) { return gsu == 1 || gsu == 2 || gsu == 4 ? gsu : 0; }
+
+// Groups a slice of su units can touch: su / gsu for the fixed classes,
+// ceil((su - 1) / 3) + 1 otherwise.
+__host__ __device__ constexpr int slice_groups(int su, int cls) { return cls ? su / cls : (su + 1) / 3 + 1; }
+// Scale words (and zero-point words) each lane loads per tile: its quarter
+// of the slice's groups, rounded up.
+__host__ __device__ constexpr int slice_sz_words(int su, int cls) { return (slice_groups(su, cls) + 3) / 4; }
+// Dwords per column of the stage: codes padded so that the 16 columns start
+// on distinct banks (4*su + 4 is 4 mod 64, 20 mod 64 or 36 mod 64), scale and
+// zero-point words padded to an odd stride.
+__host__ __device__ constexpr int slice_code_stride(int su) { return 4 * su + 4; }
+__host__ __device__ constexpr int slice_sz_stride(int su, int cls) { return 8 * slice_sz_words(su, cls) + 1; }
+__host__ __device__ constexpr int slice_stage_words(int su, int cls) {
+  return 16 * slice_code_stride(su) + 16 * slice_sz_stride(su, cls);
 }
-// Scale (and zero-point) words each lane loads per tile: its quarter of the
-// slice's groups, which number at most 16 / gsu + 1.
-__host__ __device__ constexpr int slice_sz_words(int cls) {
-  return cls == 1 ? 4 : (cls == 2 || cls == 0 ? 2 : 1);
-}
-// Dwords per column of the scale/zero stage: 4 words per lane group for the
-// scales, the same for the zero points, padded so that the 16 columns fall
-// on distinct banks and vector writes stay aligned.
-__host__ __device__ constexpr int slice_sz_stride(int cls) {
-  return slice_sz_words(cls) == 4 ? 36 : (slice_sz_words(cls) == 2 ? 18 : 9);
-}
-__host__ __device__ constexpr int slice_stage_words(int cls) {
-  return 16 * kSliceCodeStride + 16 * slice_sz_stride(cls);
-}
-inline size_t slice_lds_bytes(int cls, int waves, int rt) {
-  return ((size_t)waves * slice_stage_words(cls) + (size_t)rt * waves * 128) * sizeof(float);
+inline size_t slice_lds_bytes(int su, int cls, int waves, int rt) {
+  return ((size_t)waves * slice_stage_words(su, cls) + (size_t)rt * waves * 128) * sizeof(float);
 }
 
 struct LaunchShape {

@@ -866,32 +866,36 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restr
 
 // Three to eight decode lanes on the matrix cores, v_mfma_f32_16x16x32_f16:
 // D[i][col] = sum_k A[i][k] * B[k][col] over the 32 inputs of one unit.
-//  * B[k][col] = (code - zero) * 2^-24: the nibble masked into an fp16
-//    subnormal minus the zero point, exact (the matrix cores keep fp16
+//  * B[k][col] = (code - zero) * 2^-24 for the even nibbles of a word and
+//    (code - zero) * 2^-20 for the odd ones: each nibble is masked in place
+//    into an fp16 subnormal (the odd ones four bits up) and the zero point,
+//    shifted the same way, subtracted; all exact (the matrix cores keep fp16
 //    subnormal inputs).
-//  * A row i < 8 holds hi and row 8 + i holds lo for activation row m = i,
-//    where x[m][k] * 2^e = hi + lo, hi = fp16(y) and lo = fp16(y - hi), both
-//    rounded toward zero; e is a power of two per (row, slice) that puts the
-//    slice's largest |x| just below 2^14.  One MFMA yields the hi and the lo
-//    products of every row; they are added once per tile.
+//  * A row i < 8 holds hi and row 8 + i holds lo for activation row m = i:
+//    y = x[m][k] * 2^e (times 2^-4 for the odd-nibble inputs) is split into
+//    hi = fp16(y) and lo = fp16(y - hi), both rounded toward zero; e is a
+//    power of two per (row, slice) that puts the slice's largest |x| just
+//    below 2^14.  One MFMA yields the hi and the lo products of every row;
+//    they are added once per tile.
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
 // D[4*(l/16) .. +3][l%16].  Slot 8g + 2v of a unit is input 8g + v and slot
 // 8g + 2v + 1 is input 8g + v + 4, the order the nibble masks produce.
 //
 // Work split.  Block b owns columns [b*N/B, (b+1)*N/B) in tiles of 16
-// columns.  Its W waves split K into slices of 16 units: wave w takes slices
-// w, w + W, ..., keeps the A operand of its slice in 64 registers and streams
-// every tile of the block over that slice.  Per tile, one load instruction
-// covers 4 columns x 16 units (lanes 16c .. 16c+15 read 256 contiguous bytes
-// of one column), and each lane loads 1, 2 or 4 scale and zero-point words of
-// its column.  The tile passes through the wave's LDS stage to reach the
-// matrix layout (lane (g, col) reads word g of every unit of column col).
-// Each unit's D is scaled by its group's scale into four accumulators; at the
-// end of the tile the lo rows are added to the hi rows, multiplied by
-// 2^(24 - e) and written to the block's partial table.  After a round of
-// tiles, the block adds the waves' partials in wave order and stores Y.
-// Every row's arithmetic reads only that row's activations, so a lane's
-// outputs never depend on the other lanes.
+// columns.  K is cut into slices of SU units; the block's W <= 8 waves (two
+// per SIMD) take slices w, w + W, ..., keep the A operand of the slice in
+// 4*SU registers and stream every tile of the block over it, DEPTH tiles of
+// loads in flight.  A tile's codes load as 64 consecutive 16-byte units per
+// instruction (SU units of each column in a row, so each column's bytes are
+// contiguous); each lane also loads SZW scale and zero-point words of its
+// column.  The tile passes through the wave's LDS stage to reach the matrix
+// layout (lane (g, col) reads word g of every unit of column col).  Each
+// unit's D is scaled by its group's scale into four accumulators; at the end
+// of the tile the lo rows are added to the hi rows, multiplied by 2^(24 - e)
+// and written to the block's partial table.  After a round of tiles, the
+// block adds the waves' partials in wave order and stores Y.  Every row's
+// arithmetic reads only that row's activations, so a lane's outputs never
+// depend on the other lanes.
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -909,141 +913,66 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return e < -100 ? -100 : (e > 100 ? 100 : e);
 }
 
-template <int SZW>
-struct SzWords {
-  uint32_t w[SZW];
+template <int NW>
+struct Words {
+  uint32_t w[NW];
 };
 
-template <int SZW>
-__device__ __forceinline__ SzWords<SZW> load_sz(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  SzWords<SZW> o;
-  if constexpr (SZW == 4) {
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadNonTemporal));
-    o.w[0] = v.x;
-    o.w[1] = v.y;
-    o.w[2] = v.z;
-    o.w[3] = v.w;
-  } else if constexpr (SZW == 2) {
-    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kLoadNonTemporal));
-    o.w[0] = v.x;
-    o.w[1] = v.y;
-  } else {
-    o.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kLoadNonTemporal);
+// NW consecutive words from a buffer: 16-byte loads, then 8, then 4.
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  Words<NW> o;
+#pragma unroll
+  for (int i = 0; i + 4 <= NW; i += 4) {
+    const u32x4 v =
+        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4u * i, 0, kLoadNonTemporal));
+    o.w[i] = v.x;
+    o.w[i + 1] = v.y;
+    o.w[i + 2] = v.z;
+    o.w[i + 3] = v.w;
   }
+  constexpr int i2 = NW & ~3;
+  if constexpr (NW - i2 >= 2) {
+    const u32x2 v =
+        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4u * i2, 0, kLoadNonTemporal));
+    o.w[i2] = v.x;
+    o.w[i2 + 1] = v.y;
+  }
+  if constexpr ((NW - i2) % 2 == 1)
+    o.w[NW - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4u * (NW - 1), 0, kLoadNonTemporal);
   return o;
 }
 
-template <int SZW>
-__device__ __forceinline__ void store_sz(uint32_t* p, const uint32_t (&v)[SZW]) {
-  if constexpr (SZW == 4) {
-    *reinterpret_cast<u32x4*>(p) = u32x4{v[0], v[1], v[2], v[3]};
-  } else if constexpr (SZW == 2) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{v[0], v[1]};
-  } else {
-    p[0] = v[0];
-  }
-}
-
-// One tile of one slice in flight: 4 x 16 bytes of codes, the lane's scale
-// and zero-point words.
-template <int SZW>
+// One tile of one slice in flight: SU/4 x 16 bytes of codes, the lane's
+// scale and zero-point words.
+template <int SU, int SZW>
 struct SliceTile {
-  u32x4 c[4];
-  SzWords<SZW> s, z;
+  u32x4 c[SU / 4];
+  Words<SZW> s, z;
 };
 
-// The A operand of slice `sl` (16 units from unit 16*sl) for lane (g, i):
-// A[t] holds, for unit t, row i of the k-slots 8g .. 8g+7.  Lanes i < 8 take
-// the hi parts of row i, lanes i >= 8 the lo parts of row i - 8.  Each lane
-// loads 8 units of its row (lanes i < 8 units 0..7, lanes i >= 8 units
-// 8..15), the slice's row maximum is reduced over the 8 lanes of the row,
-// and the partner lane (i ^ 8) sends the parts this lane needs for the
-// other 8 units.  f[r] receives 2^(24 - e) of output row 4*(g & 1) + r.
-__device__ __forceinline__ void slice_operand(const GemvArgs& a, int sl, int lane, u32x4 (&A)[16],
-                                              float (&f)[4]) {
-  const int K = a.K, U = a.U, M = a.M;
-  const int g = lane >> 4;
-  const int i = lane & 15;
-  const int m = i & 7;
-  const int half = i >> 3;
-  const bool row_live = m < M;
-  const int mc = row_live ? m : 0;
-  float4 p[8], q[8];
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const int u = 16 * sl + 8 * half + tt;
-    const bool live = row_live && u < U;
-    const int uc = u < U ? u : U - 1;
-    const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)mc * K + 32 * uc + 8 * g);
-    p[tt] = src[0];
-    q[tt] = src[1];
-    if (!live) {
-      p[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
-      q[tt] = p[tt];
-    }
-  }
-  float mx = 0.0f;
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(p[tt].x), fabsf(p[tt].y)), fmaxf(fabsf(p[tt].z), fabsf(p[tt].w))));
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q[tt].x), fabsf(q[tt].y)), fmaxf(fabsf(q[tt].z), fabsf(q[tt].w))));
-  }
-  {
-    auto r32 = __builtin_amdgcn_permlane32_swap(fbits(mx), fbits(mx), false, false);
-    mx = fmaxf(bitsf(r32[0]), bitsf(r32[1]));
-    auto r16 = __builtin_amdgcn_permlane16_swap(fbits(mx), fbits(mx), false, false);
-    mx = fmaxf(bitsf(r16[0]), bitsf(r16[1]));
-    mx = fmaxf(mx, dpp_move<0x128>(mx));
-  }
-  const int e = row_exponent(mx);
-  const float sc = pow2f(e);
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const float xv[8] = {p[tt].x, q[tt].x, p[tt].y, q[tt].y, p[tt].z, q[tt].z, p[tt].w, q[tt].w};
-    u32x4 h, l;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float y0 = xv[2 * k] * sc, y1 = xv[2 * k + 1] * sc;
-      const auto hh = __builtin_amdgcn_cvt_pkrtz(y0, y1);
-      const auto ll = __builtin_amdgcn_cvt_pkrtz(y0 - (float)hh[0], y1 - (float)hh[1]);
-      h[k] = __builtin_bit_cast(uint32_t, hh);
-      l[k] = __builtin_bit_cast(uint32_t, ll);
-    }
-    // Lanes i < 8 keep hi and send lo; lanes i >= 8 keep lo and send hi.
-    u32x4 keep = half ? l : h;
-    u32x4 send = half ? h : l;
-    u32x4 recv;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) recv[k] = fbits(dpp_move<0x128>(bitsf(send[k])));
-    A[tt] = half ? recv : keep;
-    A[8 + tt] = half ? keep : recv;
-  }
-  const int r0 = 4 * (g & 1);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e_lo = __builtin_amdgcn_readlane(e, r);
-    const int e_hi = __builtin_amdgcn_readlane(e, 4 + r);
-    f[r] = pow2f(24 - (r0 ? e_hi : e_lo));
-  }
-}
-
-template <int GS>
+template <int SU, int GS, int DEPTH>
 __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
   extern __shared__ float4 lds4[];
-  constexpr int SZW = slice_sz_words(GS);
-  constexpr int SS = slice_sz_stride(GS);
-  constexpr int kStage = slice_stage_words(GS);
+  constexpr int NJ = SU / 4;  // load instructions per tile
+  constexpr int SZW = slice_sz_words(SU, GS);
+  constexpr int CS = slice_code_stride(SU);
+  constexpr int SS = slice_sz_stride(SU, GS);
+  constexpr int kStage = slice_stage_words(SU, GS);
+  constexpr int H = SU / 2;  // units each half of a row's lanes converts
+  static_assert(DEPTH == 2 || DEPTH == 3, "the ring below holds two or three tiles");
   const int M = a.M;
+  const int K = a.K;
   const int U = a.U;
   const int G = a.G;
   const int gsu = U / G;
   const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
-  const int hi4 = lane >> 4;   // load: column quarter; matrix: k group / D row group
-  const int lo16 = lane & 15;  // load: unit; matrix: column
+  const int hi4 = lane >> 4;   // matrix layout: k group / D row group
+  const int lo16 = lane & 15;  // matrix layout: column
   const int wave = uniform_int(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
-  const int nsl = (U + kSliceUnits - 1) / kSliceUnits;
+  const int nsl = (U + SU - 1) / SU;
   const int64_t cb = uniform_i64((int64_t)blockIdx.x * N / gridDim.x);
   const int64_t ce = uniform_i64(((int64_t)blockIdx.x + 1) * N / gridDim.x);
   const int ntile = (int)((ce - cb + 15) >> 4);
@@ -1056,118 +985,209 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   const char* sbase = reinterpret_cast<const char*>(a.s[0]);
   const char* zbase = reinterpret_cast<const char*>(a.z[0]);
 
+  // Load layout: instruction j, lane l carries unit t of column col, where
+  // 64j + l = SU*col + t.  The same unit goes to stage dword col*CS + 4t.
+  uint32_t ld_unit[NJ], st_off[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = 64 * j + lane;
+    const int col = c / SU;
+    const int t = c - col * SU;
+    ld_unit[j] = (uint32_t)(col * U + t);
+    st_off[j] = (uint32_t)(col * CS + 4 * t);
+  }
+
   for (int r0 = 0; r0 < ntile; r0 += RT) {
     const int rn = ntile - r0 < RT ? ntile - r0 : RT;
     bool first_pass = true;
     for (int sl = wave; sl < nsl; sl += W) {
-      const int u0 = kSliceUnits * sl;
+      const int u0 = SU * sl;
       const int h0 = u0 / gsu;
 
-      // Tile ti of the block in flight; tiles past the round read nothing
-      // (an empty buffer range), so every load is unconditional.
-      auto load = [&](int ti, SliceTile<SZW>& r) {
+      // Activations of the slice for lane (g, i): row m = i & 7, units
+      // H*half .. H*half + H - 1 (half = i >> 3), inputs 8g .. 8g+7 of each.
+      const int m = lo16 & 7;
+      const int half = lo16 >> 3;
+      const bool row_live = m < M;
+      float4 xp[H], xq[H];
+#pragma unroll
+      for (int tt = 0; tt < H; ++tt) {
+        xp[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        xq[tt] = xp[tt];
+      }
+      if (row_live) {
+#pragma unroll
+        for (int tt = 0; tt < H; ++tt) {
+          const int u = u0 + H * half + tt;
+          const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * K + 32 * (u < U ? u : U - 1) + 8 * hi4);
+          xp[tt] = src[0];  // units past K (clamped address) are masked below
+          xq[tt] = src[1];
+        }
+      }
+      // Every wave issues its activation loads before any wave issues weight
+      // loads: the memory pipeline serves a CU's loads in issue order, so the
+      // small activation reads must not queue behind the tiles.
+      if (first_pass) __builtin_amdgcn_s_barrier();
+
+      // Tile ti of the block; tiles past the round read nothing (an empty
+      // buffer range), so every load is unconditional.
+      auto load = [&](int ti, SliceTile<SU, SZW>& r) {
         const bool live = ti < r0 + rn;
         const int64_t col0 = cb + 16 * (int64_t)(live ? ti : r0);
         const int ncols = live ? (ce - col0 < 16 ? (int)(ce - col0) : 16) : 0;
         const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + col0 * (int64_t)U * 16), (short)0,
                                                           ncols * U * 16, kBufferWord3);
-        const uint32_t vq = ((uint32_t)hi4 * (uint32_t)U + (uint32_t)(u0 + lo16)) * 16u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           r.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rq, vq, (uint32_t)j * 64u * (uint32_t)U, kLoadNonTemporal));
+                                                 rq, ld_unit[j] * 16u, (uint32_t)u0 * 16u, kLoadNonTemporal));
         const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(sbase + col0 * (int64_t)G * 4), (short)0,
                                                           ncols * G * 4, kBufferWord3);
         const auto rz = __builtin_amdgcn_make_buffer_rsrc((void*)(zbase + col0 * (int64_t)G * 4), (short)0,
                                                           ncols * G * 4, kBufferWord3);
         const int colc = lo16 < ncols ? lo16 : (ncols > 0 ? ncols - 1 : 0);
         const uint32_t vs = ((uint32_t)colc * (uint32_t)G + (uint32_t)(h0 + hi4 * SZW)) * 4u;
-        r.s = load_sz<SZW>(rs, vs);
-        r.z = load_sz<SZW>(rz, vs);
+        r.s = load_words<SZW>(rs, vs);
+        r.z = load_words<SZW>(rz, vs);
       };
 
-      // Codes to [col][unit][word] (column stride kSliceCodeStride dwords);
-      // scales and zero points (as fp16 subnormal pairs) to [col][group],
-      // groups past the column's last set to zero: they hold only units
-      // past K, whose activations are zero.
-      auto write_stage = [&](const SliceTile<SZW>& r) {
+      // Codes to [col][unit][word]; scales and zero points (as fp16
+      // subnormal pairs) to [col][group], groups past the column's last set
+      // to zero: they hold only units past K, whose activations are zero.
+      auto write_stage = [&](const SliceTile<SU, SZW>& r) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<u32x4*>(stage + (4 * j + hi4) * kSliceCodeStride + 4 * lo16) = r.c[j];
-        uint32_t sv[SZW], zv[SZW];
+        for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4*>(stage + st_off[j]) = r.c[j];
+        uint32_t* zs = stage + 16 * CS + lo16 * SS + hi4 * SZW;
 #pragma unroll
         for (int c = 0; c < SZW; ++c) {
           const bool ok = h0 + hi4 * SZW + c < G;
           const uint32_t zi = (uint32_t)bitsf(r.z.w[c]);
-          sv[c] = ok ? r.s.w[c] : 0u;
-          zv[c] = ok ? (zi | (zi << 16)) : 0u;
+          zs[c] = ok ? r.s.w[c] : 0u;
+          zs[4 * SZW + c] = ok ? (zi | (zi << 16)) : 0u;
         }
-        uint32_t* zs = stage + 16 * kSliceCodeStride + lo16 * SS + hi4 * SZW;
-        store_sz<SZW>(zs, sv);
-        store_sz<SZW>(zs + 4 * SZW, zv);
       };
 
-      SliceTile<SZW> ra, rb;
-      load(r0, ra);
-      load(r0 + 1, rb);
+      // All but the last ring slot load now; the last one after the A
+      // operand is built, when the activations' registers are free.
+      SliceTile<SU, SZW> ring[DEPTH];
+#pragma unroll
+      for (int d = 0; d + 1 < DEPTH; ++d) load(r0 + d, ring[d]);
       __builtin_amdgcn_sched_barrier(0);
 
-      u32x4 A[16];
+      // The slice's A operand.  The row maximum is reduced over the row's 8
+      // lanes; e is per (row, slice).  Lanes i < 8 keep hi of their units
+      // and take hi of the other half from lane i + 8; lanes i >= 8 keep lo
+      // and take lo from lane i - 8 (DPP row rotation by 8, written only to
+      // the receiving half's banks).
+      u32x4 A[SU];
       float f[4];
-      slice_operand(a, sl, lane, A, f);
-
-      // Group structure of the slice (wave-uniform): unit t lies in group
-      // h0 + h(t); first(t) / last(t) mark the slice's part of a group.
-      uint64_t hpack = 0;
-      uint32_t fmask = 0, lmask = 0;
-      if constexpr (GS == 0) {
+      {
+        float mx = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kSliceUnits; ++t) {
-          const int u = u0 + t;
-          const int gq = u / gsu;
-          const int rem = u - gq * gsu;
-          hpack |= (uint64_t)(gq - h0) << (4 * t);
-          if (rem == 0 || t == 0) fmask |= 1u << t;
-          if (rem == gsu - 1 || t == kSliceUnits - 1) lmask |= 1u << t;
+        for (int tt = 0; tt < H; ++tt) {
+          const bool ok = u0 + H * half + tt < U;
+          float v = fmaxf(fmaxf(fabsf(xp[tt].x), fabsf(xp[tt].y)), fmaxf(fabsf(xp[tt].z), fabsf(xp[tt].w)));
+          v = fmaxf(v, fmaxf(fmaxf(fabsf(xq[tt].x), fabsf(xq[tt].y)), fmaxf(fabsf(xq[tt].z), fabsf(xq[tt].w))));
+          mx = fmaxf(mx, ok ? v : 0.0f);
+        }
+        auto r32 = __builtin_amdgcn_permlane32_swap(fbits(mx), fbits(mx), false, false);
+        mx = fmaxf(bitsf(r32[0]), bitsf(r32[1]));
+        auto r16 = __builtin_amdgcn_permlane16_swap(fbits(mx), fbits(mx), false, false);
+        mx = fmaxf(bitsf(r16[0]), bitsf(r16[1]));
+        mx = fmaxf(mx, dpp_move<0x128>(mx));
+        const int e = row_exponent(mx);
+        const float sc = pow2f(e);
+        const float sc16 = pow2f(e - 4);
+#pragma unroll
+        for (int tt = 0; tt < H; ++tt) {
+          const bool ok = u0 + H * half + tt < U;
+          const float s0 = ok ? sc : 0.0f, s1 = ok ? sc16 : 0.0f;
+          const float4 p = xp[tt], q = xq[tt];
+          const float y[8] = {p.x * s0, q.x * s0, p.y * s1, q.y * s1, p.z * s0, q.z * s0, p.w * s1, q.w * s1};
+          u32x4 h, l;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const auto hh = __builtin_amdgcn_cvt_pkrtz(y[2 * k], y[2 * k + 1]);
+            const auto ll = __builtin_amdgcn_cvt_pkrtz(y[2 * k] - (float)hh[0], y[2 * k + 1] - (float)hh[1]);
+            h[k] = __builtin_bit_cast(uint32_t, hh);
+            l[k] = __builtin_bit_cast(uint32_t, ll);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            A[tt][k] = __builtin_amdgcn_update_dpp(h[k], l[k], 0x128, 0xF, 0xC, false);
+            A[H + tt][k] = __builtin_amdgcn_update_dpp(l[k], h[k], 0x128, 0xF, 0x3, false);
+          }
+        }
+        const int rbase = 4 * (hi4 & 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e_lo = __builtin_amdgcn_readlane(e, r);
+          const int e_hi = __builtin_amdgcn_readlane(e, 4 + r);
+          f[r] = pow2f(24 - (rbase ? e_hi : e_lo));
         }
       }
+      load(r0 + DEPTH - 1, ring[DEPTH - 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int rem0 = u0 - h0 * gsu;  // unit-in-group of the slice's first unit
 
       auto compute = [&](int i) {
-        const uint32_t* cs = stage + lo16 * kSliceCodeStride + hi4;
-        const uint32_t* zs = stage + 16 * kSliceCodeStride + lo16 * SS;
-        uint32_t wd[kSliceUnits];
+        const uint32_t* cs = stage + lo16 * CS + hi4;
+        const uint32_t* zs = stage + 16 * CS + lo16 * SS;
+        uint32_t wd[SU];
 #pragma unroll
-        for (int t = 0; t < kSliceUnits; ++t) wd[t] = cs[4 * t];
+        for (int t = 0; t < SU; ++t) wd[t] = cs[4 * t];
         const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t acc = z4, d = z4;
-#pragma unroll
-        for (int t = 0; t < kSliceUnits; ++t) {
-          int h;
-          bool first, last;
-          if constexpr (GS == 0) {
-            h = (int)((hpack >> (4 * t)) & 15u);
-            first = (fmask >> t) & 1u;
-            last = (lmask >> t) & 1u;
-          } else if constexpr (GS == 16) {
-            h = 0;
-            first = t == 0;
-            last = t == kSliceUnits - 1;
-          } else {
-            h = t / GS;
-            first = t % GS == 0;
-            last = t % GS == GS - 1;
-          }
-          const half2_t zh = as_half2(zs[4 * SZW + h]);
+        f32x4_t acc = z4;
+        // B of unit t: nibbles minus zero point (zh: the group's zero point
+        // as an fp16 subnormal pair).
+        auto unit_b = [&](int t, uint32_t zh) {
+          const half2_t z0 = as_half2(zh), z1 = as_half2(zh << 4);
+          const uint32_t w = wd[t], w8 = wd[t] >> 8;
           u32x4 bw;
+          bw[0] = __builtin_bit_cast(uint32_t, as_half2(w & 0x000F000Fu) - z0);
+          bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
+          bw[2] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x000F000Fu) - z0);
+          bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
+          return __builtin_bit_cast(half8_t, bw);
+        };
+        if constexpr (GS != 0) {
+          // Groups alternate between two accumulators; a group is scaled
+          // into acc after the next group's products are issued, so the
+          // matrix core never waits for the scaling.
+          constexpr int NG = SU / GS;
+          f32x4_t dd[2] = {z4, z4};
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            bw[v] = __builtin_bit_cast(uint32_t, as_half2((wd[t] >> (4 * v)) & 0x000F000Fu) - zh);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]),
-                                                     __builtin_bit_cast(half8_t, bw), first ? z4 : d, 0, 0, 0);
-          if (last) {
-            const float sv = bitsf(zs[h]);
+          for (int t = 0; t < SU; ++t) {
+            const int hh = t / GS;
+            dd[hh & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]),
+                                                               unit_b(t, zs[4 * SZW + hh]),
+                                                               t % GS == 0 ? z4 : dd[hh & 1], 0, 0, 0);
+            if (t % GS == GS - 1 && hh > 0) {
+              const float sv = bitsf(zs[hh - 1]);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d[rr], acc[rr]);
+              for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, dd[(hh - 1) & 1][rr], acc[rr]);
+            }
+          }
+          const float sv = bitsf(zs[NG - 1]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, dd[(NG - 1) & 1][rr], acc[rr]);
+        } else {
+          f32x4_t d = z4;
+          int rem = rem0, h = 0;
+#pragma unroll
+          for (int t = 0; t < SU; ++t) {
+            const int hh = h;
+            const bool first = rem == 0 || t == 0;
+            const bool last = rem == gsu - 1 || t == SU - 1;
+            rem = rem + 1 == gsu ? 0 : rem + 1;
+            h += rem == 0 ? 1 : 0;
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]), unit_b(t, zs[4 * SZW + hh]),
+                                                       first ? z4 : d, 0, 0, 0);
+            if (last) {
+              const float sv = bitsf(zs[hh]);
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d[rr], acc[rr]);
+            }
           }
         }
         // Lanes 0..31 hold the hi rows, lanes 32..63 the lo rows.
@@ -1181,18 +1201,22 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
         }
       };
 
-      for (int i = 0;; i += 2) {
-        write_stage(ra);
-        load(r0 + i + 2, ra);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(i);
-        if (i + 1 >= rn) break;
-        write_stage(rb);
-        load(r0 + i + 3, rb);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(i + 1);
-        if (i + 2 >= rn) break;
+      // Whole turns of the ring: stage writes and loads unconditional
+      // (tiles past the round read nothing), one back edge, so each stage
+      // write waits only for its own slot; only the compute is skipped past
+      // the round's last tile.
+      for (int i = 0; i < rn; i += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          write_stage(ring[d]);
+          load(r0 + i + d + DEPTH, ring[d]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + d < rn) compute(i + d);
+        }
       }
+      // The refills past the round are still in flight; let them land before
+      // the ring registers are reused.
+      __builtin_amdgcn_s_waitcnt(0);
       first_pass = false;
     }
     __syncthreads();
@@ -1202,13 +1226,13 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
       const int c = o & 15;
       const int tm = o >> 4;
       const int i = tm / M;
-      const int m = tm - i * M;
+      const int mm = tm - i * M;
       const int64_t col = cb + 16 * (int64_t)(r0 + i) + c;
       if (col < ce) {
-        const float* pp = part + ((size_t)(i * W) * 8 + m) * 16 + c;
+        const float* pp = part + ((size_t)(i * W) * 8 + mm) * 16 + c;
         float y = pp[0];
         for (int w = 1; w < W; ++w) y += pp[(size_t)w * 128];
-        a.out[0][(int64_t)m * N + col] = y;
+        a.out[0][(int64_t)mm * N + col] = y;
       }
     }
     __syncthreads();
@@ -1277,17 +1301,21 @@ hipError_t dispatch_lds_m(const GemvArgs& a, const LaunchShape& s, hipStream_t s
   return s.ncol == 1 ? launch_lds<kPlain, M, 1>(a, s, st, occ) : launch_lds<kPlain, M, 2>(a, s, st, occ);
 }
 
-hipError_t dispatch_slice(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
-  static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised8{false}, raised16{false},
-      raised0{false};
+template <int SU, int DEPTH>
+hipError_t dispatch_slice_su(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised0{false};
   switch (slice_class(a.U / a.G)) {
-    case 1: return launch_or_query(gemv_slice_kernel<1>, raised1, a, s, st, occ);
-    case 2: return launch_or_query(gemv_slice_kernel<2>, raised2, a, s, st, occ);
-    case 4: return launch_or_query(gemv_slice_kernel<4>, raised4, a, s, st, occ);
-    case 8: return launch_or_query(gemv_slice_kernel<8>, raised8, a, s, st, occ);
-    case 16: return launch_or_query(gemv_slice_kernel<16>, raised16, a, s, st, occ);
-    default: return launch_or_query(gemv_slice_kernel<0>, raised0, a, s, st, occ);
+    case 1: return launch_or_query(gemv_slice_kernel<SU, 1, DEPTH>, raised1, a, s, st, occ);
+    case 2: return launch_or_query(gemv_slice_kernel<SU, 2, DEPTH>, raised2, a, s, st, occ);
+    case 4: return launch_or_query(gemv_slice_kernel<SU, 4, DEPTH>, raised4, a, s, st, occ);
+    default: return launch_or_query(gemv_slice_kernel<SU, 0, DEPTH>, raised0, a, s, st, occ);
   }
+}
+
+hipError_t dispatch_slice(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if (a.su == 24) return dispatch_slice_su<24, 2>(a, s, st, occ);
+  if (a.su == 20) return dispatch_slice_su<20, 3>(a, s, st, occ);
+  return dispatch_slice_su<16, 3>(a, s, st, occ);
 }
 
 hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
