@@ -250,8 +250,8 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     if (B < 1) B = 1;
     const int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
     const size_t budget = dev.lds_cu / (size_t)bpc < dev.lds_block ? dev.lds_cu / (size_t)bpc : dev.lds_block;
-    const size_t fixed = slice_lds_bytes(su, cls, W, 0);
-    const size_t per_tile = slice_lds_bytes(su, cls, W, 1) - fixed;
+    const size_t fixed = slice_lds_bytes(su, cls, a.G, W, 0);
+    const size_t per_tile = slice_lds_bytes(su, cls, a.G, W, 1) - fixed;
     if (fixed + per_tile > budget)
       return fail(INT4_ERR_SHAPE, "matrix-core lanes need %zu bytes of LDS per block; %zu available",
                   fixed + per_tile, budget);
@@ -263,7 +263,8 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     s->ncol = 16;
     s->depth = 1;
     s->block_threads = 64 * W;
-    s->lds_bytes = slice_lds_bytes(su, cls, W, (int)rt);
+    s->lds_bytes = slice_lds_bytes(su, cls, a.G, W, (int)rt);
+    a.g_recip = a.G == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + (uint64_t)a.G - 1) / (uint64_t)a.G);
     s->grid = (int)B;
     a.total_waves = B * W;
     return INT4_OK;

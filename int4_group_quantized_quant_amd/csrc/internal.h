@@ -42,6 +42,7 @@ struct GemvArgs {
   int32_t M;            // lanes (kPlain)
   int32_t rt;           // tiles of 16 columns per round (matrix-core kernel)
   int32_t su;           // units per K slice (matrix-core kernel)
+  uint32_t g_recip;     // ceil(2^32 / G), 0 when G = 1 (matrix-core kernel's table copy)
 };
 
 // Float offset of the staged activations in the register kernel's LDS: after
@@ -58,9 +59,10 @@ enum Variant : int {
 // Matrix-core lanes kernel.  K is cut into slices of SU units (SU = 16, 20
 // or 24); each wave holds one slice's activations in registers and streams
 // the block's tiles of 16 columns over it.  Its LDS holds, per wave, a stage
-// of one tile (codes: 16 columns of 4*SU + 4 dwords; scales and zero points:
-// 16 columns of 8*SZW + 1 dwords) and, per block, the partial sums of a
-// round of tiles: 8 rows x 16 columns per (tile, wave).
+// of one tile's codes (16 columns of 4*SU + 4 dwords) and, per block, for a
+// round of RT tiles: the partial sums (8 rows x 16 columns per (tile, wave))
+// and a table of the round's scales and zero points (16*RT columns of GP
+// dwords each, for both).
 constexpr int kSliceMaxWaves = 8;  // two waves per SIMD
 
 // Group-size class of gsu = gs/32 units per group: 1, 2 or 4 (slices start
@@ -71,19 +73,19 @@ __host__ __device__ constexpr int slice_class(int gsu) { return gsu == 1 || gsu 
 // Groups a slice of su units can touch: su / gsu for the fixed classes,
 // ceil((su - 1) / 3) + 1 otherwise.
 __host__ __device__ constexpr int slice_groups(int su, int cls) { return cls ? su / cls : (su + 1) / 3 + 1; }
-// Scale words (and zero-point words) each lane loads per tile: its quarter
-// of the slice's groups, rounded up.
-__host__ __device__ constexpr int slice_sz_words(int su, int cls) { return (slice_groups(su, cls) + 3) / 4; }
-// Dwords per column of the stage: codes padded so that the 16 columns start
-// on distinct banks (4*su + 4 is 4 mod 64, 20 mod 64 or 36 mod 64), scale and
-// zero-point words padded to an odd stride.
+// Dwords per column of the code stage: padded so that the 16 columns start on
+// distinct pairs of banks.
 __host__ __device__ constexpr int slice_code_stride(int su) { return 4 * su + 4; }
-__host__ __device__ constexpr int slice_sz_stride(int su, int cls) { return 8 * slice_sz_words(su, cls) + 1; }
-__host__ __device__ constexpr int slice_stage_words(int su, int cls) {
-  return 16 * slice_code_stride(su) + 16 * slice_sz_stride(su, cls);
+__host__ __device__ constexpr int slice_stage_words(int su) { return 16 * slice_code_stride(su); }
+// Dwords per column of the scale / zero-point table: the G groups, then
+// zeros for the groups a slice past K can name, rounded up to an odd count
+// so that the 16 columns of a tile fall on distinct banks.
+__host__ __device__ constexpr int slice_table_stride(int G, int su, int cls) {
+  return (G + slice_groups(su, cls)) | 1;
 }
-inline size_t slice_lds_bytes(int su, int cls, int waves, int rt) {
-  return ((size_t)waves * slice_stage_words(su, cls) + (size_t)rt * waves * 128) * sizeof(float);
+inline size_t slice_lds_bytes(int su, int cls, int G, int waves, int rt) {
+  return ((size_t)waves * slice_stage_words(su) + (size_t)rt * waves * 128 +
+          (size_t)2 * rt * 16 * slice_table_stride(G, su, cls)) * sizeof(float);
 }
 
 struct LaunchShape {

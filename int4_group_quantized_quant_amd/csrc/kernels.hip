@@ -913,58 +913,26 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return e < -100 ? -100 : (e > 100 ? 100 : e);
 }
 
-template <int NW>
-struct Words {
-  uint32_t w[NW];
-};
-
-// NW consecutive words from a buffer: 16-byte loads, then 8, then 4.
-template <int NW>
-__device__ __forceinline__ Words<NW> load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  Words<NW> o;
-#pragma unroll
-  for (int i = 0; i + 4 <= NW; i += 4) {
-    const u32x4 v =
-        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4u * i, 0, kLoadNonTemporal));
-    o.w[i] = v.x;
-    o.w[i + 1] = v.y;
-    o.w[i + 2] = v.z;
-    o.w[i + 3] = v.w;
-  }
-  constexpr int i2 = NW & ~3;
-  if constexpr (NW - i2 >= 2) {
-    const u32x2 v =
-        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4u * i2, 0, kLoadNonTemporal));
-    o.w[i2] = v.x;
-    o.w[i2 + 1] = v.y;
-  }
-  if constexpr ((NW - i2) % 2 == 1)
-    o.w[NW - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4u * (NW - 1), 0, kLoadNonTemporal);
-  return o;
-}
-
-// One tile of one slice in flight: SU/4 x 16 bytes of codes, the lane's
-// scale and zero-point words.
-template <int SU, int SZW>
+// One tile of one slice in flight: SU/4 x 16 bytes of codes.
+template <int SU>
 struct SliceTile {
   u32x4 c[SU / 4];
-  Words<SZW> s, z;
 };
 
 template <int SU, int GS, int DEPTH>
 __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
   extern __shared__ float4 lds4[];
   constexpr int NJ = SU / 4;  // load instructions per tile
-  constexpr int SZW = slice_sz_words(SU, GS);
   constexpr int CS = slice_code_stride(SU);
-  constexpr int SS = slice_sz_stride(SU, GS);
-  constexpr int kStage = slice_stage_words(SU, GS);
+  constexpr int kStage = slice_stage_words(SU);
   constexpr int H = SU / 2;  // units each half of a row's lanes converts
+  constexpr int NB = 5;      // table chunks per thread loaded ahead of the activations
   static_assert(DEPTH == 2 || DEPTH == 3, "the ring below holds two or three tiles");
   const int M = a.M;
   const int K = a.K;
   const int U = a.U;
   const int G = a.G;
+  const int GP = slice_table_stride(G, SU, GS);
   const int gsu = U / G;
   const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
@@ -981,6 +949,8 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   uint32_t* lds = reinterpret_cast<uint32_t*>(lds4);
   uint32_t* stage = lds + wave * kStage;
   float* part = reinterpret_cast<float*>(lds + W * kStage);
+  uint32_t* s_tab = lds + W * kStage + RT * W * 128;
+  uint32_t* z_tab = s_tab + RT * 16 * GP;
   const char* qbase = reinterpret_cast<const char*>(a.q[0]);
   const char* sbase = reinterpret_cast<const char*>(a.s[0]);
   const char* zbase = reinterpret_cast<const char*>(a.z[0]);
@@ -999,6 +969,55 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
 
   for (int r0 = 0; r0 < ntile; r0 += RT) {
     const int rn = ntile - r0 < RT ? ntile - r0 : RT;
+
+    // The round's scales and zero points.  Its columns [c_lo, c_lo + ncr)
+    // are consecutive rows of the [N][G] arrays, so each array is one
+    // contiguous range of ncr*G words, copied in 16-byte chunks by the whole
+    // block (whole cache lines) into [column][GP] tables; the zero points
+    // are stored as fp16 subnormal pairs, and the GP - G entries after a
+    // column's groups are zero (groups named by units past K, whose
+    // activations are zero).
+    const int64_t c_lo = cb + 16 * (int64_t)r0;
+    const int ncr = (int)((ce < c_lo + 16 * rn ? ce : c_lo + 16 * rn) - c_lo);
+    const int nel = ncr * G;
+    const int nchunk = (nel + 3) >> 2;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(sbase + c_lo * (int64_t)G * 4), (short)0, nel * 4,
+                                                      kBufferWord3);
+    const auto rz = __builtin_amdgcn_make_buffer_rsrc((void*)(zbase + c_lo * (int64_t)G * 4), (short)0, nel * 4,
+                                                      kBufferWord3);
+    auto table_put = [&](int c, u32x4 sv, u32x4 zv) {
+      if (c >= nchunk) return;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * c + k;
+        if (e < nel) {
+          // col = e / G: high word of e * ceil(2^32 / G), one step too
+          // large at most.
+          int col = a.g_recip ? (int)__umulhi((uint32_t)e, a.g_recip) : e;
+          int g = e - col * G;
+          if (g < 0) {
+            col -= 1;
+            g += G;
+          }
+          const uint32_t zi = (uint32_t)bitsf(zv[k]);
+          s_tab[col * GP + g] = sv[k];
+          z_tab[col * GP + g] = zi | (zi << 16);
+        }
+      }
+    };
+    u32x4 tsv[NB], tzv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint32_t off = (uint32_t)(threadIdx.x + b * blockDim.x) * 16u;
+      tsv[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadNonTemporal));
+      tzv[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, kLoadNonTemporal));
+    }
+    for (int col = wave; col < ncr; col += W)
+      if (lane < GP - G) {
+        s_tab[col * GP + G + lane] = 0u;
+        z_tab[col * GP + G + lane] = 0u;
+      }
+
     bool first_pass = true;
     for (int sl = wave; sl < nsl; sl += W) {
       const int u0 = SU * sl;
@@ -1024,14 +1043,33 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
           xq[tt] = src[1];
         }
       }
-      // Every wave issues its activation loads before any wave issues weight
-      // loads: the memory pipeline serves a CU's loads in issue order, so the
-      // small activation reads must not queue behind the tiles.
-      if (first_pass) __builtin_amdgcn_s_barrier();
+      if (first_pass) {
+        // The table: the first chunks are in flight, the rest (long rows
+        // only) load here; then every wave's table writes complete before
+        // any wave reads (LDS counter, then a barrier with no memory
+        // fence).  The barrier also makes every wave issue its activation
+        // loads before any wave issues weight loads: the memory pipeline
+        // serves a CU's loads in issue order, so the small activation reads
+        // must not queue behind the tiles.
+        // The thread index made opaque here, so that the table's per-element
+        // addresses are computed where they are used rather than hoisted
+        // and held across the activation loads.
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) table_put(tid + b * (int)blockDim.x, tsv[b], tzv[b]);
+        for (int c = tid + NB * (int)blockDim.x; c < nchunk; c += (int)blockDim.x) {
+          const u32x4 sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)c * 16u, 0, kLoadNonTemporal));
+          const u32x4 zv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)c * 16u, 0, kLoadNonTemporal));
+          table_put(c, sv, zv);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_s_barrier();
+      }
 
       // Tile ti of the block; tiles past the round read nothing (an empty
       // buffer range), so every load is unconditional.
-      auto load = [&](int ti, SliceTile<SU, SZW>& r) {
+      auto load = [&](int ti, SliceTile<SU>& r) {
         const bool live = ti < r0 + rn;
         const int64_t col0 = cb + 16 * (int64_t)(live ? ti : r0);
         const int ncols = live ? (ce - col0 < 16 ? (int)(ce - col0) : 16) : 0;
@@ -1041,35 +1079,16 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
         for (int j = 0; j < NJ; ++j)
           r.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rq, ld_unit[j] * 16u, (uint32_t)u0 * 16u, kLoadNonTemporal));
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(sbase + col0 * (int64_t)G * 4), (short)0,
-                                                          ncols * G * 4, kBufferWord3);
-        const auto rz = __builtin_amdgcn_make_buffer_rsrc((void*)(zbase + col0 * (int64_t)G * 4), (short)0,
-                                                          ncols * G * 4, kBufferWord3);
-        const int colc = lo16 < ncols ? lo16 : (ncols > 0 ? ncols - 1 : 0);
-        const uint32_t vs = ((uint32_t)colc * (uint32_t)G + (uint32_t)(h0 + hi4 * SZW)) * 4u;
-        r.s = load_words<SZW>(rs, vs);
-        r.z = load_words<SZW>(rz, vs);
       };
-
-      // Codes to [col][unit][word]; scales and zero points (as fp16
-      // subnormal pairs) to [col][group], groups past the column's last set
-      // to zero: they hold only units past K, whose activations are zero.
-      auto write_stage = [&](const SliceTile<SU, SZW>& r) {
+      // Codes to [col][unit][word].
+      auto write_stage = [&](const SliceTile<SU>& r) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) *reinterpret_cast<u32x4*>(stage + st_off[j]) = r.c[j];
-        uint32_t* zs = stage + 16 * CS + lo16 * SS + hi4 * SZW;
-#pragma unroll
-        for (int c = 0; c < SZW; ++c) {
-          const bool ok = h0 + hi4 * SZW + c < G;
-          const uint32_t zi = (uint32_t)bitsf(r.z.w[c]);
-          zs[c] = ok ? r.s.w[c] : 0u;
-          zs[4 * SZW + c] = ok ? (zi | (zi << 16)) : 0u;
-        }
       };
 
       // All but the last ring slot load now; the last one after the A
       // operand is built, when the activations' registers are free.
-      SliceTile<SU, SZW> ring[DEPTH];
+      SliceTile<SU> ring[DEPTH];
 #pragma unroll
       for (int d = 0; d + 1 < DEPTH; ++d) load(r0 + d, ring[d]);
       __builtin_amdgcn_sched_barrier(0);
@@ -1132,7 +1151,11 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
 
       auto compute = [&](int i) {
         const uint32_t* cs = stage + lo16 * CS + hi4;
-        const uint32_t* zs = stage + 16 * CS + lo16 * SS;
+        // The lane's column in the round (the round's last one past its
+        // end) and the slice's first group.
+        const int colr = 16 * i + lo16 < ncr ? 16 * i + lo16 : ncr - 1;
+        const uint32_t* ts = s_tab + colr * GP + h0;
+        const uint32_t* tz = z_tab + colr * GP + h0;
         uint32_t wd[SU];
 #pragma unroll
         for (int t = 0; t < SU; ++t) wd[t] = cs[4 * t];
@@ -1159,16 +1182,15 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
 #pragma unroll
           for (int t = 0; t < SU; ++t) {
             const int hh = t / GS;
-            dd[hh & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]),
-                                                               unit_b(t, zs[4 * SZW + hh]),
+            dd[hh & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]), unit_b(t, tz[hh]),
                                                                t % GS == 0 ? z4 : dd[hh & 1], 0, 0, 0);
             if (t % GS == GS - 1 && hh > 0) {
-              const float sv = bitsf(zs[hh - 1]);
+              const float sv = bitsf(ts[hh - 1]);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, dd[(hh - 1) & 1][rr], acc[rr]);
             }
           }
-          const float sv = bitsf(zs[NG - 1]);
+          const float sv = bitsf(ts[NG - 1]);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, dd[(NG - 1) & 1][rr], acc[rr]);
         } else {
@@ -1181,10 +1203,10 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
             const bool last = rem == gsu - 1 || t == SU - 1;
             rem = rem + 1 == gsu ? 0 : rem + 1;
             h += rem == 0 ? 1 : 0;
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]), unit_b(t, zs[4 * SZW + hh]),
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, A[t]), unit_b(t, tz[hh]),
                                                        first ? z4 : d, 0, 0, 0);
             if (last) {
-              const float sv = bitsf(zs[hh]);
+              const float sv = bitsf(ts[hh]);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) acc[rr] = fmaf(sv, d[rr], acc[rr]);
             }
