@@ -86,8 +86,13 @@ int int4_quantize_pack(const float* W, int64_t N, int64_t K, int32_t group_size,
  * (M == 0 writes nothing).  The weights are read from memory once per call
  * for all lanes; lanes never interact ([P1] lockstep batch decode: linear
  * layers run the batched INT4 GEMM; [P4] MATVEC_INT4 K-parallel matvec for
- * the single-lane case).  M * K * 4 bytes must fit the device's per-block
- * local data share (160 KiB on gfx950), else INT4_ERR_SHAPE.
+ * the single-lane case).  Limits of the per-block local data share (160 KiB
+ * on gfx950), else INT4_ERR_SHAPE: for M = 1, K * 4 bytes must fit it
+ * (K <= 40960); for M >= 2 it holds the scales and zero points of 16
+ * columns (2 * 16 * (K/gs + at most 25) words) beside about 54 KiB of
+ * staging, which allows K/gs up to about 820.  At M >= 2 every lane's outputs are
+ * bit-identical whatever the other lanes hold; they need not be bit-identical
+ * to the M = 1 call (both are within the tolerance).
  */
 int int4_matvec(const float* X, int32_t M, const uint32_t* q, const float* scales,
                 const float* zeros, int64_t N, int64_t K, int32_t group_size,

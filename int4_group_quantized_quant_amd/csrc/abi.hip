@@ -166,18 +166,17 @@ int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bp
 // Launch geometry.  Both kernels run persistent grids: as many blocks as are
 // resident on the device at once, so no block waits for a second round.
 //
-// Register kernel (M <= 2, K <= 16384): nch = ceil(K/2048) chunks of cw units,
+// Register kernel (M = 1, K <= 16384): nch = ceil(K/2048) chunks of cw units,
 // P = 8/nch rows of nch waves per block (about 8 waves: two per SIMD, which
 // streams best), columns split evenly over the B*P rows, one LDS partial per
 // (column, stream, lane, chunk), the activations staged once per block.
 //
-// Matrix-core kernel (plain, M >= 3): blocks of W <= 8 waves, each wave one
+// Matrix-core kernel (plain, M >= 2): blocks of W <= 8 waves, each wave one
 // slice of 16, 20 or 24 units of K per pass, 8 / W blocks per CU, the
 // block's tiles of 16 columns in rounds that fit the partial table in LDS.
 //
-// LDS kernel (larger K for one or two lanes): 256-thread blocks, the M
-// activation rows staged in LDS (M*K*4 bytes), columns split evenly over the
-// waves.
+// LDS kernel (larger K for one lane): 256-thread blocks, the activation row
+// staged in LDS (K*4 bytes), columns split evenly over the waves.
 int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   DeviceInfo dev;
   RETURN_IF(device_info(&dev));
@@ -186,7 +185,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   const int nstream = mode == kGated ? 2 : 1;
   s->lds_max = dev.lds_block;
   const int rows = mode == kPlain ? M : 1;
-  if (M <= 2 && a.nch <= 8) {
+  if (M == 1 && a.nch <= 8) {
     const int nch = a.nch;
     const int P = nch >= 8 ? 1 : 8 / nch;
     auto table = [&](int64_t blocks) {
@@ -229,7 +228,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // Too little LDS for the partial table and the activations: the LDS
     // kernel needs only the activations.
   }
-  if (mode == kPlain && M >= 3) {
+  if (mode == kPlain && M >= 2) {
     // Matrix-core lanes: slices of SU = 16, 20 or 24 units, at most 8 waves
     // (two per SIMD) per block, P passes of the waves over the slices; one
     // block's columns in rounds of RT tiles whose partials fit the LDS.

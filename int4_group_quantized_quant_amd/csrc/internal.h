@@ -53,7 +53,7 @@ __host__ __device__ inline int x_lds_offset(int part_floats) { return (part_floa
 enum Variant : int {
   kVariantLds = 0,   // activations staged in LDS, one wave per column group
   kVariantReg = 1,   // activations in registers, one wave per (row, K chunk)
-  kVariantSlice = 2, // three to eight lanes on the matrix cores, K sliced over the waves
+  kVariantSlice = 2, // two to eight lanes on the matrix cores, K sliced over the waves
 };
 
 // Matrix-core lanes kernel.  K is cut into slices of SU units (SU = 16, 20

@@ -7,7 +7,7 @@
 // GEMM for decode lanes).  The WGSL kernels give 16 lanes per column with a
 // shared-memory lane sum; the design here is CDNA-native instead.
 //
-// Shared by both matvec kernels:
+// The one-lane kernels (gemv_reg_kernel, gemv_lds_kernel):
 //  * A column's K/32 sixteen-byte code units are spread over the 64 lanes of
 //    a wave, so one buffer_load_dwordx4 of a wave is one contiguous piece of
 //    one column (up to 1 KiB).  Each wave addresses its columns through
@@ -28,7 +28,7 @@
 //    rotations).  Several values are reduced at once by pairing them in the
 //    swap steps; every value still sees exactly the single-value tree.
 //
-// gemv_reg_kernel (one or two lanes, K <= 16384): K is cut into nch chunks
+// gemv_reg_kernel (one lane, K <= 16384; every fused variant): K is cut into nch chunks
 // of at most 64 units.  A block holds P rows of nch waves (about 8 waves);
 // the block stages the activations once in LDS, then wave (p, c) keeps the
 // inputs of chunk c in registers, streams the columns of row p NCOL at a
@@ -37,14 +37,14 @@
 // partials in chunk order and runs the epilogue (routing, SiLU gate, norm
 // scale, plain store).  Blocks are persistent: one per CU.
 //
-// gemv_lds_kernel (three to eight lanes, or longer K): the activation rows
-// are staged in LDS, transposed so lane l reads unit l's inputs with
-// conflict-free ds_read_b128; each wave walks whole columns chunk by chunk
-// (the register kernel's nch chunks of cw units), reducing every chunk
-// across the wave and summing the chunk totals in chunk order -- the
-// register kernel's order, so every lane count gives the same bits.
+// gemv_lds_kernel (one lane, longer K): the activation row is staged in
+// LDS, transposed so lane l reads unit l's inputs with conflict-free
+// ds_read_b128; each wave walks whole columns chunk by chunk (the register
+// kernel's nch chunks of cw units), reducing every chunk across the wave and
+// summing the chunk totals in chunk order -- the register kernel's order.
 //
-// No MFMA: at one to eight lanes the work is a bandwidth-bound stream.
+// gemv_slice_kernel (two to eight lanes): the matrix cores, with K sliced
+// over the waves of a block (described at the kernel).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

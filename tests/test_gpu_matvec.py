@@ -3,8 +3,9 @@
 Ragged shapes (N not a multiple of the column step, K not a multiple of the
 64-unit chunk), every group size the kernels accept, one-hot and
 integer-exact closed forms (bitwise), lane independence (bitwise: against
-the single-lane call for one and two lanes, against calls with every other
-row replaced for the matrix-core lanes), and untouched memory around the
+calls with every other row replaced, for the matrix-core lanes, M >= 2),
+K long enough for several passes over the waves, more columns than one round
+of the LDS table, the table's LDS limit, and untouched memory around the
 outputs."""
 import numpy as np
 import pytest
@@ -72,13 +73,7 @@ def test_lanes(q4, M, N, K, gs):
     Y = run_matvec(q4, X, q, s, z)
     assert Y.shape == (M, N)
     assert_dot_close(Y, Y_ref, B, f"lanes M={M}")
-    if M <= 2:
-        # One and two lanes share the register kernel's per-lane arithmetic:
-        # each lane's bits are the single-lane call's.
-        for m in range(M):
-            y1 = run_matvec(q4, X[m], q, s, z)
-            np.testing.assert_array_equal(Y[m].view(np.uint32), y1.view(np.uint32))
-    else:
+    if M >= 2:
         # Matrix-core lanes never interact: replacing every other row leaves
         # a row's outputs bit-identical.
         for keep in (0, M - 1):
@@ -100,14 +95,25 @@ def check_lanes(q4, X, q, s, z, K, gs, seed):
         np.testing.assert_array_equal(Y2[keep].view(np.uint32), Y[keep].view(np.uint32))
 
 
-@pytest.mark.parametrize("M", [3, 8])
+@pytest.mark.parametrize("M", [2, 3, 8])
 @pytest.mark.parametrize("N,K,gs", [(37, 16416, 32),   # 33 slices of 16 units: three passes of 11
                                     (29, 8256, 96),    # 17 slices, three units per group
                                     (23, 9216, 256),   # 18 slices, eight units per group
-                                    (40, 7168, 1024)]) # every slice inside one group
+                                    (40, 7168, 1024),  # every slice inside one group
+                                    (19, 25600, 32)])  # 800 groups per column: near the LDS table limit
 def test_lanes_long_k(q4, M, N, K, gs):
     q, s, z = quantized(0xB180 + M + K, N, K, gs)
     check_lanes(q4, synth.lanes(0xB181 + K, M, K), q, s, z, K, gs, 0xB182)
+
+
+def test_lanes_table_limit(q4):
+    # 1024 groups per column do not fit the per-block scale/zero table.
+    import torch
+    q, s, z = quantized(0xB190, 4, 32768, 32)
+    _, qd, sd, zd = to_dev(np.zeros(1, np.float32), q.view(np.int32), s, z)
+    X = torch.zeros((2, 32768), dtype=torch.float32, device="cuda")
+    with pytest.raises(q4.Int4Error):
+        q4.int4_matvec(X, qd, sd, zd)
 
 
 def test_lanes_many_rounds(q4):
@@ -144,7 +150,7 @@ def test_one_hot_is_bit_exact(q4, K, gs):
                                           err_msg=f"one-hot k={k}")
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
 @pytest.mark.parametrize("N,K,gs", [(100, 1024, 32), (41, 4160, 64)])
 def test_integer_exact(q4, M, N, K, gs):
     rng = np.random.default_rng(M * 1000 + K)
