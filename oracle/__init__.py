@@ -61,8 +61,16 @@ def _load():
                                  _f64p, _f64p, _f64p, _f64p, _f64p]
     lib.oracle_norm.argtypes = [_f32p, _f32p, _f32p, ctypes.c_float, _u32p, _f32p, _f32p,
                                 _i64, _i64, _i32, _f64p, _f64p, _f32p, _f64p]
+    lib.oracle_dual.argtypes = [_f32p, _u32p, _f32p, _f32p, _u32p, _f32p, _f32p, _i64, _i64, _i32,
+                                _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_input_gated.argtypes = [_i32, _f32p, _f32p, _u32p, _f32p, _f32p, _i64, _i64, _i32,
+                                       _f64p, _f64p, _f64p]
+    lib.oracle_norm_swiglu.argtypes = [_f32p, _f32p, _f32p, ctypes.c_float,
+                                       _u32p, _f32p, _f32p, _u32p, _f32p, _f32p, _i64, _i64, _i32,
+                                       _f64p, _f64p, _f64p, _f64p, _f64p, _f32p]
     for fn in (lib.oracle_quantize_pack, lib.oracle_dequant, lib.oracle_matvec,
-               lib.oracle_matvec_f32, lib.oracle_split4, lib.oracle_gated, lib.oracle_norm):
+               lib.oracle_matvec_f32, lib.oracle_split4, lib.oracle_gated, lib.oracle_norm,
+               lib.oracle_dual, lib.oracle_input_gated, lib.oracle_norm_swiglu):
         fn.restype = None
     _lib = lib
     return lib
@@ -167,6 +175,60 @@ def norm(a_a, a_b, w_norm, eps: float, q, scales, zeros, K: int, group_size: int
                         ctypes.c_float(eps), q, _c(scales, np.float32), _c(zeros, np.float32),
                         N, K, group_size, y, B, residual, normed)
     return {"y": y, "B": B, "residual": residual, "normed": normed}
+
+
+def dual(x, q0, s0, z0, q1, s1, z1, K: int, group_size: int):
+    """Returns dict with y0, b0, y1, b1 (all f64 [N])."""
+    x = _c(x, np.float32)
+    q0 = _c(q0, np.uint32)
+    q1 = _c(q1, np.uint32)
+    N = q0.shape[0]
+    _check_shape(K, group_size)
+    out = {k: np.empty(N, np.float64) for k in ("y0", "b0", "y1", "b1")}
+    _load().oracle_dual(x, q0, _c(s0, np.float32), _c(z0, np.float32),
+                        q1, _c(s1, np.float32), _c(z1, np.float32), N, K, group_size,
+                        out["y0"], out["b0"], out["y1"], out["b1"])
+    return out
+
+
+def _input_gated(kind: int, a, b, q, scales, zeros, K: int, group_size: int):
+    q = _c(q, np.uint32)
+    N = q.shape[0]
+    _check_shape(K, group_size)
+    y = np.empty(N, np.float64)
+    B = np.empty(N, np.float64)
+    xg = np.empty(K, np.float64)
+    _load().oracle_input_gated(kind, _c(a, np.float32), _c(b, np.float32), q,
+                               _c(scales, np.float32), _c(zeros, np.float32),
+                               N, K, group_size, y, B, xg)
+    return {"y": y, "B": B, "xg": xg}
+
+
+def sigmoid_gated(a, gate, q, scales, zeros, K: int, group_size: int):
+    """y = W . (a * sigmoid(gate)); returns dict with y, B (f64 [N]) and xg (f64 [K])."""
+    return _input_gated(0, a, gate, q, scales, zeros, K, group_size)
+
+
+def swiglu_gated(gate, up, q, scales, zeros, K: int, group_size: int):
+    """y = W . (silu(gate) * up); returns dict with y, B (f64 [N]) and xg (f64 [K])."""
+    return _input_gated(1, gate, up, q, scales, zeros, K, group_size)
+
+
+def norm_swiglu(a_a, a_b, w_norm, eps: float, q_gate, s_gate, z_gate, q_up, s_up, z_up,
+                K: int, group_size: int):
+    """Returns dict with h, g, u, bg, bu (f64 [N]) and residual (f32 [K])."""
+    q_gate = _c(q_gate, np.uint32)
+    q_up = _c(q_up, np.uint32)
+    N = q_gate.shape[0]
+    _check_shape(K, group_size)
+    out = {k: np.empty(N, np.float64) for k in ("h", "g", "u", "bg", "bu")}
+    out["residual"] = np.empty(K, np.float32)
+    _load().oracle_norm_swiglu(_c(a_a, np.float32), _c(a_b, np.float32), _c(w_norm, np.float32),
+                               ctypes.c_float(eps), q_gate, _c(s_gate, np.float32),
+                               _c(z_gate, np.float32), q_up, _c(s_up, np.float32),
+                               _c(z_up, np.float32), N, K, group_size,
+                               out["h"], out["g"], out["u"], out["bg"], out["bu"], out["residual"])
+    return out
 
 
 def tolerance(B):

@@ -250,3 +250,77 @@ void oracle_norm(const float* a_a, const float* a_b, const float* w_norm, float 
         B[n] = mag;
     }
 }
+
+/* ------------------------------------------------------ next-row variants */
+
+/*
+ * Dual matvec ([P4] fuseDualMatVecDecodeEntries / DualMatVecInt4, and the
+ * [P1] batch port fuseBatchDualMatVecEntries): two matrices with the same N,
+ * K and group size read one shared input; each output is the plain matvec of
+ * its own matrix, nothing else changes.
+ */
+void oracle_dual(const float* x,
+                 const uint32_t* q0, const float* s0, const float* z0,
+                 const uint32_t* q1, const float* s1, const float* z1,
+                 int64_t N, int64_t K, int32_t gs,
+                 double* y0, double* b0, double* y1, double* b1) {
+    oracle_matvec(x, 1, q0, s0, z0, N, K, gs, y0, b0);
+    oracle_matvec(x, 1, q1, s1, z1, N, K, gs, y1, b1);
+}
+
+/*
+ * Input-gated matvec: the elementwise gate is applied to the input vector,
+ * then the plain matvec runs on the gated vector.
+ *   kind 0 ([P4] fuseGatedOProjDecodeEntries, GatedMatVecInt4 fed by the
+ *          attention SigmoidGate):  xg[k] = a[k] * sigma(b[k]),
+ *          sigma(t) = 1 / (1 + exp(-t))
+ *   kind 1 ([P4] fuseSwiGLUGatedProjDecodeEntries, SwiGLUGatedMatVecInt4):
+ *          xg[k] = silu(a[k]) * b[k],  silu(t) = t / (1 + exp(-t))
+ * The gate is evaluated in fp64 from the binary32 inputs; y[n] = sum_k
+ * xg[k] * dq[n][k] and B[n] = sum_k |xg[k] * dq[n][k]| (fp64, k ascending).
+ */
+void oracle_input_gated(int32_t kind, const float* a, const float* b,
+                        const uint32_t* q, const float* scales, const float* zeros,
+                        int64_t N, int64_t K, int32_t gs,
+                        double* y, double* B, double* xg) {
+    for (int64_t k = 0; k < K; ++k) {
+        double ak = (double)a[k], bk = (double)b[k];
+        if (kind == 0)
+            xg[k] = ak * (1.0 / (1.0 + exp(-bk)));
+        else
+            xg[k] = (ak / (1.0 + exp(-ak))) * bk;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = xg[k] * (double)dq_at(q, scales, zeros, K, gs, n, k);
+            acc += p;
+            mag += fabs(p);
+        }
+        y[n] = acc;
+        B[n] = mag;
+    }
+}
+
+/*
+ * RMSNorm-prefixed SwiGLU front ([P4] fuseNormSwiGLUDecodeEntries /
+ * NormSwiGLUMatVec): the residual-add + RMSNorm prologue of oracle_norm,
+ * then the gate and up matvecs of the normalized vector and
+ * h[n] = silu(g[n]) * u[n] as in oracle_gated.  residual = a_a + a_b in
+ * binary32 (the one side output the pages keep).
+ */
+void oracle_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm, float eps,
+                        const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                        const uint32_t* q_up, const float* s_up, const float* z_up,
+                        int64_t N, int64_t K, int32_t gs,
+                        double* h, double* g, double* u, double* bg, double* bu,
+                        float* residual) {
+    double* normed = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    oracle_norm(a_a, a_b, w_norm, eps, q_gate, s_gate, z_gate, N, K, gs, g, bg, residual, normed);
+    oracle_norm(a_a, a_b, w_norm, eps, q_up, s_up, z_up, N, K, gs, u, bu, residual, normed);
+    for (int64_t n = 0; n < N; ++n) {
+        double silu = g[n] / (1.0 + exp(-g[n]));
+        h[n] = silu * u[n];
+    }
+    free(normed);
+}

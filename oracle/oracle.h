@@ -33,6 +33,21 @@ void oracle_norm(const float* a_a, const float* a_b, const float* w_norm, float 
                  const uint32_t* q, const float* scales, const float* zeros,
                  int64_t N, int64_t K, int32_t gs,
                  double* y, double* B, float* residual, double* normed);
+void oracle_dual(const float* x,
+                 const uint32_t* q0, const float* s0, const float* z0,
+                 const uint32_t* q1, const float* s1, const float* z1,
+                 int64_t N, int64_t K, int32_t gs,
+                 double* y0, double* b0, double* y1, double* b1);
+void oracle_input_gated(int32_t kind, const float* a, const float* b,
+                        const uint32_t* q, const float* scales, const float* zeros,
+                        int64_t N, int64_t K, int32_t gs,
+                        double* y, double* B, double* xg);
+void oracle_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm, float eps,
+                        const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                        const uint32_t* q_up, const float* s_up, const float* z_up,
+                        int64_t N, int64_t K, int32_t gs,
+                        double* h, double* g, double* u, double* bg, double* bu,
+                        float* residual);
 
 #ifdef __cplusplus
 }
