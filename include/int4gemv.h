@@ -31,7 +31,7 @@
  *     the caller's next synchronization.
  *   - Shapes: K >= gs, K % gs == 0, gs % 32 == 0 (a 32-code, 16-byte load
  *     never straddles a group).  N >= 0; N == 0 writes nothing (see norm).
- *   - Alignment: q, X (and a_a, a_b, w_norm, W) must be 16-byte aligned;
+ *   - Alignment: q, X (and every other input vector, and W) must be 16-byte aligned;
  *     scales, zeros and outputs 4-byte aligned.
  *   - Outputs must not overlap any input or each other ([P4]
  *     fuseNormMatVecDecodeEntries / fuseMambaFrontDecodeEntries alias rules).
@@ -146,6 +146,70 @@ int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, fl
                      const uint32_t* q, const float* scales, const float* zeros,
                      int64_t N, int64_t K, int32_t group_size,
                      float* y, float* residual_out, float* norm_out, void* stream);
+
+/*
+ * Dual matvec: two projections that share one input vector and the same N,
+ * K and gs, in one call that reads the input once ([P4]
+ * fuseDualMatVecDecodeEntries, DualMatVecInt4: q_proj + gate_proj or
+ * k_proj + v_proj of full-attention decode; [P1] fuseBatchDualMatVecEntries):
+ *   y0[n] = x . w0[n],  y1[n] = x . w1[n].
+ * Each output is bit-identical to int4_matvec (M = 1) of its own matrix.
+ * Same local-data-share limit as int4_matvec at M = 1.
+ */
+int int4_matvec_dual(const float* x,
+                     const uint32_t* q0, const float* s0, const float* z0,
+                     const uint32_t* q1, const float* s1, const float* z1,
+                     int64_t N, int64_t K, int32_t group_size,
+                     float* y0, float* y1, void* stream);
+
+/*
+ * Sigmoid-gated input matvec ([P4] fuseGatedOProjDecodeEntries: the
+ * attention SigmoidGate, attn_out * sigmoid(gate), recomputed inside the
+ * o_proj matvec's input load, GatedMatVecInt4; [P1]
+ * fuseBatchGatedProjEntries "sigmoid"):
+ *   xg[k] = a[k] * sigmoid(gate[k]),  sigmoid(t) = 1 / (1 + exp(-t)),
+ *   y[n]  = xg . w[n].
+ * The gate is evaluated in binary32 (with exp(-|t|), so it never
+ * overflows); y is within the dot-product tolerance of the fp64 definition.
+ * a and gate must be 16-byte aligned; K * 4 bytes must fit the per-block
+ * local data share.
+ */
+int int4_matvec_sigmoid_gated(const float* a, const float* gate,
+                              const uint32_t* q, const float* scales, const float* zeros,
+                              int64_t N, int64_t K, int32_t group_size,
+                              float* y, void* stream);
+
+/*
+ * SwiGLU-gated input matvec ([P4] fuseSwiGLUGatedProjDecodeEntries: a
+ * standalone SwiGLU feeding an int4 projection, e.g. the linear-attention
+ * block's silu(z) * norm_out into out_proj, SwiGLUGatedMatVecInt4; [P1]
+ * fuseBatchGatedProjEntries "swiglu"):
+ *   xg[k] = silu(gate[k]) * up[k],  silu(t) = t / (1 + exp(-t)),
+ *   y[n]  = xg . w[n].
+ * Evaluation, alignment and limits as int4_matvec_sigmoid_gated.
+ */
+int int4_matvec_swiglu_gated(const float* gate, const float* up,
+                             const uint32_t* q, const float* scales, const float* zeros,
+                             int64_t N, int64_t K, int32_t group_size,
+                             float* y, void* stream);
+
+/*
+ * RMSNorm-prefixed SwiGLU front of a decode MLP in one call ([P4]
+ * fuseNormSwiGLUDecodeEntries, NormSwiGLUMatVec: ResidualRMSNorm + gate
+ * matvec + up matvec + SwiGLU; block 0 keeps the residual sum for the
+ * residual chain):
+ *   r, inv, x as int4_matvec_norm;  g[n] = x . w_gate[n],  u[n] = x . w_up[n],
+ *   h[n] = silu(g[n]) * u[n].
+ * g and u are bit-identical to int4_matvec_norm's y for each matrix;
+ * residual_out (r, exact in binary32) is optional (NULL = not written).
+ * eps must be finite and >= 0.  N == 0 still writes residual_out when given.
+ * K * 4 bytes must fit the per-block local data share.
+ */
+int int4_matvec_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm, float eps,
+                            const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                            const uint32_t* q_up, const float* s_up, const float* z_up,
+                            int64_t N, int64_t K, int32_t group_size,
+                            float* h, float* residual_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "Int4Error", "int4_quantize_pack", "int4_matvec", "int4_matvec_split4",
-    "int4_matvec_gated", "int4_matvec_norm", "lib", "LIB_PATH",
+    "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
+    "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "lib", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -46,8 +47,15 @@ lib.int4_matvec_split4.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _
 lib.int4_matvec_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 lib.int4_matvec_norm.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i64, _i64, _i32,
                                  _vp, _vp, _vp, _vp]
+lib.int4_matvec_dual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]
+lib.int4_matvec_sigmoid_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_norm_swiglu.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _i64, _i64, _i32, _vp, _vp, _vp]
 for _fn in (lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
-            lib.int4_matvec_gated, lib.int4_matvec_norm):
+            lib.int4_matvec_gated, lib.int4_matvec_norm, lib.int4_matvec_dual,
+            lib.int4_matvec_sigmoid_gated, lib.int4_matvec_swiglu_gated,
+            lib.int4_matvec_norm_swiglu):
     _fn.restype = ctypes.c_int
 
 
@@ -195,3 +203,70 @@ def int4_matvec_norm(a_a: torch.Tensor, a_b: torch.Tensor, w_norm: torch.Tensor,
                                 _ptr(y) if N else None, _ptr(residual_out), _ptr(norm_out),
                                 _stream(stream)))
     return y, residual_out, norm_out
+
+
+def _pair(q0, s0, z0, q1, s1, z1, t0, t1):
+    N, K, gs = _weights(q0, s0, z0, t0)
+    if _weights(q1, s1, z1, t1) != (N, K, gs):
+        raise ValueError(f"the{t0.replace('_', ' ')} and{t1.replace('_', ' ')} weights must share N, K and group size")
+    return N, K, gs
+
+
+def int4_matvec_dual(x: torch.Tensor, q0, s0, z0, q1, s1, z1, y0=None, y1=None, stream=None):
+    """(y0, y1) = (x . w0[n], x . w1[n]): two projections of one input in one call."""
+    N, K, gs = _pair(q0, s0, z0, q1, s1, z1, "0", "1")
+    _dev(x, "x", _F32)
+    y0 = torch.empty(N, dtype=torch.float32, device=x.device) if y0 is None else y0
+    y1 = torch.empty(N, dtype=torch.float32, device=x.device) if y1 is None else y1
+    _dev(y0, "y0", _F32)
+    _dev(y1, "y1", _F32)
+    _check(lib.int4_matvec_dual(_ptr(x), _ptr(q0), _ptr(s0), _ptr(z0), _ptr(q1), _ptr(s1),
+                                _ptr(z1), N, K, gs, _ptr(y0), _ptr(y1), _stream(stream)))
+    return y0, y1
+
+
+def int4_matvec_sigmoid_gated(a: torch.Tensor, gate: torch.Tensor, q, scales, zeros, y=None,
+                              stream=None) -> torch.Tensor:
+    """y[n] = (a * sigmoid(gate)) . w[n]."""
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(a, "a", _F32)
+    _dev(gate, "gate", _F32)
+    y = torch.empty(N, dtype=torch.float32, device=a.device) if y is None else y
+    _dev(y, "y", _F32)
+    _check(lib.int4_matvec_sigmoid_gated(_ptr(a), _ptr(gate), _ptr(q), _ptr(scales), _ptr(zeros),
+                                         N, K, gs, _ptr(y), _stream(stream)))
+    return y
+
+
+def int4_matvec_swiglu_gated(gate: torch.Tensor, up: torch.Tensor, q, scales, zeros, y=None,
+                             stream=None) -> torch.Tensor:
+    """y[n] = (silu(gate) * up) . w[n]."""
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(gate, "gate", _F32)
+    _dev(up, "up", _F32)
+    y = torch.empty(N, dtype=torch.float32, device=gate.device) if y is None else y
+    _dev(y, "y", _F32)
+    _check(lib.int4_matvec_swiglu_gated(_ptr(gate), _ptr(up), _ptr(q), _ptr(scales), _ptr(zeros),
+                                        N, K, gs, _ptr(y), _stream(stream)))
+    return y
+
+
+def int4_matvec_norm_swiglu(a_a: torch.Tensor, a_b: torch.Tensor, w_norm: torch.Tensor,
+                            eps: float, q_gate, s_gate, z_gate, q_up, s_up, z_up, h=None,
+                            residual_out=None, want_residual: bool = True, stream=None):
+    """h = silu(x . w_gate) * (x . w_up), x = RMSNorm(a_a + a_b) * w_norm -> (h, residual_out or None)."""
+    N, K, gs = _pair(q_gate, s_gate, z_gate, q_up, s_up, z_up, "_gate", "_up")
+    for t, name in ((a_a, "a_a"), (a_b, "a_b"), (w_norm, "w_norm")):
+        _dev(t, name, _F32)
+    dev = a_a.device
+    h = torch.empty(N, dtype=torch.float32, device=dev) if h is None else h
+    if residual_out is None and want_residual:
+        residual_out = torch.empty(K, dtype=torch.float32, device=dev)
+    for t, name in ((h, "h"), (residual_out, "residual_out")):
+        if t is not None:
+            _dev(t, name, _F32)
+    _check(lib.int4_matvec_norm_swiglu(_ptr(a_a), _ptr(a_b), _ptr(w_norm), float(eps),
+                                       _ptr(q_gate), _ptr(s_gate), _ptr(z_gate), _ptr(q_up),
+                                       _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(h) if N else None,
+                                       _ptr(residual_out), _stream(stream)))
+    return h, residual_out

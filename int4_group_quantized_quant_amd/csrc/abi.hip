@@ -182,7 +182,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   RETURN_IF(device_info(&dev));
   const int M = a.M;
   const int64_t N = a.N;
-  const int nstream = mode == kGated ? 2 : 1;
+  const int nstream = mode_streams(mode);
   s->lds_max = dev.lds_block;
   const int rows = mode == kPlain ? M : 1;
   if (M == 1 && a.nch <= 8) {
@@ -268,7 +268,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     a.total_waves = B * W;
     return INT4_OK;
   }
-  const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode == kNorm ? 64 : 0);
+  const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode_has_norm(mode) ? 64 : 0);
   if (lds > dev.lds_block)
     return fail(INT4_ERR_SHAPE, "activations need %zu bytes of LDS per block; the device allows %zu",
                 lds, dev.lds_block);
@@ -502,6 +502,140 @@ int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, fl
   a.residual_out = residual_out;
   a.norm_out = norm_out;
   return run(kNorm, a, stream);
+}
+
+int int4_matvec_dual(const float* x, const uint32_t* q0, const float* s0, const float* z0,
+                     const uint32_t* q1, const float* s1, const float* z1, int64_t N, int64_t K,
+                     int32_t group_size, float* y0, float* y1, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0) return ok();
+  if (!x || !q0 || !s0 || !z0 || !q1 || !s1 || !z1 || !y0 || !y1)
+    return fail(INT4_ERR_NULL, "x, both weight triplets, y0 and y1 are required");
+  RETURN_IF(check_align(x, 16, "x"));
+  RETURN_IF(check_align(q0, 16, "q0"));
+  RETURN_IF(check_align(q1, 16, "q1"));
+  RETURN_IF(check_align(s0, 4, "s0"));
+  RETURN_IF(check_align(z0, 4, "z0"));
+  RETURN_IF(check_align(s1, 4, "s1"));
+  RETURN_IF(check_align(z1, 4, "z1"));
+  RETURN_IF(check_align(y0, 4, "y0"));
+  RETURN_IF(check_align(y1, 4, "y1"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{x, (uint64_t)K * 4, "x"},
+                      {q0, (uint64_t)N * K / 2, "q0"}, {s0, G * 4, "s0"}, {z0, G * 4, "z0"},
+                      {q1, (uint64_t)N * K / 2, "q1"}, {s1, G * 4, "s1"}, {z1, G * 4, "z1"}};
+  const Span outs[] = {{y0, (uint64_t)N * 4, "y0"}, {y1, (uint64_t)N * 4, "y1"}};
+  RETURN_IF(check_alias(ins, 7, outs, 2));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = x;
+  a.M = 1;
+  a.q[0] = reinterpret_cast<const uint4*>(q0);
+  a.s[0] = s0;
+  a.z[0] = z0;
+  a.q[1] = reinterpret_cast<const uint4*>(q1);
+  a.s[1] = s1;
+  a.z[1] = z1;
+  a.out[0] = y0;
+  a.out[1] = y1;
+  return run(kDual, a, stream);
+}
+
+// Shared by the two input-gated entry points: p and r are the two input
+// vectors (a and gate, or gate and up).
+static int input_gated(Mode mode, const float* p, const float* r, const char* pn, const char* rn,
+                const uint32_t* q, const float* scales, const float* zeros, int64_t N, int64_t K,
+                int32_t group_size, float* y, void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0) return ok();
+  if (!p || !r || !q || !scales || !zeros || !y)
+    return fail(INT4_ERR_NULL, "%s, %s, q, scales, zeros and y are required", pn, rn);
+  RETURN_IF(check_align(p, 16, pn));
+  RETURN_IF(check_align(r, 16, rn));
+  RETURN_IF(check_align(q, 16, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(y, 4, "y"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{p, (uint64_t)K * 4, pn}, {r, (uint64_t)K * 4, rn},
+                      {q, (uint64_t)N * K / 2, "q"}, {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{y, (uint64_t)N * 4, "y"}};
+  RETURN_IF(check_alias(ins, 5, outs, 1));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = p;
+  a.x2 = r;
+  a.M = 1;
+  a.q[0] = reinterpret_cast<const uint4*>(q);
+  a.s[0] = scales;
+  a.z[0] = zeros;
+  a.out[0] = y;
+  return run(mode, a, stream);
+}
+
+int int4_matvec_sigmoid_gated(const float* a_in, const float* gate, const uint32_t* q,
+                              const float* scales, const float* zeros, int64_t N, int64_t K,
+                              int32_t group_size, float* y, void* stream) {
+  return input_gated(kSigIn, a_in, gate, "a", "gate", q, scales, zeros, N, K, group_size, y, stream);
+}
+
+int int4_matvec_swiglu_gated(const float* gate, const float* up, const uint32_t* q,
+                             const float* scales, const float* zeros, int64_t N, int64_t K,
+                             int32_t group_size, float* y, void* stream) {
+  return input_gated(kSwiIn, gate, up, "gate", "up", q, scales, zeros, N, K, group_size, y, stream);
+}
+
+int int4_matvec_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm, float eps,
+                            const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                            const uint32_t* q_up, const float* s_up, const float* z_up, int64_t N,
+                            int64_t K, int32_t group_size, float* h, float* residual_out,
+                            void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  RETURN_IF(check_kgs(K, group_size));
+  if (!(isfinite(eps) && eps >= 0.0f)) return fail(INT4_ERR_ARG, "eps must be finite and >= 0");
+  if (N == 0 && !residual_out) return ok();
+  if (!a_a || !a_b || !w_norm) return fail(INT4_ERR_NULL, "a_a, a_b and w_norm are required");
+  if (N > 0 && (!q_gate || !s_gate || !z_gate || !q_up || !s_up || !z_up || !h))
+    return fail(INT4_ERR_NULL, "both weight triplets and h are required when N > 0");
+  RETURN_IF(check_align(a_a, 16, "a_a"));
+  RETURN_IF(check_align(a_b, 16, "a_b"));
+  RETURN_IF(check_align(w_norm, 16, "w_norm"));
+  RETURN_IF(check_align(q_gate, 16, "q_gate"));
+  RETURN_IF(check_align(q_up, 16, "q_up"));
+  RETURN_IF(check_align(s_gate, 4, "s_gate"));
+  RETURN_IF(check_align(z_gate, 4, "z_gate"));
+  RETURN_IF(check_align(s_up, 4, "s_up"));
+  RETURN_IF(check_align(z_up, 4, "z_up"));
+  RETURN_IF(check_align(h, 4, "h"));
+  RETURN_IF(check_align(residual_out, 16, "residual_out"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{a_a, (uint64_t)K * 4, "a_a"}, {a_b, (uint64_t)K * 4, "a_b"},
+                      {w_norm, (uint64_t)K * 4, "w_norm"},
+                      {q_gate, (uint64_t)N * K / 2, "q_gate"}, {s_gate, G * 4, "s_gate"},
+                      {z_gate, G * 4, "z_gate"},
+                      {q_up, (uint64_t)N * K / 2, "q_up"}, {s_up, G * 4, "s_up"}, {z_up, G * 4, "z_up"}};
+  const Span outs[] = {{h, (uint64_t)N * 4, "h"},
+                       {residual_out, residual_out ? (uint64_t)K * 4 : 0, "residual_out"}};
+  RETURN_IF(check_alias(ins, 9, outs, 2));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = a_a;
+  a.x2 = a_b;
+  a.w_norm = w_norm;
+  a.eps = eps;
+  a.M = 1;
+  a.q[0] = reinterpret_cast<const uint4*>(q_gate);
+  a.s[0] = s_gate;
+  a.z[0] = z_gate;
+  a.q[1] = reinterpret_cast<const uint4*>(q_up);
+  a.s[1] = s_up;
+  a.z[1] = z_up;
+  a.out[0] = h;
+  a.residual_out = residual_out;
+  a.norm_out = nullptr;
+  return run(kNormSwi, a, stream);
 }
 
 }  // extern "C"

@@ -9,25 +9,39 @@ namespace int4gemv {
 
 // Epilogue / prologue variant of the streaming matvec kernel.
 enum Mode : int {
-  kPlain = 0,   // Y[m][n] for M lanes
-  kSplit4 = 1,  // one lane, columns routed into four buffers
-  kGated = 2,   // one lane, two weight streams, h = silu(g) * u
-  kNorm = 3,    // one lane, residual-add + RMSNorm prologue
+  kPlain = 0,    // Y[m][n] for M lanes
+  kSplit4 = 1,   // one lane, columns routed into four buffers
+  kGated = 2,    // one lane, two weight streams, h = silu(g) * u
+  kNorm = 3,     // one lane, residual-add + RMSNorm prologue
+  kDual = 4,     // one lane, two weight streams, y0 = g and y1 = u
+  kSigIn = 5,    // one lane, input x = a * sigmoid(gate)
+  kSwiIn = 6,    // one lane, input x = silu(gate) * up
+  kNormSwi = 7,  // one lane, RMSNorm prologue, two streams, h = silu(g) * u
 };
+
+// Weight streams a mode reads (gate/up or the two projections of a pair).
+__host__ __device__ constexpr int mode_streams(int mode) {
+  return mode == kGated || mode == kDual || mode == kNormSwi ? 2 : 1;
+}
+// Modes whose input is the residual-add + RMSNorm of (a_a, a_b, w_norm).
+__host__ __device__ constexpr bool mode_has_norm(int mode) { return mode == kNorm || mode == kNormSwi; }
+// Modes whose input is an elementwise gate of two vectors (x, x2).
+__host__ __device__ constexpr bool mode_gates_input(int mode) { return mode == kSigIn || mode == kSwiIn; }
 
 // Everything a matvec launch needs; passed by value as the kernel argument.
 struct GemvArgs {
-  const float* x;       // kPlain/kSplit4/kGated: X [M][K]; kNorm: a_a [K]
-  const float* x2;      // kNorm: a_b [K]
-  const float* w_norm;  // kNorm: RMSNorm gain [K]
-  float eps;            // kNorm
+  const float* x;       // X [M][K]; norm modes: a_a [K]; kSigIn: a [K]; kSwiIn: gate [K]
+  const float* x2;      // norm modes: a_b [K]; kSigIn: gate [K]; kSwiIn: up [K]
+  const float* w_norm;  // norm modes: RMSNorm gain [K]
+  float eps;            // norm modes
   const uint4* q[2];    // packed codes per weight stream, 16-byte units [N][K/32]
   const float* s[2];    // scales per stream [N][K/gs]
   const float* z[2];    // zero points per stream [N][K/gs]
   float* out[4];        // kPlain: out[0] = Y [M][N]; kSplit4: four routed buffers;
-                        // kGated: out[0] = h; kNorm: out[0] = y
-  float* residual_out;  // kNorm, nullable
-  float* norm_out;      // kNorm, nullable
+                        // kGated, kNormSwi: out[0] = h; kDual: out[0] = y0, out[1] = y1;
+                        // kNorm, kSigIn, kSwiIn: out[0] = y
+  float* residual_out;  // norm modes, nullable
+  float* norm_out;      // kNorm, nullable (null for kNormSwi)
   int64_t N;            // output columns
   int64_t n0, n1, n2;   // kSplit4 split points
   int64_t total_waves;  // waves in the grid; wave w owns columns [w*N/W, (w+1)*N/W)

@@ -360,12 +360,43 @@ __device__ __forceinline__ void write_norm_outputs(const GemvArgs& a, float inv)
   }
 }
 
+// ------------------------------------------------------------ elementwise gates
+
+// sigmoid(t) = 1 / (1 + e^-t) and silu(t) = t * sigmoid(t) in binary32, with
+// e = e^-|t| so that the exponential never overflows: for negative t,
+// sigmoid(t) = e / (1 + e).  ([P1] SwiGLU: silu(gate) * up; [P4] SigmoidGate
+// feeding GatedMatVecInt4: attn_out * sigmoid(gate).)
+__device__ __forceinline__ float sigmoid_f32(float t) {
+  const float e = expf(-fabsf(t));
+  return t >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+}
+__device__ __forceinline__ float silu_f32(float t) {
+  const float e = expf(-fabsf(t));
+  return t >= 0.0f ? t / (1.0f + e) : (t * e) / (1.0f + e);
+}
+
+// Gated input of float4 i ([P4] GatedMatVecInt4 / SwiGLUGatedMatVecInt4:
+// the elementwise gate is rebuilt inside the matvec's input load):
+// kSigIn x = a * sigmoid(gate), kSwiIn x = silu(gate) * up.
+template <int MODE>
+__device__ __forceinline__ float4 gated_in4(const GemvArgs& a, int i) {
+  const float4 p = reinterpret_cast<const float4*>(a.x)[i];
+  const float4 r = reinterpret_cast<const float4*>(a.x2)[i];
+  if constexpr (MODE == kSigIn)
+    return make_float4(p.x * sigmoid_f32(r.x), p.y * sigmoid_f32(r.y), p.z * sigmoid_f32(r.z),
+                       p.w * sigmoid_f32(r.w));
+  else
+    return make_float4(silu_f32(p.x) * r.x, silu_f32(p.y) * r.y, silu_f32(p.z) * r.z,
+                       silu_f32(p.w) * r.w);
+}
+
 // Column epilogue shared by both kernels: `tot[st][m]` are the finished sums
-// of column `col` (stream st: 0 = the weights / gate, 1 = up).
-// `inv` is inv_rms for kNorm and unused otherwise.
+// of column `col` (stream st: 0 = the weights / gate / first projection,
+// 1 = up / second projection).  `inv` is inv_rms for the norm modes and
+// unused otherwise.
 template <int M, int MODE>
 __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
-                                             const float (&tot)[MODE == kGated ? 2 : 1][M],
+                                             const float (&tot)[mode_streams(MODE)][M],
                                              float inv) {
   if constexpr (MODE == kPlain) {
 #pragma unroll
@@ -378,14 +409,18 @@ __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
     else if (col < a.n1) a.out[1][col - a.n0] = v;
     else if (col < a.n2) a.out[2][col - a.n1] = v;
     else a.out[3][col - a.n2] = v;
+  } else if constexpr (MODE == kDual) {
+    a.out[0][col] = tot[0][0];
+    a.out[1][col] = tot[1][0];
+  } else if constexpr (MODE == kSigIn || MODE == kSwiIn) {
+    a.out[0][col] = tot[0][0];
+  } else if constexpr (MODE == kNormSwi) {
+    // g and u are the int4_matvec_norm values of the two streams.
+    const float g = tot[0][0] * inv;
+    const float u = tot[1][0] * inv;
+    a.out[0][col] = silu_f32(g) * u;
   } else {
-    // silu(g) = g / (1 + e^-g), evaluated as g e / (1 + e) with e = e^g for
-    // negative g so that e^-g never overflows ([P1] SwiGLU: silu(gate) * up).
-    const float g = tot[0][0];
-    const float u = tot[1][0];
-    const float e = expf(-fabsf(g));
-    const float silu = g >= 0.0f ? g / (1.0f + e) : (g * e) / (1.0f + e);
-    a.out[0][col] = silu * u;
+    a.out[0][col] = silu_f32(tot[0][0]) * tot[1][0];
   }
 }
 
@@ -394,7 +429,7 @@ __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
 
 template <int M, int NCOL, int MODE, int DEPTH>
 __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
-  constexpr int NSTREAM = MODE == kGated ? 2 : 1;
+  constexpr int NSTREAM = mode_streams(MODE);
   constexpr int NSLOT = NCOL * NSTREAM;
   constexpr int V = M * NSLOT;
   constexpr int NZ = (V + 3) / 4;
@@ -421,11 +456,12 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   float* scratch = part + a.part_floats;
 
   // Activations: the block stages the M rows once in LDS (coalesced; for
-  // the norm, x = (a_a + a_b) * w_norm and block 0 writes residual_out),
-  // then each lane keeps its unit's 32 inputs in registers for the sweep.
+  // the norm, x = (a_a + a_b) * w_norm and block 0 writes residual_out; for
+  // a gated input, the gated vector), then each lane keeps its unit's 32
+  // inputs in registers for the sweep.
   float4* xl = reinterpret_cast<float4*>(part + x_lds_offset(a.part_floats));
   const int n4 = a.K >> 2;
-  if constexpr (MODE == kNorm) {
+  if constexpr (mode_has_norm(MODE)) {
     // Per-thread share of sum_k r_k^2, then the wave's total in its slot.
     float ssq = 0.0f;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) {
@@ -440,6 +476,8 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
     }
     const float wsum = wave_sum(ssq);
     if (lane == 0) scratch[wave] = wsum;
+  } else if constexpr (mode_gates_input(MODE)) {
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(i & 7) * a.U + (i >> 3)] = gated_in4<MODE>(a, i);
   } else {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -531,7 +569,7 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   // from the wave totals in wave order: the same value in every block.
   // Block 0 writes norm_out = x * inv_rms from the staged x.
   float inv = 1.0f;
-  if constexpr (MODE == kNorm) {
+  if constexpr (mode_has_norm(MODE)) {
     float ss = scratch[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) ss += scratch[w];
     inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
@@ -576,12 +614,12 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ X, int K, int 
 
 template <int M, int NCOL, int MODE>
 __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
-  constexpr int NSTREAM = MODE == kGated ? 2 : 1;
+  constexpr int NSTREAM = mode_streams(MODE);
   constexpr int NSLOT = NCOL * NSTREAM;
   extern __shared__ float4 xl[];
-  float inv = 1.0f;  // inv_rms (kNorm)
+  float inv = 1.0f;  // inv_rms (norm modes)
 
-  if constexpr (MODE == kNorm) {
+  if constexpr (mode_has_norm(MODE)) {
     float* scratch = reinterpret_cast<float*>(xl + (size_t)8 * a.U);
     inv = block_inv_rms(a, scratch);
     for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
@@ -590,6 +628,9 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
       xl[(i & 7) * a.U + (i >> 3)] = prescale4(v);
     }
     write_norm_outputs(a, inv);
+  } else if constexpr (mode_gates_input(MODE)) {
+    for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x)
+      xl[(i & 7) * a.U + (i >> 3)] = prescale4(gated_in4<MODE>(a, i));
   } else {
     stage_x<M>(a.x, a.K, a.U, xl);
   }
@@ -1299,7 +1340,7 @@ hipError_t launch_lds(const GemvArgs& a, const LaunchShape& s, hipStream_t strea
 
 template <int MODE>
 hipError_t dispatch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
-  if constexpr (MODE == kGated) {
+  if constexpr (mode_streams(MODE) == 2) {
     return s.ncol == 1 ? launch_reg<MODE, 1, 1>(a, s, st, occ) : launch_reg<MODE, 1, 2>(a, s, st, occ);
   } else if constexpr (MODE == kPlain) {
     if (a.M == 2)
@@ -1347,6 +1388,10 @@ hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStrea
       case kSplit4: return dispatch_reg<kSplit4>(a, s, st, occ);
       case kGated: return dispatch_reg<kGated>(a, s, st, occ);
       case kNorm: return dispatch_reg<kNorm>(a, s, st, occ);
+      case kDual: return dispatch_reg<kDual>(a, s, st, occ);
+      case kSigIn: return dispatch_reg<kSigIn>(a, s, st, occ);
+      case kSwiIn: return dispatch_reg<kSwiIn>(a, s, st, occ);
+      case kNormSwi: return dispatch_reg<kNormSwi>(a, s, st, occ);
       default: return dispatch_reg<kPlain>(a, s, st, occ);
     }
   }
@@ -1354,6 +1399,10 @@ hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStrea
     case kSplit4: return launch_lds<kSplit4, 1, 1>(a, s, st, occ);
     case kGated: return launch_lds<kGated, 1, 1>(a, s, st, occ);
     case kNorm: return launch_lds<kNorm, 1, 1>(a, s, st, occ);
+    case kDual: return launch_lds<kDual, 1, 1>(a, s, st, occ);
+    case kSigIn: return launch_lds<kSigIn, 1, 1>(a, s, st, occ);
+    case kSwiIn: return launch_lds<kSwiIn, 1, 1>(a, s, st, occ);
+    case kNormSwi: return launch_lds<kNormSwi, 1, 1>(a, s, st, occ);
     default: break;
   }
   switch (a.M) {
@@ -1372,7 +1421,7 @@ hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStrea
 
 int max_ncol(Mode mode, int M, int variant) {
   if (variant == kVariantReg) {
-    if (mode == kGated) return 2;
+    if (mode_streams(mode) == 2) return 2;
     return M == 1 ? 4 : 2;
   }
   return mode == kPlain ? 2 : 1;

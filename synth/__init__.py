@@ -25,6 +25,14 @@ family the pages serve; no dataset is involved):
     c5  decode lanes    X[M, 5120] (row m = counter offset m*K), M in {1,2,4,8},
                         W[25600, 5120]    gs 64, 1% of groups with one x20 outlier
                                                    seeds 0x501/0x502/0x503
+Next-row workloads (fused decode variants around the hot path, same recipe):
+    n1  dual q + gate   x[4096]           W0,W1[4096, 4096] gs 128 seeds 0x601..0x603
+    n2  sigmoid-gated   a, gate[4096]     W[4096, 4096]     gs 128 seeds 0x701..0x703
+        o_proj
+    n3  SwiGLU-gated    gate, up[8192]    W[4096, 8192]     gs 128 seeds 0x801..0x803
+        out_proj
+    n4  norm + SwiGLU   a_a,a_b[4096] N(0,1), w_norm U(0.5,1.5), eps 1e-6,
+        MLP front       Wg,Wu[14336, 4096] gs 128         seeds 0x901..0x905
 Weights are N(0, 0.02^2) (0.02 is the standard deviation), activations N(0, 1).
 """
 from __future__ import annotations
@@ -133,6 +141,41 @@ CONFIGS = {
     "c5": dict(name="decode lanes M in {1,2,4,8} N=25600 K=5120 gs=64", N=25600, K=5120, gs=64,
                Ms=(1, 2, 4, 8)),
 }
+
+
+NEXT = {
+    "n1": dict(name="dual q + gate projection 2 x N=4096 K=4096 gs=128", N=4096, K=4096, gs=128),
+    "n2": dict(name="sigmoid-gated o_proj N=4096 K=4096 gs=128", N=4096, K=4096, gs=128),
+    "n3": dict(name="SwiGLU-gated out_proj N=4096 K=8192 gs=128", N=4096, K=8192, gs=128),
+    "n4": dict(name="norm + SwiGLU MLP front 2 x N=14336 K=4096 gs=128", N=14336, K=4096,
+               gs=128, eps=1e-6),
+}
+
+
+def n1_inputs():
+    c = NEXT["n1"]
+    return dict(x=normal_f32(0x601, c["K"]), W0=weights(0x602, c["N"], c["K"]),
+                W1=weights(0x603, c["N"], c["K"]))
+
+
+def n2_inputs():
+    c = NEXT["n2"]
+    return dict(a=normal_f32(0x701, c["K"]), gate=normal_f32(0x702, c["K"]),
+                W=weights(0x703, c["N"], c["K"]))
+
+
+def n3_inputs():
+    c = NEXT["n3"]
+    return dict(gate=normal_f32(0x801, c["K"]), up=normal_f32(0x802, c["K"]),
+                W=weights(0x803, c["N"], c["K"]))
+
+
+def n4_inputs():
+    c = NEXT["n4"]
+    K = c["K"]
+    return dict(a_a=normal_f32(0x901, K), a_b=normal_f32(0x902, K),
+                w_norm=uniform_f32(0x903, K, 0.5, 1.5), Wg=weights(0x904, c["N"], K),
+                Wu=weights(0x905, c["N"], K), eps=c["eps"])
 
 
 def c1_inputs():

@@ -33,10 +33,12 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(int4_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_every_entry_point():
     names = declared_functions()
     for n in ("int4_quantize_pack", "int4_matvec", "int4_matvec_split4", "int4_matvec_gated",
-              "int4_matvec_norm", "int4_status_str", "int4_last_error"):
+              "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
+              "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_status_str",
+              "int4_last_error"):
         assert n in names
 
 
@@ -145,3 +147,46 @@ def test_norm_eps_errors(lib):
     for eps in (-1e-6, float("nan"), float("inf")):
         assert lib.int4_matvec_norm(A, A + 0x10000, A + 0x20000, ctypes.c_float(eps), B, C, D, 16,
                                     256, 64, E, None, None, None) == ARG
+
+
+# ------------------------------------------------ dual, input-gated, norm + SwiGLU
+
+G_ = 0x70000000
+H_ = 0x80000000
+
+
+def test_next_variants_empty_calls_are_no_ops(lib):
+    assert lib.int4_matvec_dual(None, None, None, None, None, None, None, 0, 256, 64,
+                                None, None, None) == OK
+    assert lib.int4_matvec_sigmoid_gated(None, None, None, None, None, 0, 256, 64, None, None) == OK
+    assert lib.int4_matvec_swiglu_gated(None, None, None, None, None, 0, 256, 64, None, None) == OK
+    assert lib.int4_matvec_norm_swiglu(None, None, None, ctypes.c_float(1e-6), None, None, None,
+                                       None, None, None, 0, 256, 64, None, None, None) == OK
+
+
+def test_next_variants_shape_null_align_alias(lib):
+    N, K, gs = 16, 256, 64
+    # shapes
+    assert lib.int4_matvec_dual(A, B, C, D, E, F, G_, N, K, 48, H_, H_ + 0x1000, None) == SHAPE
+    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1000, B, C, D, N, 96, 64, E, None) == SHAPE
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B, C, D, -1, K, gs, E, None) == SHAPE
+    # nulls
+    assert lib.int4_matvec_dual(A, B, C, D, E, F, G_, N, K, gs, H_, None, None) == NULL
+    assert lib.int4_matvec_sigmoid_gated(A, None, B, C, D, N, K, gs, E, None) == NULL
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B, C, D, N, K, gs, None, None) == NULL
+    assert lib.int4_matvec_norm_swiglu(A, A + 0x1000, A + 0x2000, ctypes.c_float(1e-6),
+                                       B, C, D, None, F, G_, N, K, gs, H_, None, None) == NULL
+    # alignment: the second input vector must be 16-byte aligned too
+    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1004, B, C, D, N, K, gs, E, None) == ALIGN
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B + 4, C, D, N, K, gs, E, None) == ALIGN
+    assert lib.int4_matvec_dual(A, B, C, D, E + 8, F, G_, N, K, gs, H_, H_ + 0x1000, None) == ALIGN
+    # aliasing: outputs against each other and against either input vector
+    assert lib.int4_matvec_dual(A, B, C, D, E, F, G_, N, K, gs, H_, H_ + 8, None) == ALIAS
+    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1000, B, C, D, N, K, gs, A + 0x1010, None) == ALIAS
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B, C, D, N, K, gs, A + 16, None) == ALIAS
+    assert lib.int4_matvec_norm_swiglu(A, A + 0x1000, A + 0x2000, ctypes.c_float(1e-6),
+                                       B, C, D, E, F, G_, N, K, gs, H_, H_ + 16, None) == ALIAS
+    # eps
+    for eps in (-1.0, float("nan")):
+        assert lib.int4_matvec_norm_swiglu(A, A + 0x1000, A + 0x2000, ctypes.c_float(eps),
+                                           B, C, D, E, F, G_, N, K, gs, H_, None, None) == ARG

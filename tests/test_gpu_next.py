@@ -1,0 +1,253 @@
+"""GPU parity of the fused decode variants next to the hot path: the dual
+matvec, the sigmoid- and SwiGLU-gated input matvecs and the norm + SwiGLU
+MLP front.  Small shapes span several column tiles, ragged tails and both
+kernel families (K <= 16384 on the register kernel, longer K on the LDS
+kernel); the full workload sizes are checked on sampled columns."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_dot_close, gated_tolerance, integer_problem
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(129, 1024, 128), (1000, 4096, 128), (33, 2080, 32), (19, 16416, 32), (13, 20480, 64)]
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import torch
+    torch.cuda.set_device(0)
+    import int4_group_quantized_quant_amd as m
+    return m
+
+
+def to_dev(*arrs):
+    import torch
+    return [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrs]
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def quantized(seed, N, K, gs):
+    return oracle.quantize_pack(synth.weights(seed, N, K), gs)
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def close_ulps(got, want, ulps=8):
+    """|got - want| within a few binary32 ulps of want (want fp64)."""
+    got = np.asarray(got, np.float64)
+    return np.all(np.abs(got - want) <= ulps * np.spacing(np.abs(want).astype(np.float32)) + 1e-37)
+
+
+# ------------------------------------------------------------------ dual
+
+@pytest.mark.parametrize("N,K,gs", SHAPES)
+def test_dual(q4, N, K, gs):
+    q0, s0, z0 = quantized(0xF000 + N, N, K, gs)
+    q1, s1, z1 = quantized(0xF001 + N, N, K, gs)
+    x = synth.normal_f32(0xF002, K)
+    ref = oracle.dual(x, q0, s0, z0, q1, s1, z1, K, gs)
+    xd, *w = to_dev(x, q0.view(np.int32), s0, z0, q1.view(np.int32), s1, z1)
+    y0, y1 = q4.int4_matvec_dual(xd, *w)
+    assert_dot_close(host(y0), ref["y0"], ref["b0"], "dual y0")
+    assert_dot_close(host(y1), ref["y1"], ref["b1"], "dual y1")
+    # Each output is the single-lane matvec of its own matrix, bit for bit.
+    np.testing.assert_array_equal(bits(host(y0)), bits(host(q4.int4_matvec(xd, *w[:3]))))
+    np.testing.assert_array_equal(bits(host(y1)), bits(host(q4.int4_matvec(xd, *w[3:]))))
+
+
+def test_dual_integer_exact(q4):
+    rng = np.random.default_rng(0xF010)
+    N, K, gs = 300, 1024, 64
+    q0, s0, z0, X, e0 = integer_problem(rng, N, K, gs)
+    q1, s1, z1, _, _ = integer_problem(rng, N, K, gs)
+    ref = oracle.dual(X[0], q0, s0, z0, q1, s1, z1, K, gs)
+    xd, *w = to_dev(X[0], q0.view(np.int32), s0, z0, q1.view(np.int32), s1, z1)
+    y0, y1 = q4.int4_matvec_dual(xd, *w)
+    np.testing.assert_array_equal(host(y0), e0[0].astype(np.float32))
+    np.testing.assert_array_equal(host(y1), ref["y1"].astype(np.float32))
+
+
+def test_dual_rejects_mismatched_and_aliased(q4):
+    N, K, gs = 20, 512, 64
+    q0, s0, z0 = quantized(0xF020, N, K, gs)
+    x = synth.normal_f32(0xF021, K)
+    xd, qd, sd, zd = to_dev(x, q0.view(np.int32), s0, z0)
+    q2, s2, z2 = to_dev(*[a[:10] for a in (q0.view(np.int32), s0, z0)])
+    with pytest.raises(ValueError):
+        q4.int4_matvec_dual(xd, qd, sd, zd, q2, s2, z2)
+    y = host(q4.int4_matvec(xd, qd, sd, zd))
+    with pytest.raises(q4.Int4Error):
+        q4.int4_matvec_dual(xd, qd, sd, zd, qd, sd, zd, y0=xd[:N], y1=None)
+    assert y.shape == (N,)
+
+
+# ------------------------------------------------------------------ input-gated
+
+@pytest.mark.parametrize("N,K,gs", SHAPES)
+def test_sigmoid_gated(q4, N, K, gs):
+    q, s, z = quantized(0xF100 + N, N, K, gs)
+    a = synth.normal_f32(0xF101, K)
+    g = (3.0 * synth.normal_f32(0xF102, K)).astype(np.float32)
+    ref = oracle.sigmoid_gated(a, g, q, s, z, K, gs)
+    ad, gd, *w = to_dev(a, g, q.view(np.int32), s, z)
+    y = q4.int4_matvec_sigmoid_gated(ad, gd, *w)
+    assert_dot_close(host(y), ref["y"], ref["B"], "sigmoid-gated")
+
+
+@pytest.mark.parametrize("N,K,gs", SHAPES)
+def test_swiglu_gated(q4, N, K, gs):
+    q, s, z = quantized(0xF200 + N, N, K, gs)
+    g = (2.0 * synth.normal_f32(0xF201, K)).astype(np.float32)
+    u = synth.normal_f32(0xF202, K)
+    ref = oracle.swiglu_gated(g, u, q, s, z, K, gs)
+    gd, ud, *w = to_dev(g, u, q.view(np.int32), s, z)
+    y = q4.int4_matvec_swiglu_gated(gd, ud, *w)
+    assert_dot_close(host(y), ref["y"], ref["B"], "swiglu-gated")
+
+
+def test_input_gates_special_values_exact(q4):
+    # sigmoid(0) = 1/2 and silu(t) = t for large t are exact in binary32 too,
+    # so integer problems come out exact; very negative gates give zeros.
+    rng = np.random.default_rng(0xF300)
+    N, K, gs = 150, 2048, 64
+    q, s, z, X, exact = integer_problem(rng, N, K, gs)
+    w = to_dev(q.view(np.int32), s, z)
+    a2 = (2 * X[0]).astype(np.float32)
+    zeros_k = np.zeros(K, np.float32)
+    ad, zd, xd = to_dev(a2, zeros_k, X[0])
+    np.testing.assert_array_equal(host(q4.int4_matvec_sigmoid_gated(ad, zd, *w)),
+                                  exact[0].astype(np.float32))
+    # e^-32 is below half an ulp of 1, so sigmoid(32) = 1 and silu(32) = 32;
+    # |32 * x| <= 256 keeps every partial sum an integer below 2^24.
+    big, neg = to_dev(np.full(K, 32.0, np.float32), np.full(K, -200.0, np.float32))
+    np.testing.assert_array_equal(host(q4.int4_matvec_sigmoid_gated(ad, big, *w)),
+                                  (2 * exact[0]).astype(np.float32))
+    np.testing.assert_array_equal(host(q4.int4_matvec_sigmoid_gated(ad, neg, *w)), np.zeros(N, np.float32))
+    np.testing.assert_array_equal(host(q4.int4_matvec_swiglu_gated(big, xd, *w)),
+                                  (32 * exact[0]).astype(np.float32))
+    np.testing.assert_array_equal(host(q4.int4_matvec_swiglu_gated(zd, xd, *w)), np.zeros(N, np.float32))
+    np.testing.assert_array_equal(host(q4.int4_matvec_swiglu_gated(neg, xd, *w)), np.zeros(N, np.float32))
+
+
+# ------------------------------------------------------------------ norm + SwiGLU
+
+def norm_inputs(seed, K):
+    return (synth.normal_f32(seed, K), synth.normal_f32(seed + 1, K),
+            synth.uniform_f32(seed + 2, K, 0.5, 1.5))
+
+
+@pytest.mark.parametrize("N,K,gs", SHAPES)
+def test_norm_swiglu(q4, N, K, gs):
+    qg, sg, zg = quantized(0xF400 + N, N, K, gs)
+    qu, su, zu = quantized(0xF401 + N, N, K, gs)
+    a_a, a_b, wn = norm_inputs(0xF402, K)
+    ref = oracle.norm_swiglu(a_a, a_b, wn, 1e-6, qg, sg, zg, qu, su, zu, K, gs)
+    dev = to_dev(a_a, a_b, wn, qg.view(np.int32), sg, zg, qu.view(np.int32), su, zu)
+    h, r = q4.int4_matvec_norm_swiglu(*dev[:3], 1e-6, *dev[3:])
+    hh = host(h).astype(np.float64)
+    tol = gated_tolerance(ref)
+    assert np.all(np.abs(hh - ref["h"]) <= tol), f"max err/tol {np.max(np.abs(hh - ref['h']) / tol)}"
+    np.testing.assert_array_equal(bits(host(r)), bits(ref["residual"]))
+    # g and u are int4_matvec_norm's outputs bit for bit: only silu(g) * u rounds.
+    g, _, _ = q4.int4_matvec_norm(*dev[:3], 1e-6, *dev[3:6], want_residual=False, want_norm=False)
+    u, _, _ = q4.int4_matvec_norm(*dev[:3], 1e-6, *dev[6:], want_residual=False, want_norm=False)
+    g = host(g).astype(np.float64)
+    u = host(u).astype(np.float64)
+    assert close_ulps(hh, g / (1.0 + np.exp(-g)) * u)
+
+
+def test_norm_swiglu_optional_residual_and_empty(q4):
+    import torch
+    N, K, gs = 40, 1024, 64
+    qg, sg, zg = quantized(0xF500, N, K, gs)
+    qu, su, zu = quantized(0xF501, N, K, gs)
+    a_a, a_b, wn = norm_inputs(0xF502, K)
+    ref = oracle.norm_swiglu(a_a, a_b, wn, 1e-5, qg, sg, zg, qu, su, zu, K, gs)
+    dev = to_dev(a_a, a_b, wn, qg.view(np.int32), sg, zg, qu.view(np.int32), su, zu)
+    h, r = q4.int4_matvec_norm_swiglu(*dev[:3], 1e-5, *dev[3:], want_residual=False)
+    assert r is None
+    assert np.all(np.abs(host(h) - ref["h"]) <= gated_tolerance(ref))
+    qe = torch.empty((0, K // 8), dtype=torch.int32, device="cuda")
+    se = torch.empty((0, K // gs), dtype=torch.float32, device="cuda")
+    h0, r0 = q4.int4_matvec_norm_swiglu(*dev[:3], 1e-5, qe, se, se, qe, se, se)
+    assert h0.shape == (0,)
+    np.testing.assert_array_equal(host(r0), ref["residual"])
+
+
+# ------------------------------------------------------------------ full workload sizes
+
+def sample_cols(N, seed):
+    rng = np.random.default_rng(seed)
+    cols = set(rng.choice(N, size=min(N, 384), replace=False).tolist())
+    cols |= set(range(min(N, 8))) | set(range(max(0, N - 8), N))
+    return np.array(sorted(cols))
+
+
+def gpu_quantized(q4, W, gs, cols):
+    """GPU codes for all of W, oracle codes for the sampled rows (compared bitwise)."""
+    import torch
+    qd, sd, zd = q4.int4_quantize_pack(torch.from_numpy(W).cuda(), gs)
+    ref = oracle.quantize_pack(W[cols], gs)
+    idx = torch.from_numpy(cols).cuda()
+    for got, want in zip((qd, sd, zd), ref):
+        np.testing.assert_array_equal(bits(host(got[idx])), bits(want))
+    return (qd, sd, zd), ref
+
+
+def test_n1_dual_full(q4):
+    import torch
+    c = synth.NEXT["n1"]
+    inp = synth.n1_inputs()
+    cols = sample_cols(c["N"], 0x61)
+    (w0, r0) = gpu_quantized(q4, inp["W0"], c["gs"], cols)
+    (w1, r1) = gpu_quantized(q4, inp["W1"], c["gs"], cols)
+    y0, y1 = q4.int4_matvec_dual(torch.from_numpy(inp["x"]).cuda(), *w0, *w1)
+    ref = oracle.dual(inp["x"], *r0, *r1, c["K"], c["gs"])
+    assert_dot_close(host(y0)[cols], ref["y0"], ref["b0"], "n1 y0")
+    assert_dot_close(host(y1)[cols], ref["y1"], ref["b1"], "n1 y1")
+
+
+def test_n2_sigmoid_gated_full(q4):
+    import torch
+    c = synth.NEXT["n2"]
+    inp = synth.n2_inputs()
+    cols = sample_cols(c["N"], 0x62)
+    w, r = gpu_quantized(q4, inp["W"], c["gs"], cols)
+    y = q4.int4_matvec_sigmoid_gated(*to_dev(inp["a"], inp["gate"]), *w)
+    ref = oracle.sigmoid_gated(inp["a"], inp["gate"], *r, c["K"], c["gs"])
+    assert_dot_close(host(y)[cols], ref["y"], ref["B"], "n2")
+
+
+def test_n3_swiglu_gated_full(q4):
+    c = synth.NEXT["n3"]
+    inp = synth.n3_inputs()
+    cols = sample_cols(c["N"], 0x63)
+    w, r = gpu_quantized(q4, inp["W"], c["gs"], cols)
+    y = q4.int4_matvec_swiglu_gated(*to_dev(inp["gate"], inp["up"]), *w)
+    ref = oracle.swiglu_gated(inp["gate"], inp["up"], *r, c["K"], c["gs"])
+    assert_dot_close(host(y)[cols], ref["y"], ref["B"], "n3")
+
+
+def test_n4_norm_swiglu_full(q4):
+    c = synth.NEXT["n4"]
+    inp = synth.n4_inputs()
+    cols = sample_cols(c["N"], 0x64)
+    wg, rg = gpu_quantized(q4, inp["Wg"], c["gs"], cols)
+    wu, ru = gpu_quantized(q4, inp["Wu"], c["gs"], cols)
+    dev = to_dev(inp["a_a"], inp["a_b"], inp["w_norm"])
+    h, r = q4.int4_matvec_norm_swiglu(*dev, inp["eps"], *wg, *wu)
+    ref = oracle.norm_swiglu(inp["a_a"], inp["a_b"], inp["w_norm"], inp["eps"], *rg, *ru,
+                             c["K"], c["gs"])
+    hh = host(h)[cols].astype(np.float64)
+    assert np.all(np.abs(hh - ref["h"]) <= gated_tolerance(ref)), "n4"
+    np.testing.assert_array_equal(host(r), ref["residual"])
