@@ -68,6 +68,9 @@ def _load():
     lib.oracle_norm_swiglu.argtypes = [_f32p, _f32p, _f32p, ctypes.c_float,
                                        _u32p, _f32p, _f32p, _u32p, _f32p, _f32p, _i64, _i64, _i32,
                                        _f64p, _f64p, _f64p, _f64p, _f64p, _f32p]
+    lib.oracle_embedding.argtypes = [np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS"),
+                                     _i64, _u32p, _f32p, _f32p, _i64, _i64, _i32, _f32p]
+    lib.oracle_embedding.restype = None
     for fn in (lib.oracle_quantize_pack, lib.oracle_dequant, lib.oracle_matvec,
                lib.oracle_matvec_f32, lib.oracle_split4, lib.oracle_gated, lib.oracle_norm,
                lib.oracle_dual, lib.oracle_input_gated, lib.oracle_norm_swiglu):
@@ -228,6 +231,18 @@ def norm_swiglu(a_a, a_b, w_norm, eps: float, q_gate, s_gate, z_gate, q_up, s_up
                                _c(z_gate, np.float32), q_up, _c(s_up, np.float32),
                                _c(z_up, np.float32), N, K, group_size,
                                out["h"], out["g"], out["u"], out["bg"], out["bu"], out["residual"])
+    return out
+
+
+def embedding(ids, q, scales, zeros, K: int, group_size: int) -> np.ndarray:
+    """ids int32 [T] -> out f32 [T, K]: the dequantized table rows (zeros for ids outside [0, N))."""
+    ids = _c(ids, np.int32)
+    q = _c(q, np.uint32)
+    N = q.shape[0]
+    _check_shape(K, group_size)
+    out = np.empty((ids.shape[0], K), np.float32)
+    _load().oracle_embedding(ids, ids.shape[0], q, _c(scales, np.float32), _c(zeros, np.float32),
+                             N, K, group_size, out)
     return out
 
 

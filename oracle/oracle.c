@@ -324,3 +324,20 @@ void oracle_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm,
     }
     free(normed);
 }
+
+/*
+ * Int4 embedding row gather ([P1] EmbeddingInt4, the first kernel of a
+ * forward pass, and the per-layer-embedding rows gathered and dequantized
+ * for the input tokens; [P3] the embed_tokens .q/.scales/.zeros triplet):
+ *   out[t][k] = dq[ids[t]][k] = (code - zero) * scale   (binary32)
+ * A row of the table is stored like a weight column.  Ids outside [0, N)
+ * give a row of zeros (the reading taken for an out-of-range token).
+ */
+void oracle_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                      const float* zeros, int64_t N, int64_t K, int32_t gs, float* out) {
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = ids[t];
+        for (int64_t k = 0; k < K; ++k)
+            out[t * K + k] = (n >= 0 && n < N) ? dq_at(q, scales, zeros, K, gs, n, k) : 0.0f;
+    }
+}

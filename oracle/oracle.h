@@ -48,6 +48,8 @@ void oracle_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm,
                         int64_t N, int64_t K, int32_t gs,
                         double* h, double* g, double* u, double* bg, double* bu,
                         float* residual);
+void oracle_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                      const float* zeros, int64_t N, int64_t K, int32_t gs, float* out);
 
 #ifdef __cplusplus
 }

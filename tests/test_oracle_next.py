@@ -188,3 +188,36 @@ def test_norm_swiglu_equals_the_unfused_chain():
     np.testing.assert_allclose(r["u"], u, rtol=0, atol=1e-12 * np.max(r["bu"]))
     scale = np.abs(u) * np.max(r["bg"]) + np.abs(g) * np.max(r["bu"])
     np.testing.assert_allclose(r["h"], g * expit(g) * u, rtol=0, atol=1e-11 * np.max(scale) + 1e-300)
+
+
+# ------------------------------------------------------------------ embedding gather
+
+def test_embedding_hand_values():
+    # Row 1 holds codes 0..15 in its first two words (low nibble first), codes 0
+    # elsewhere; group 0 (inputs 0..31) has scale 0.5 and zero 3, group 1
+    # (inputs 32..63) scale -2 and zero 15: values by hand.
+    K, gs = 64, 32
+    q = np.zeros((3, K // 8), np.uint32)
+    q[1, 0] = 0x76543210
+    q[1, 1] = 0xFEDCBA98
+    s = np.array([[1.0, 1.0], [0.5, -2.0], [1.0, 1.0]], np.float32)
+    z = np.array([[0.0, 0.0], [3.0, 15.0], [0.0, 0.0]], np.float32)
+    out = oracle.embedding(np.array([1], np.int32), q, s, z, K, gs)
+    want = np.zeros(K, np.float32)
+    want[:8] = [-1.5, -1.0, -0.5, 0.0, 0.5, 1.0, 1.5, 2.0]
+    want[8:16] = [2.5, 3.0, 3.5, 4.0, 4.5, 5.0, 5.5, 6.0]       # (8..15 - 3) * 0.5
+    want[16:32] = -1.5                                           # codes 0 in group 0: (0 - 3) * 0.5
+    want[32:] = 30.0                                             # codes 0 in group 1: (0 - 15) * -2
+    np.testing.assert_array_equal(out[0], want)
+
+
+def test_embedding_rows_match_an_independent_decode():
+    N, K, gs = 50, 512, 128
+    q, s, z = quantized(0x91, N, K, gs)
+    ids = np.array([0, 49, 7, 7, -1, 50, 3, 2**31 - 1], np.int32)
+    out = oracle.embedding(ids, q, s, z, K, gs)
+    codes = unpack(q, K).astype(np.float32)
+    dq = (codes - np.repeat(z, gs, axis=1)) * np.repeat(s, gs, axis=1)  # binary32, one rounding
+    for t, n in enumerate(ids):
+        want = dq[n] if 0 <= n < N else np.zeros(K, np.float32)
+        np.testing.assert_array_equal(out[t].view(np.uint32), want.astype(np.float32).view(np.uint32))
