@@ -14,6 +14,15 @@ value = effective GB/s of the step = algorithmic bytes per step / time per step,
 where algorithmic bytes = packed codes N*K/2 + fp32 scales and zeros
 N*(K/gs)*8 + fp32 activations in + fp32 outputs out (what the method must move).
 
+Next-row calls (the fused variants beside the hot path) are timed the same
+way and reported under "next_rows"; they are not part of the step:
+  dual     x[4096] . W0, W1 [4096, 4096]                                 (gs 128)
+  sig      (a * sigmoid(gate))[4096] . W[4096, 4096]                      (gs 128)
+  swiglu   (silu(gate) * up)[8192] . W[4096, 8192]                        (gs 128)
+  normswi  silu(x . Wg) * (x . Wu), x = RMSNorm(a_a + a_b) * w_norm, [14336, 4096] (gs 128)
+  embed    rows ids[T] of an int4 table [151936, 4096] dequantized, T = 1 and 4096 (gs 128);
+           bytes = ids + the T rows' codes, scales and zeros + the fp32 output
+
 Per-call durations: each call is also timed alone, in a graph of back-to-back
 calls cycling over >= 1 GiB of device copies of its buffers, with HIP events
 on the stream the kernels run on.  The norm LM head call is the dominant
@@ -190,6 +199,75 @@ def build_workload(q4, torch, dev):
     return calls, quant, {"y4": y4, "a4": a4, "w4": w4}
 
 
+def build_next(q4, torch, dev):
+    """Calls of the fused variants next to the hot path (timed alone, not in the step)."""
+    n1, n2, n3, n4 = (synth.NEXT[k] for k in ("n1", "n2", "n3", "n4"))
+    calls = []
+
+    def quantize(W, gs):
+        return q4.int4_quantize_pack(torch.from_numpy(W).to(dev), gs)
+
+    def clones(tensors, r):
+        sets = [tuple(tensors)]
+        for _ in range(r - 1):
+            sets.append(tuple(t.clone() for t in tensors))
+        return sets
+
+    def wbytes(ws):
+        return sum(t.numel() * 4 for t in ws)
+
+    log("generating and quantizing next-row weights (dual, gated inputs, norm + SwiGLU)")
+    i1 = synth.n1_inputs()
+    w1 = (*quantize(i1["W0"], n1["gs"]), *quantize(i1["W1"], n1["gs"]))
+    x1 = torch.from_numpy(i1["x"]).to(dev)
+    y1 = (torch.empty(n1["N"], device=dev), torch.empty(n1["N"], device=dev))
+    b1 = 2 * alg_bytes(n1["N"], n1["K"], n1["gs"], 0, n1["N"]) + 4 * n1["K"]
+    calls.append(Call(f"dual 2x{n1['N']}x{n1['K']}", b1,
+                      lambda s: q4.int4_matvec_dual(x1, *s, y0=y1[0], y1=y1[1]),
+                      lambda r: clones(w1, r), wbytes(w1)))
+
+    i2 = synth.n2_inputs()
+    w2 = quantize(i2["W"], n2["gs"])
+    a2 = [torch.from_numpy(i2[k]).to(dev) for k in ("a", "gate")]
+    y2 = torch.empty(n2["N"], device=dev)
+    b2 = alg_bytes(n2["N"], n2["K"], n2["gs"], 2 * n2["K"], n2["N"])
+    calls.append(Call(f"sigmoid-gated {n2['N']}x{n2['K']}", b2,
+                      lambda s: q4.int4_matvec_sigmoid_gated(*a2, *s, y=y2),
+                      lambda r: clones(w2, r), wbytes(w2)))
+
+    i3 = synth.n3_inputs()
+    w3 = quantize(i3["W"], n3["gs"])
+    a3 = [torch.from_numpy(i3[k]).to(dev) for k in ("gate", "up")]
+    y3 = torch.empty(n3["N"], device=dev)
+    b3 = alg_bytes(n3["N"], n3["K"], n3["gs"], 2 * n3["K"], n3["N"])
+    calls.append(Call(f"swiglu-gated {n3['N']}x{n3['K']}", b3,
+                      lambda s: q4.int4_matvec_swiglu_gated(*a3, *s, y=y3),
+                      lambda r: clones(w3, r), wbytes(w3)))
+
+    i4 = synth.n4_inputs()
+    w4 = (*quantize(i4["Wg"], n4["gs"]), *quantize(i4["Wu"], n4["gs"]))
+    a4 = [torch.from_numpy(i4[k]).to(dev) for k in ("a_a", "a_b", "w_norm")]
+    h4 = torch.empty(n4["N"], device=dev)
+    r4 = torch.empty(n4["K"], device=dev)
+    b4 = 2 * alg_bytes(n4["N"], n4["K"], n4["gs"], 0, 0) + 4 * (3 * n4["K"] + n4["N"] + n4["K"])
+    calls.append(Call(f"norm+swiglu 2x{n4['N']}x{n4['K']}", b4,
+                      lambda s: q4.int4_matvec_norm_swiglu(*a4, n4["eps"], *s, h=h4, residual_out=r4),
+                      lambda r: clones(w4, r), wbytes(w4)))
+
+    i5 = synth.n5_inputs()
+    n5 = synth.NEXT["n5"]
+    w5 = quantize(i5["W"], n5["gs"])
+    del i5["W"]
+    for T in n5["Ts"]:
+        ids = torch.from_numpy(i5["ids"][:T].copy()).to(dev)
+        out = torch.empty((T, n5["K"]), device=dev)
+        b5 = 4 * T + T * (n5["K"] // 2 + (n5["K"] // n5["gs"]) * 8) + 4 * T * n5["K"]
+        calls.append(Call(f"embedding T={T} {n5['N']}x{n5['K']}", b5,
+                          lambda s, ids=ids, out=out: q4.int4_embedding_gather(ids, *s, out=out),
+                          lambda r: clones(w5, r), wbytes(w5)))
+    return calls
+
+
 # ---------------------------------------------------------------- timing
 
 def capture(torch, fn):
@@ -352,6 +430,18 @@ def main():
         log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
             f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)")
 
+    # Next-row calls, timed alone (not part of the step).
+    next_rows = {}
+    for c in build_next(q4, torch, dev):
+        us, r = time_call(torch, c)
+        next_rows[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
+                             "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
+                             "alg_bytes": c.nbytes, "rotating_copies": r}
+        log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
+            f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)  [next row, not in the step]")
+        del c
+    torch.cuda.empty_cache()
+
     # The step graph.
     sets = [c.sets_fn(1)[0] for c in calls]
     step = capture(torch, lambda: [c.fn(s) for c, s in zip(calls, sets)])
@@ -401,6 +491,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_call": per_call,
+        "next_rows": next_rows,
         "quantize_pack": {"elements": quant["elements"], "seconds": round(quant["seconds"], 4),
                           "GBps_fp32_in": round(4 * quant["elements"] / quant["seconds"] / 1e9, 1)},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),

@@ -211,6 +211,22 @@ int int4_matvec_norm_swiglu(const float* a_a, const float* a_b, const float* w_n
                             int64_t N, int64_t K, int32_t group_size,
                             float* h, float* residual_out, void* stream);
 
+/*
+ * Int4 embedding row gather and dequant ([P1] EmbeddingInt4, the first
+ * kernel of a forward pass, and the per-layer-embedding rows gathered and
+ * dequantized for the input tokens only; [P3] the embed_tokens .q / .scales
+ * / .zeros triplet).  The table [N][K] is stored like a weight matrix (row n
+ * = "column" n above):
+ *   out[t][k] = (code(ids[t], k) - zero) * scale,   0 <= t < T,
+ * in binary32 with one rounding, so the rows are bit-identical to the
+ * definition.  ids is an int32 device array of T token ids; an id outside
+ * [0, N) writes a row of zeros.  out is [T][K] fp32, 16-byte aligned.
+ * T == 0 writes nothing; N == 0 (an empty table) writes zeros.
+ */
+int int4_embedding_gather(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                          const float* zeros, int64_t N, int64_t K, int32_t group_size,
+                          float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

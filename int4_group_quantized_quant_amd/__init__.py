@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "Int4Error", "int4_quantize_pack", "int4_matvec", "int4_matvec_split4",
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
-    "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "lib", "LIB_PATH",
+    "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "lib",
+    "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -52,7 +53,8 @@ lib.int4_matvec_sigmoid_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _
 lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 lib.int4_matvec_norm_swiglu.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i64, _i64, _i32, _vp, _vp, _vp]
-for _fn in (lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
+lib.int4_embedding_gather.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+for _fn in (lib.int4_embedding_gather, lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
             lib.int4_matvec_gated, lib.int4_matvec_norm, lib.int4_matvec_dual,
             lib.int4_matvec_sigmoid_gated, lib.int4_matvec_swiglu_gated,
             lib.int4_matvec_norm_swiglu):
@@ -270,3 +272,17 @@ def int4_matvec_norm_swiglu(a_a: torch.Tensor, a_b: torch.Tensor, w_norm: torch.
                                        _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(h) if N else None,
                                        _ptr(residual_out), _stream(stream)))
     return h, residual_out
+
+
+def int4_embedding_gather(ids: torch.Tensor, q, scales, zeros, out=None, stream=None) -> torch.Tensor:
+    """ids int32 [T] -> out float32 [T, K]: rows ids[t] of the int4 table, dequantized."""
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(ids, "ids", (torch.int32,))
+    T = ids.numel()
+    out = torch.empty((T, K), dtype=torch.float32, device=ids.device) if out is None else out
+    _dev(out, "out", _F32)
+    if out.numel() != T * K:
+        raise ValueError(f"out must hold T*K = {T * K} floats")
+    _check(lib.int4_embedding_gather(_ptr(ids), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs,
+                                     _ptr(out), _stream(stream)))
+    return out

@@ -638,4 +638,31 @@ int int4_matvec_norm_swiglu(const float* a_a, const float* a_b, const float* w_n
   return run(kNormSwi, a, stream);
 }
 
+int int4_embedding_gather(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                          const float* zeros, int64_t N, int64_t K, int32_t group_size, float* out,
+                          void* stream) {
+  if (N < 0 || T < 0) return fail(INT4_ERR_SHAPE, "N and T must be >= 0 (N=%lld, T=%lld)", (long long)N,
+                                  (long long)T);
+  RETURN_IF(check_kgs(K, group_size));
+  if (T == 0) return ok();
+  if (!ids || !out) return fail(INT4_ERR_NULL, "ids and out are required");
+  if (N > 0 && (!q || !scales || !zeros)) return fail(INT4_ERR_NULL, "q, scales and zeros are required when N > 0");
+  RETURN_IF(check_align(ids, 4, "ids"));
+  RETURN_IF(check_align(q, 4, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(out, 16, "out"));
+  if ((uint64_t)T * (uint64_t)K > ((uint64_t)1 << 40))
+    return fail(INT4_ERR_SHAPE, "T*K=%llu is larger than supported", (unsigned long long)T * K);
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{ids, (uint64_t)T * 4, "ids"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{out, (uint64_t)T * K * 4, "out"}};
+  RETURN_IF(check_alias(ins, 4, outs, 1));
+  hipError_t e = launch_embedding(ids, T, q, scales, zeros, N, (int32_t)K, group_size, out,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -123,6 +123,11 @@ hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& shape
 int max_ncol(Mode mode, int M, int variant);
 
 // Quantize + pack launch: groups [0, total_groups), each gs consecutive floats.
+// Int4 embedding row gather: out [T][K] from rows ids[t] of the table.
+hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                            const float* zeros, int64_t N, int32_t K, int32_t gs, float* out,
+                            hipStream_t stream);
+
 hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,
                            float* scales, float* zeros, hipStream_t stream);
 

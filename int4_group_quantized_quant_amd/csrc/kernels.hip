@@ -730,6 +730,42 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   }
 }
 
+// ------------------------------------------------------------ embedding gather
+
+// out[t][k] = (code - zero) * scale of row ids[t] of a table stored like the
+// weight columns ([P1] EmbeddingInt4 and the per-layer-embedding row gather).
+// One lane per 32-bit code word: a 4-byte load, eight values, two 16-byte
+// stores, so a wave reads 256 contiguous bytes and writes 2 KiB.  The value
+// is rounded once, as the definition states.  Ids outside [0, N) write zeros.
+__global__ __launch_bounds__(256) void embedding_gather_kernel(const int32_t* __restrict__ ids, int64_t T,
+                                                               const uint32_t* __restrict__ q,
+                                                               const float* __restrict__ scales,
+                                                               const float* __restrict__ zeros, int64_t N,
+                                                               int32_t K, int32_t gs, float* __restrict__ out) {
+  const int64_t wpr = K >> 3;  // code words per row
+  const int64_t total = T * wpr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t t = i / wpr;
+    const int64_t w = i - t * wpr;
+    const int64_t n = ids[t];
+    float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+    if (n >= 0 && n < N) {
+      const uint32_t word = q[n * wpr + w];
+      const int64_t g = n * (K / gs) + (w * 8) / gs;
+      const float sc = scales[g], zp = zeros[g];
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = ((float)((word >> (4 * j)) & 15u) - zp) * sc;
+      lo = make_float4(v[0], v[1], v[2], v[3]);
+      hi = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    float4* dst = reinterpret_cast<float4*>(out + t * (int64_t)K + w * 8);
+    dst[0] = lo;
+    dst[1] = hi;
+  }
+}
+
 // ------------------------------------------------------------ quantize + pack
 
 // Clamp to [0, 15] in binary32; NaN and both zeros give +0.
@@ -1340,16 +1376,9 @@ hipError_t launch_lds(const GemvArgs& a, const LaunchShape& s, hipStream_t strea
 
 template <int MODE>
 hipError_t dispatch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if (a.M != 1) return hipErrorInvalidValue;  // the register kernel runs one lane
   if constexpr (mode_streams(MODE) == 2) {
     return s.ncol == 1 ? launch_reg<MODE, 1, 1>(a, s, st, occ) : launch_reg<MODE, 1, 2>(a, s, st, occ);
-  } else if constexpr (MODE == kPlain) {
-    if (a.M == 2)
-      return s.ncol == 1 ? launch_reg<MODE, 2, 1>(a, s, st, occ) : launch_reg<MODE, 2, 2>(a, s, st, occ);
-    switch (s.ncol) {
-      case 1: return launch_reg<MODE, 1, 1>(a, s, st, occ);
-      case 2: return launch_reg<MODE, 1, 2>(a, s, st, occ);
-      default: return launch_reg<MODE, 1, 4>(a, s, st, occ);
-    }
   } else {
     switch (s.ncol) {
       case 1: return launch_reg<MODE, 1, 1>(a, s, st, occ);
@@ -1434,6 +1463,17 @@ hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, in
 
 hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t stream) {
   return dispatch(mode, a, s, stream, nullptr);
+}
+
+hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                            const float* zeros, int64_t N, int32_t K, int32_t gs, float* out,
+                            hipStream_t stream) {
+  const int64_t total = T * (K / 8);
+  int64_t grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;  // grid-stride beyond this
+  hipLaunchKernelGGL(embedding_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ids, T, q,
+                     scales, zeros, N, K, gs, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,

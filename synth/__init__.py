@@ -33,6 +33,8 @@ Next-row workloads (fused decode variants around the hot path, same recipe):
         out_proj
     n4  norm + SwiGLU   a_a,a_b[4096] N(0,1), w_norm U(0.5,1.5), eps 1e-6,
         MLP front       Wg,Wu[14336, 4096] gs 128         seeds 0x901..0x905
+    n5  embedding       ids[T] uniform in [0, 151936) (T = 1 and 4096), table
+        gather          [151936, 4096] gs 128               seeds 0xA01/0xA02
 Weights are N(0, 0.02^2) (0.02 is the standard deviation), activations N(0, 1).
 """
 from __future__ import annotations
@@ -149,6 +151,8 @@ NEXT = {
     "n3": dict(name="SwiGLU-gated out_proj N=4096 K=8192 gs=128", N=4096, K=8192, gs=128),
     "n4": dict(name="norm + SwiGLU MLP front 2 x N=14336 K=4096 gs=128", N=14336, K=4096,
                gs=128, eps=1e-6),
+    "n5": dict(name="int4 embedding gather from a [151936, 4096] gs=128 table, T = 1 and 4096",
+               N=151936, K=4096, gs=128, Ts=(1, 4096)),
 }
 
 
@@ -176,6 +180,16 @@ def n4_inputs():
     return dict(a_a=normal_f32(0x901, K), a_b=normal_f32(0x902, K),
                 w_norm=uniform_f32(0x903, K, 0.5, 1.5), Wg=weights(0x904, c["N"], K),
                 Wu=weights(0x905, c["N"], K), eps=c["eps"])
+
+
+def token_ids(seed: int, T: int, N: int) -> np.ndarray:
+    """int32 ids floor(u_i * N) for i in [0, T)."""
+    return np.minimum((uniform(seed, 0, T) * N).astype(np.int64), N - 1).astype(np.int32)
+
+
+def n5_inputs(N: int | None = None):
+    c = NEXT["n5"]
+    return dict(ids=token_ids(0xA01, max(c["Ts"]), c["N"]), W=weights(0xA02, N or c["N"], c["K"]))
 
 
 def c1_inputs():

@@ -16,8 +16,8 @@ OK, NULL, SHAPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5
 
 def _ensure_built():
     if not os.path.exists(LIB):
-        from int4_group_quantized_quant_amd import _build
-        _build.build()
+        import __graft_entry__
+        __graft_entry__.build()
 
 
 @pytest.fixture(scope="module")
@@ -37,8 +37,8 @@ def test_header_declares_every_entry_point():
     names = declared_functions()
     for n in ("int4_quantize_pack", "int4_matvec", "int4_matvec_split4", "int4_matvec_gated",
               "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
-              "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_status_str",
-              "int4_last_error"):
+              "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather",
+              "int4_status_str", "int4_last_error"):
         assert n in names
 
 
@@ -190,3 +190,16 @@ def test_next_variants_shape_null_align_alias(lib):
     for eps in (-1.0, float("nan")):
         assert lib.int4_matvec_norm_swiglu(A, A + 0x1000, A + 0x2000, ctypes.c_float(eps),
                                            B, C, D, E, F, G_, N, K, gs, H_, None, None) == ARG
+
+
+def test_embedding_gather_validation(lib):
+    K, gs = 256, 64
+    assert lib.int4_embedding_gather(None, 0, None, None, None, 16, K, gs, None, None) == OK   # T == 0
+    assert lib.int4_embedding_gather(A, -1, B, C, D, 16, K, gs, E, None) == SHAPE
+    assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, 48, E, None) == SHAPE
+    assert lib.int4_embedding_gather(None, 4, B, C, D, 16, K, gs, E, None) == NULL
+    assert lib.int4_embedding_gather(A, 4, None, C, D, 16, K, gs, E, None) == NULL
+    assert lib.int4_embedding_gather(A + 2, 4, B, C, D, 16, K, gs, E, None) == ALIGN
+    assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, gs, E + 4, None) == ALIGN
+    assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, gs, B + 64, None) == ALIAS
+    assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, gs, A - 16, None) == ALIAS

@@ -184,6 +184,39 @@ def test_norm_swiglu_optional_residual_and_empty(q4):
     np.testing.assert_array_equal(host(r0), ref["residual"])
 
 
+# ------------------------------------------------------------------ embedding gather
+
+@pytest.mark.parametrize("N,K,gs,T", [(1000, 1024, 128, 37), (77, 4096, 64, 300), (5, 2080, 32, 9)])
+def test_embedding_gather(q4, N, K, gs, T):
+    q, s, z = quantized(0xF600 + N, N, K, gs)
+    rng = np.random.default_rng(N)
+    ids = rng.integers(0, N, T).astype(np.int32)
+    ids[:4] = [0, N - 1, -1, N]          # both ends and two ids out of range
+    ids[-1] = 2**31 - 1
+    if T > 6:
+        ids[5] = ids[4]                  # a repeated token
+    ref = oracle.embedding(ids, q, s, z, K, gs)
+    idd, qd, sd, zd = to_dev(ids, q.view(np.int32), s, z)
+    out = host(q4.int4_embedding_gather(idd, qd, sd, zd))
+    np.testing.assert_array_equal(bits(out), bits(ref))
+
+
+def test_embedding_gather_empty_cases(q4):
+    import torch
+    K, gs = 512, 64
+    q, s, z = quantized(0xF700, 8, K, gs)
+    qd, sd, zd = to_dev(q.view(np.int32), s, z)
+    ids0 = torch.empty(0, dtype=torch.int32, device="cuda")
+    assert q4.int4_embedding_gather(ids0, qd, sd, zd).shape == (0, K)
+    # An empty table: every id is out of range, every row is zeros.
+    qe = torch.empty((0, K // 8), dtype=torch.int32, device="cuda")
+    se = torch.empty((0, K // gs), dtype=torch.float32, device="cuda")
+    ids = torch.tensor([0, 3, -2], dtype=torch.int32, device="cuda")
+    out = torch.full((3, K), 7.0, device="cuda")
+    q4.int4_embedding_gather(ids, qe, se, se, out=out)
+    np.testing.assert_array_equal(host(out), np.zeros((3, K), np.float32))
+
+
 # ------------------------------------------------------------------ full workload sizes
 
 def sample_cols(N, seed):
@@ -251,3 +284,22 @@ def test_n4_norm_swiglu_full(q4):
     hh = host(h)[cols].astype(np.float64)
     assert np.all(np.abs(hh - ref["h"]) <= gated_tolerance(ref)), "n4"
     np.testing.assert_array_equal(host(r), ref["residual"])
+
+
+def test_n5_embedding_gather_full(q4):
+    import torch
+    c = synth.NEXT["n5"]
+    inp = synth.n5_inputs()
+    rows = sample_cols(c["N"], 0x65)
+    w, r = gpu_quantized(q4, inp["W"], c["gs"], rows)
+    del inp["W"]
+    # Gather T ids drawn from the sampled rows (so the oracle holds their codes),
+    # in the order and multiplicity of the workload's id stream.
+    T = max(c["Ts"])
+    ids = rows[inp["ids"] % len(rows)].astype(np.int32)
+    out = host(q4.int4_embedding_gather(torch.from_numpy(ids).cuda(), *w))
+    # The oracle table holds the sampled rows only: map each id to its position there.
+    pos = np.searchsorted(rows, ids).astype(np.int32)
+    ref = oracle.embedding(pos, *r, c["K"], c["gs"])
+    assert out.shape == (T, c["K"])
+    np.testing.assert_array_equal(bits(out), bits(ref))
