@@ -43,6 +43,7 @@
 #ifndef INT4GEMV_H
 #define INT4GEMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -226,6 +227,24 @@ int int4_matvec_norm_swiglu(const float* a_a, const float* a_b, const float* w_n
 int int4_embedding_gather(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
                           const float* zeros, int64_t N, int64_t K, int32_t group_size,
                           float* out, void* stream);
+
+/*
+ * Prefill GEMM: Y[t][n] = sum_k X[t][k] * w[n][k] for T tokens at once
+ * ([P1] the prefill path runs a tiled matmul for any number of rows, decode
+ * the K-parallel matvec).  Same weights, layouts and tolerance as
+ * int4_matvec (X [T][K], Y [T][N] row-major; any T >= 0).  Runs on the
+ * matrix cores with the activations split into two fp16 halves, so each
+ * output is within 1e-4 * sum_k |x w| + 1e-6 of the exact sum.
+ *
+ * workspace: device memory of at least int4_gemm_workspace_bytes(T, N, K,
+ * group_size) bytes, 256-byte aligned, owned by the caller; its contents are
+ * scratch (overwritten, not read back across calls).  Two calls that share
+ * a workspace must not overlap in time.  Requires N * K / 2 < 2^31.
+ */
+size_t int4_gemm_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t group_size);
+int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales,
+              const float* zeros, int64_t N, int64_t K, int32_t group_size, float* Y,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,8 +21,8 @@ import torch
 __all__ = [
     "Int4Error", "int4_quantize_pack", "int4_matvec", "int4_matvec_split4",
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
-    "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "lib",
-    "LIB_PATH",
+    "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
+    "int4_gemm_workspace_bytes", "lib", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -54,7 +54,10 @@ lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i
 lib.int4_matvec_norm_swiglu.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i64, _i64, _i32, _vp, _vp, _vp]
 lib.int4_embedding_gather.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
-for _fn in (lib.int4_embedding_gather, lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
+lib.int4_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
+lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
+lib.int4_gemm.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, ctypes.c_size_t, _vp]
+for _fn in (lib.int4_gemm, lib.int4_embedding_gather, lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
             lib.int4_matvec_gated, lib.int4_matvec_norm, lib.int4_matvec_dual,
             lib.int4_matvec_sigmoid_gated, lib.int4_matvec_swiglu_gated,
             lib.int4_matvec_norm_swiglu):
@@ -286,3 +289,30 @@ def int4_embedding_gather(ids: torch.Tensor, q, scales, zeros, out=None, stream=
     _check(lib.int4_embedding_gather(_ptr(ids), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs,
                                      _ptr(out), _stream(stream)))
     return out
+
+
+def int4_gemm_workspace_bytes(T: int, N: int, K: int, group_size: int) -> int:
+    """Bytes of device workspace int4_gemm needs for these sizes."""
+    return int(lib.int4_gemm_workspace_bytes(T, N, K, group_size))
+
+
+def int4_gemm(X: torch.Tensor, q, scales, zeros, Y=None, workspace=None, stream=None) -> torch.Tensor:
+    """X float32 [T, K] -> Y float32 [T, N] (prefill GEMM on the matrix cores).
+
+    workspace: a uint8 device tensor of at least int4_gemm_workspace_bytes bytes
+    (256-byte aligned); allocated here when not given.
+    """
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(X, "X", _F32)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError(f"X must be [T, {K}]")
+    T = X.shape[0]
+    Y = torch.empty((T, N), dtype=torch.float32, device=X.device) if Y is None else Y
+    _dev(Y, "Y", _F32)
+    need = int4_gemm_workspace_bytes(T, N, K, gs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _dev(workspace, "workspace", (torch.uint8,))
+    _check(lib.int4_gemm(_ptr(X), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
+                         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return Y

@@ -665,4 +665,64 @@ int int4_embedding_gather(const int32_t* ids, int64_t T, const uint32_t* q, cons
   return ok();
 }
 
+size_t int4_gemm_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t group_size) {
+  if (T <= 0 || N <= 0 || K <= 0 || group_size <= 0) return 0;
+  return gemm_layout(T, N, K, group_size).bytes;
+}
+
+int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales, const float* zeros,
+              int64_t N, int64_t K, int32_t group_size, float* Y, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (N < 0 || T < 0) return fail(INT4_ERR_SHAPE, "N and T must be >= 0 (N=%lld, T=%lld)", (long long)N,
+                                  (long long)T);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0 || T == 0) return ok();
+  if ((uint64_t)N * (uint64_t)K / 2 >= ((uint64_t)1 << 31))
+    return fail(INT4_ERR_SHAPE, "N*K/2 = %llu bytes of codes exceed 2^31", (unsigned long long)N * K / 2);
+  const GemmLayout L = gemm_layout(T, N, K, group_size);
+  if ((uint64_t)L.Tp * (uint64_t)L.Kp * 4 >= ((uint64_t)1 << 40) || L.Tp / 128 * (L.Np / 128) >= ((int64_t)1 << 31))
+    return fail(INT4_ERR_SHAPE, "T=%lld is larger than supported", (long long)T);
+  if (!X || !q || !scales || !zeros || !Y) return fail(INT4_ERR_NULL, "X, q, scales, zeros and Y are required");
+  if (!workspace) return fail(INT4_ERR_NULL, "workspace is required (int4_gemm_workspace_bytes)");
+  if (workspace_bytes < L.bytes)
+    return fail(INT4_ERR_SHAPE, "workspace holds %zu bytes; this call needs %zu", workspace_bytes, L.bytes);
+  RETURN_IF(check_align(X, 16, "X"));
+  RETURN_IF(check_align(q, 16, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(Y, 4, "Y"));
+  RETURN_IF(check_align(workspace, 256, "workspace"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{X, (uint64_t)T * K * 4, "X"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{Y, (uint64_t)T * N * 4, "Y"}, {workspace, L.bytes, "workspace"}};
+  RETURN_IF(check_alias(ins, 4, outs, 2));
+  char* ws = static_cast<char*>(workspace);
+  GemmArgs a{};
+  a.X = X;
+  a.s = scales;
+  a.z = zeros;
+  a.q = q;
+  a.Y = Y;
+  a.xs = reinterpret_cast<uint32_t*>(ws + L.xs_off);
+  a.fac = reinterpret_cast<float*>(ws + L.fac_off);
+  a.st = reinterpret_cast<float*>(ws + L.st_off);
+  a.zt = reinterpret_cast<uint32_t*>(ws + L.zt_off);
+  a.T = T;
+  a.N = N;
+  a.Tp = L.Tp;
+  a.Np = L.Np;
+  a.Gp = L.Gp;
+  a.RB = L.Tp / 128;
+  a.CB = L.Np / 128;
+  a.qbytes = (int64_t)(N * K / 2);
+  a.K = (int32_t)K;
+  a.Kp = (int32_t)L.Kp;
+  a.gs = group_size;
+  a.G = (int32_t)(K / group_size);
+  hipError_t e = launch_gemm(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -1,0 +1,349 @@
+// gemm.hip -- int4 group-quantized GEMM for prefill on the matrix cores:
+// Y[t][n] = sum_k X[t][k] * w[n][k] for T tokens at once ([P1] the prefill
+// path runs a tiled matmul for any M, decode the K-parallel matvec).  Unlike
+// the decode matvec this is a dense contraction with T-fold reuse of every
+// weight, so it is bound by the matrix cores, not by HBM.
+//
+// Operands of v_mfma_f32_16x16x32_f16 (lane l holds A[l%16][8(l/16)..+7],
+// B[8(l/16)..+7][l%16], D[4(l/16)..+3][l%16]):
+//  * B = (code - zero) as exact fp16 subnormals: the even nibbles of a code
+//    word masked in place (code * 2^-24), the odd ones four bits up
+//    (code * 2^-20), minus the zero point shifted the same way.  A word's
+//    eight slots hold inputs 0, 4, 1, 5, 2, 6, 3, 7 of its 8-input block.
+//  * A = the activations split into hi = fp16(y) and lo = fp16(y - hi) (both
+//    rounded toward zero; y - hi is exact in fp32), y = x * 2^e_t with the odd
+//    inputs also times 2^-4, in the slot order above; e_t per token puts the
+//    row's largest |x| just below 2^14.  hi + lo carries y to 2^-21 relative.
+//    A prep kernel writes this split once per call into the caller's
+//    workspace, so the GEMM's inner loop holds no conversions.
+//  * Two MFMAs per fragment pair (hi, lo) into one accumulator; the group's
+//    scale multiplies that accumulator into the total once per group, and
+//    the total is finally multiplied by 2^(24 - e_t).
+//
+// Tiling: a block of 4 waves computes a 128 x 128 tile of Y; wave (wr, wc)
+// owns rows 64 wr .. +63 and columns 64 wc .. +63 as 4 x 4 MFMA tiles.  K is
+// streamed in stages of 64 inputs through a double-buffered LDS ring (the
+// next stage's global loads are issued before the current stage's MFMAs).
+// Blocks are mapped so that each XCD works through consecutive tiles of one
+// row block: the row block's activations stay in that XCD's L2 while its
+// columns stream past.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "internal.h"
+
+namespace int4gemv {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kTile = 128;      // rows and columns of a block tile
+constexpr int kStageK = 64;     // inputs per LDS stage
+constexpr int kAStride = 68;    // dwords per activation row of a stage: 8 blocks x (4 hi + 4 lo) + 4 pad
+constexpr int kBStride = 10;    // dwords per weight column of a stage: 8 code words + 2 pad
+constexpr int kStageWords = kTile * kAStride + kTile * kBStride;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords
+
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
+__device__ __forceinline__ half2_t as_half2(uint32_t b) { return __builtin_bit_cast(half2_t, b); }
+__device__ __forceinline__ float pow2f(int e) { return bitsf((uint32_t)(e + 127) << 23); }
+
+// e for a token row whose largest magnitude is amax: amax * 2^e < 2^14.
+__device__ __forceinline__ int token_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int biased = (int)((fbits(amax) >> 23) & 0xFFu);
+  const int E = biased == 0 ? -126 : biased - 126;  // amax < 2^E
+  const int e = 14 - E;
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+// hi and lo of two binary32 values as fp16 pairs, both rounded toward zero.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  const half2_t l = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]));
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// ------------------------------------------------------------ prep
+
+// Blocks [0, Tp): the split activations of token row blockIdx.x (zeros for
+// the pad rows and the pad inputs).  Blocks [Tp, Tp + tiles): one 32 x 32
+// tile of the transposed scale table st[g][n] and zero-point table zt[g][n]
+// (zt holds zero | zero << 16, the fp16 subnormal pair), zeros outside
+// [0, G) x [0, N).
+__global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
+  __shared__ float red[4];
+  __shared__ uint32_t ts[32][33];
+  __shared__ uint32_t tz[32][33];
+  const int tid = threadIdx.x;
+  if ((int64_t)blockIdx.x < a.Tp) {
+    const int64_t m = blockIdx.x;
+    const bool real = m < a.T;
+    const float* x = a.X + m * (int64_t)a.K;
+    float amax = 0.0f;
+    if (real)
+      for (int i = tid; i < (a.K >> 2); i += 256) {
+        const float4 v = reinterpret_cast<const float4*>(x)[i];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int e = token_exponent(amax);
+    if (tid == 0) a.fac[m] = real ? pow2f(24 - e) : 0.0f;
+    const float fe = pow2f(e), fo = pow2f(e - 4);
+    u32x4* dst = reinterpret_cast<u32x4*>(a.xs + m * (int64_t)(a.Kp / 8) * 8);
+    for (int b = tid; b < a.Kp / 8; b += 256) {
+      uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
+      if (real && 8 * b < a.K) {
+        const float4 p = reinterpret_cast<const float4*>(x)[2 * b];
+        const float4 r = reinterpret_cast<const float4*>(x)[2 * b + 1];
+        // slots 0..7 = inputs 0, 4, 1, 5, 2, 6, 3, 7; odd inputs times 2^-4
+        split2(p.x * fe, r.x * fe, h[0], l[0]);
+        split2(p.y * fo, r.y * fo, h[1], l[1]);
+        split2(p.z * fe, r.z * fe, h[2], l[2]);
+        split2(p.w * fo, r.w * fo, h[3], l[3]);
+      }
+      dst[2 * b] = u32x4{h[0], h[1], h[2], h[3]};
+      dst[2 * b + 1] = u32x4{l[0], l[1], l[2], l[3]};
+    }
+    return;
+  }
+  // Transposed scale / zero-point tile.
+  const int64_t t = (int64_t)blockIdx.x - a.Tp;
+  const int64_t ntn = a.Np / 32;
+  const int64_t gt = t / ntn, nt = t - gt * ntn;
+  const int64_t g0 = gt * 32, nb0 = nt * 32;
+  const int c = tid & 31, r0 = tid >> 5;
+#pragma unroll
+  for (int r = r0; r < 32; r += 8) {
+    const int64_t n = nb0 + r, g = g0 + c;
+    uint32_t sv = 0u, zv = 0u;
+    if (n < a.N && g < a.G) {
+      sv = fbits(a.s[n * a.G + g]);
+      zv = (uint32_t)a.z[n * a.G + g] * 0x00010001u;
+    }
+    ts[r][c] = sv;
+    tz[r][c] = zv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = r0; r < 32; r += 8) {
+    const int64_t g = g0 + r, n = nb0 + c;
+    if (g < a.Gp) {
+      a.st[g * a.Np + n] = bitsf(ts[c][r]);
+      a.zt[g * a.Np + n] = tz[c][r];
+    }
+  }
+}
+
+// ------------------------------------------------------------ GEMM
+
+__global__ __launch_bounds__(256) void gemm_int4_kernel(GemmArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int l16 = lane & 15, q4 = lane >> 4;
+
+  // XCD-aware tile order: XCD x (= block id mod 8) takes a contiguous run of
+  // tiles, row block major.
+  const int64_t nb = a.RB * a.CB;
+  const int64_t b = blockIdx.x;
+  const int64_t x8 = b & 7, i8 = b >> 3, q8 = nb >> 3, r8 = nb & 7;
+  const int64_t tile = x8 * q8 + (x8 < r8 ? x8 : r8) + i8;
+  const int64_t rb = tile / a.CB, cb = tile - rb * a.CB;
+  const int64_t m0 = rb * kTile, n0 = cb * kTile;
+
+  // Global loads of a stage.  Activations: 128 rows x 256 bytes, thread t
+  // takes 16-byte pieces t + 256 i (16 threads per row, contiguous).  Codes:
+  // 128 columns x 32 bytes, thread t takes half t % 2 of column t / 2 through
+  // a buffer resource (columns past N and words past the matrix read 0).
+  const int64_t xrow = (int64_t)a.Kp / 8 * 8;  // dwords per token row
+  const uint32_t* xsb = a.xs + m0 * xrow;
+  const int bcol = tid >> 1, bhalf = tid & 1;
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.q, (short)0, (int)a.qbytes, kBufferWord3);
+  const uint32_t qcol_off = (uint32_t)(n0 + bcol) * (uint32_t)(a.K / 2);
+
+  u32x4 ra[8];
+  u32x4 rbw;
+  auto load_stage = [&](int st) {
+    const int64_t kw = (int64_t)st * (kStageK / 8) * 8;  // dword offset of the stage in a row
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 4, piece = c & 15;
+      ra[i] = *reinterpret_cast<const u32x4*>(xsb + row * xrow + kw + piece * 4);
+    }
+    const uint32_t off = qcol_off + (uint32_t)(st * (kStageK / 2) + bhalf * 16);
+    rbw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+  };
+  auto store_stage = [&](int buf) {
+    uint32_t* sa = lds + buf * kStageWords;
+    uint32_t* sb = sa + kTile * kAStride;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 4, piece = c & 15;
+      *reinterpret_cast<u32x4*>(sa + row * kAStride + piece * 4) = ra[i];
+    }
+    u32x2* pb = reinterpret_cast<u32x2*>(sb + bcol * kBStride + bhalf * 4);
+    pb[0] = u32x2{rbw[0], rbw[1]};
+    pb[1] = u32x2{rbw[2], rbw[3]};
+  };
+
+  // Scale and zero point of the lane's four columns for a 32-input step.
+  const float* stb = a.st + n0 + 64 * wc + l16;
+  const uint32_t* ztb = a.zt + n0 + 64 * wc + l16;
+  auto load_sz = [&](int kk, float (&s)[4], uint32_t (&z)[4]) {
+    const int64_t g = (int64_t)kk * 32 / a.gs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[j] = stb[g * a.Np + 16 * j];
+      z[j] = ztb[g * a.Np + 16 * j];
+    }
+  };
+
+  const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[4][4], tmp[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = z4;
+      tmp[i][j] = z4;
+    }
+
+  const int nst = a.Kp / kStageK;
+  const int nsteps = a.Kp / 32;
+  float sc[2][4];
+  uint32_t zc[2][4];
+  load_stage(0);
+  load_sz(0, sc[0], zc[0]);
+  load_sz(1, sc[1], zc[1]);
+  store_stage(0);
+  __syncthreads();
+
+  for (int st = 0; st < nst; ++st) {
+    const bool more = st + 1 < nst;
+    float sn[2][4];
+    uint32_t zn[2][4];
+    if (more) {
+      load_stage(st + 1);
+      load_sz(2 * st + 2, sn[0], zn[0]);
+      load_sz(2 * st + 3, sn[1], zn[1]);
+    }
+    const uint32_t* sa = lds + (st & 1) * kStageWords;
+    const uint32_t* sb = sa + kTile * kAStride;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kk = 2 * st + ks;
+      half8_t bf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = sb[(64 * wc + 16 * j + l16) * kBStride + ks * 4 + q4];
+        const uint32_t w8 = w >> 8;
+        const half2_t z0 = as_half2(zc[ks][j]), z1 = as_half2(zc[ks][j] << 4);
+        u32x4 bw;
+        bw[0] = __builtin_bit_cast(uint32_t, as_half2(w & 0x000F000Fu) - z0);
+        bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
+        bw[2] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x000F000Fu) - z0);
+        bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
+        bf[j] = __builtin_bit_cast(half8_t, bw);
+      }
+      u32x4 ah[4], al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t* pa = sa + (64 * wr + 16 * i + l16) * kAStride + (ks * 4 + q4) * 8;
+        ah[i] = *reinterpret_cast<const u32x4*>(pa);
+        al[i] = *reinterpret_cast<const u32x4*>(pa + 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[i]), bf[j],
+                                                             tmp[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[i]), bf[j],
+                                                             tmp[i][j], 0, 0, 0);
+      // A group ends after this step: its scale multiplies the group's sums.
+      if (((kk + 1) * 32) % a.gs == 0 || kk + 1 == nsteps) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc[ks][j], tmp[i][j][r], acc[i][j][r]);
+            tmp[i][j] = z4;
+          }
+      }
+    }
+    if (more) {
+      store_stage((st + 1) & 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[h][j] = sn[h][j];
+          zc[h][j] = zn[h][j];
+        }
+    }
+    __syncthreads();
+  }
+
+  // Y = total * 2^(24 - e_t); lane holds rows 4 (l/16) + r of each 16-row tile.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + 64 * wr + 16 * i + 4 * q4 + r;
+      if (row >= a.T) continue;
+      const float f = a.fac[row];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + 64 * wc + 16 * j + l16;
+        if (col < a.N) a.Y[row * a.N + col] = acc[i][j][r] * f;
+      }
+    }
+}
+
+}  // namespace
+
+size_t gemm_lds_bytes() { return (size_t)2 * kStageWords * sizeof(uint32_t); }
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+  // Dynamic LDS beyond 64 KiB must be allowed once per kernel.
+  static std::atomic<bool> raised{false};
+  const size_t lds = gemm_lds_bytes();
+  if (!raised.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_int4_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised.store(true, std::memory_order_release);
+  }
+  const int64_t prep_blocks = a.Tp + (a.Np / 32) * ((a.Gp + 31) / 32);
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_int4_kernel, dim3((unsigned)(a.RB * a.CB)), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace int4gemv

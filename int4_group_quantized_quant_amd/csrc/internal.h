@@ -122,12 +122,66 @@ hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& shape
 // Largest `ncol` instantiated for (mode, M, variant).
 int max_ncol(Mode mode, int M, int variant);
 
-// Quantize + pack launch: groups [0, total_groups), each gs consecutive floats.
+// ------------------------------------------------------------ prefill GEMM
+
+// Everything the prefill GEMM's two launches need.  The workspace (owned by
+// the caller) holds, in this order, each region 256-byte aligned:
+//   xs   [Tp][Kp] split activations: per 8-input block, 4 dwords of fp16 hi
+//        then 4 dwords of fp16 lo (slot order 0, 4, 1, 5, 2, 6, 3, 7)
+//   fac  [Tp] 2^(24 - e_t) per token row (0 for the pad rows)
+//   st   [Gp][Np] scales, transposed; zt [Gp][Np] zero points as fp16
+//        subnormal pairs (zero | zero << 16), transposed; 0 outside the matrix
+// with Tp, Np = T, N rounded up to 128, Kp = K rounded up to 64,
+// Gp = ceil(Kp / gs).
+struct GemmArgs {
+  const float* X;     // [T][K]
+  const float* s;     // [N][G]
+  const float* z;     // [N][G]
+  const uint32_t* q;  // [N][K/8]
+  float* Y;           // [T][N]
+  uint32_t* xs;
+  float* fac;
+  float* st;
+  uint32_t* zt;
+  int64_t T, N, Tp, Np, Gp, RB, CB;
+  int64_t qbytes;  // N * K / 2
+  int32_t K, Kp, gs, G;
+};
+
+struct GemmLayout {
+  int64_t Tp, Np, Kp, Gp;
+  size_t xs_off, fac_off, st_off, zt_off, bytes;
+};
+
+inline size_t gemm_align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline GemmLayout gemm_layout(int64_t T, int64_t N, int64_t K, int32_t gs) {
+  GemmLayout L;
+  L.Tp = (T + 127) / 128 * 128;
+  L.Np = (N + 127) / 128 * 128;
+  L.Kp = (K + 63) / 64 * 64;
+  L.Gp = (L.Kp + gs - 1) / gs;
+  L.xs_off = 0;
+  L.fac_off = gemm_align256(L.xs_off + (size_t)L.Tp * (size_t)L.Kp * 4);
+  L.st_off = gemm_align256(L.fac_off + (size_t)L.Tp * 4);
+  L.zt_off = gemm_align256(L.st_off + (size_t)L.Gp * (size_t)L.Np * 4);
+  L.bytes = gemm_align256(L.zt_off + (size_t)L.Gp * (size_t)L.Np * 4);
+  return L;
+}
+
+// Dynamic LDS of the GEMM kernel (two stages).
+size_t gemm_lds_bytes();
+
+// The prep launch (split activations, transposed scale / zero tables) and
+// the GEMM launch, in stream order.
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
 // Int4 embedding row gather: out [T][K] from rows ids[t] of the table.
 hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
                             const float* zeros, int64_t N, int32_t K, int32_t gs, float* out,
                             hipStream_t stream);
 
+// Quantize + pack launch: groups [0, total_groups), each gs consecutive floats.
 hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uint32_t* q,
                            float* scales, float* zeros, hipStream_t stream);
 

@@ -941,7 +941,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restr
 
 // ------------------------------------------------------------ matrix-core lanes kernel
 
-// Three to eight decode lanes on the matrix cores, v_mfma_f32_16x16x32_f16:
+// Two to eight decode lanes on the matrix cores, v_mfma_f32_16x16x32_f16:
 // D[i][col] = sum_k A[i][k] * B[k][col] over the 32 inputs of one unit.
 //  * B[k][col] = (code - zero) * 2^-24 for the even nibbles of a word and
 //    (code - zero) * 2^-20 for the odd ones: each nibble is masked in place

@@ -203,3 +203,27 @@ def test_embedding_gather_validation(lib):
     assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, gs, E + 4, None) == ALIGN
     assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, gs, B + 64, None) == ALIAS
     assert lib.int4_embedding_gather(A, 4, B, C, D, 16, K, gs, A - 16, None) == ALIAS
+
+
+def test_gemm_workspace_and_validation(lib):
+    lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.int4_gemm_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    T, N, K, gs = 5, 77, 96, 96
+    need = lib.int4_gemm_workspace_bytes(T, N, K, gs)
+    # Tp=128, Kp=128, Np=128, Gp=2: split activations 128*128*4, factors 128*4,
+    # two transposed tables 2*128*4 each, every region rounded up to 256 bytes.
+    assert need == 128 * 128 * 4 + 512 + 1024 + 1024
+    assert lib.int4_gemm_workspace_bytes(0, N, K, gs) == 0
+    W = 0x90000000
+    sz = ctypes.c_size_t
+    assert lib.int4_gemm(None, 0, None, None, None, N, K, gs, None, None, sz(0), None) == OK
+    assert lib.int4_gemm(A, T, B, C, D, N, K, 48, E, W, sz(need), None) == SHAPE
+    assert lib.int4_gemm(A, T, B, C, D, N, K, gs, E, W, sz(need - 1), None) == SHAPE
+    assert lib.int4_gemm(A, T, B, C, D, N, K, gs, E, None, sz(need), None) == NULL
+    assert lib.int4_gemm(A, T, B, C, D, N, K, gs, None, W, sz(need), None) == NULL
+    assert lib.int4_gemm(A, T, B, C, D, N, K, gs, E, W + 128, sz(need), None) == ALIGN
+    assert lib.int4_gemm(A + 4, T, B, C, D, N, K, gs, E, W, sz(need), None) == ALIGN
+    assert lib.int4_gemm(A, T, B, C, D, N, K, gs, E, A, sz(need), None) == ALIAS      # workspace over X
+    assert lib.int4_gemm(A, T, B, C, D, N, K, gs, W + 64, W, sz(need), None) == ALIAS  # Y inside workspace
+    assert lib.int4_gemm(A, T, B, C, D, 1 << 20, 1 << 12, 128, E, W, sz(1 << 40), None) == SHAPE  # N*K/2 >= 2^31
+    assert "2^31" in _err(lib)

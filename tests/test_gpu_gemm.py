@@ -1,0 +1,121 @@
+"""GPU parity of the prefill GEMM (int4_gemm) against the oracle's matvec of
+all T rows: ragged T, N and K (a pad half-stage when K % 64 == 32), group
+sizes 32 to 128 and 96, integer problems that must come out exact, rows of
+very different magnitudes, and the full workload size on sampled outputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_dot_close, integer_problem
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import torch
+    torch.cuda.set_device(0)
+    import int4_group_quantized_quant_amd as m
+    return m
+
+
+def to_dev(*arrs):
+    import torch
+    return [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrs]
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def quantized(seed, N, K, gs):
+    return oracle.quantize_pack(synth.weights(seed, N, K), gs)
+
+
+@pytest.mark.parametrize("T,N,K,gs", [
+    (1, 1, 32, 32), (5, 77, 96, 96), (130, 129, 160, 32), (64, 256, 4096, 128),
+    (200, 300, 2080, 32), (37, 300, 1056, 96), (257, 131, 512, 64),
+])
+def test_gemm(q4, T, N, K, gs):
+    q, s, z = quantized(0x6000 + T + N, N, K, gs)
+    X = synth.lanes(0x6001 + T, T, K)
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    Xd, qd, sd, zd = to_dev(X, q.view(np.int32), s, z)
+    Y = host(q4.int4_gemm(Xd, qd, sd, zd))
+    assert Y.shape == (T, N)
+    assert_dot_close(Y, Y_ref, B, f"gemm T={T} N={N} K={K} gs={gs}")
+
+
+def test_gemm_integer_exact(q4):
+    rng = np.random.default_rng(0x6100)
+    T, N, K, gs = 150, 200, 1024, 64
+    q, s, z, X, exact = integer_problem(rng, N, K, gs, M=T)
+    Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
+    np.testing.assert_array_equal(Y, exact.astype(np.float32))
+
+
+def test_gemm_row_scales_and_zero_rows(q4):
+    # Rows whose magnitudes differ by up to 2^200, an all-zero row, and rows
+    # with one huge entry among small ones: each row gets its own exponent.
+    N, K, gs = 96, 512, 128
+    q, s, z = quantized(0x6200, N, K, gs)
+    X = synth.lanes(0x6201, 8, K).astype(np.float64)
+    X[1] *= 1e30
+    X[2] *= 1e-30
+    X[3] = 0.0
+    X[4, 17] = 3e4
+    X[5] *= 1e-39  # binary32 subnormals
+    X = X.astype(np.float32)
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
+    assert_dot_close(Y, Y_ref, B, "gemm row scales")
+    np.testing.assert_array_equal(Y[3], np.zeros(N, np.float32))
+
+
+def test_gemm_matches_matvec_lanes_within_tolerance(q4):
+    # The same rows through the decode path (M <= 8) and the GEMM.
+    N, K, gs = 300, 2048, 64
+    q, s, z = quantized(0x6300, N, K, gs)
+    X = synth.lanes(0x6301, 8, K)
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    dev = to_dev(X, q.view(np.int32), s, z)
+    assert_dot_close(host(q4.int4_gemm(*dev)), Y_ref, B, "gemm")
+    assert_dot_close(host(q4.int4_matvec(*dev)), Y_ref, B, "matvec lanes")
+
+
+def test_gemm_workspace_reuse_and_empty(q4):
+    import torch
+    N, K, gs = 64, 256, 64
+    q, s, z = quantized(0x6400, N, K, gs)
+    qd, sd, zd = to_dev(q.view(np.int32), s, z)
+    ws = torch.empty(q4.int4_gemm_workspace_bytes(300, N, K, gs), dtype=torch.uint8, device="cuda")
+    for T in (300, 17):  # a larger call, then a smaller one in the same workspace
+        X = synth.lanes(0x6401 + T, T, K)
+        Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+        Y = host(q4.int4_gemm(to_dev(X)[0], qd, sd, zd, workspace=ws))
+        assert_dot_close(Y, Y_ref, B, f"gemm T={T} reused workspace")
+    X0 = torch.empty((0, K), device="cuda")
+    assert q4.int4_gemm(X0, qd, sd, zd).shape == (0, N)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(q4.Int4Error):
+        q4.int4_gemm(to_dev(synth.lanes(1, 4, K))[0], qd, sd, zd, workspace=small)
+
+
+def test_prefill_full_size_sampled(q4):
+    import torch
+    c = synth.NEXT["n6"]
+    inp = synth.n6_inputs()
+    T, N, K, gs = c["T"], c["N"], c["K"], c["gs"]
+    rng = np.random.default_rng(0x66)
+    cols = np.array(sorted(set(rng.choice(N, 256, replace=False).tolist()) | {0, N - 1}))
+    rows = np.array(sorted(set(rng.choice(T, 12, replace=False).tolist()) | {0, T - 1}))
+    qd, sd, zd = q4.int4_quantize_pack(torch.from_numpy(inp["W"]).cuda(), gs)
+    q, s, z = oracle.quantize_pack(inp["W"][cols], gs)
+    idx = torch.from_numpy(cols).cuda()
+    np.testing.assert_array_equal(host(qd[idx]).view(np.uint32), q)
+    Y = host(q4.int4_gemm(torch.from_numpy(inp["X"]).cuda(), qd, sd, zd))
+    Y_ref, B = oracle.matvec(inp["X"][rows], q, s, z, K, gs)
+    assert_dot_close(Y[np.ix_(rows, cols)], Y_ref, B, "prefill full size")
