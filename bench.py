@@ -22,6 +22,8 @@ way and reported under "next_rows"; they are not part of the step:
   normswi  silu(x . Wg) * (x . Wu), x = RMSNorm(a_a + a_b) * w_norm, [14336, 4096] (gs 128)
   embed    rows ids[T] of an int4 table [151936, 4096] dequantized, T = 1 and 4096 (gs 128);
            bytes = ids + the T rows' codes, scales and zeros + the fp32 output
+  prefill  X[512, 4096] . W[4096, 4096]^T (gs 128) on the matrix cores; reported as
+           useful TFLOP/s (2 T N K flops per call, prep launch included)
 
 Per-call durations: each call is also timed alone, in a graph of back-to-back
 calls cycling over >= 1 GiB of device copies of its buffers, with HIP events
@@ -52,6 +54,7 @@ import synth  # noqa: E402
 
 METRIC = "int4 GEMV µs/call + effective HBM GB/s (% of MI355X peak), 1 GPU"
 PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 MALL_ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "norm_lmhead_151936x4096_traffic.md")
 KERNEL_SRC = os.path.join(ROOT, "int4_group_quantized_quant_amd", "csrc", "kernels.hip")
@@ -265,6 +268,19 @@ def build_next(q4, torch, dev):
         calls.append(Call(f"embedding T={T} {n5['N']}x{n5['K']}", b5,
                           lambda s, ids=ids, out=out: q4.int4_embedding_gather(ids, *s, out=out),
                           lambda r: clones(w5, r), wbytes(w5)))
+
+    i6 = synth.n6_inputs()
+    n6 = synth.NEXT["n6"]
+    w6 = quantize(i6["W"], n6["gs"])
+    X6 = torch.from_numpy(i6["X"]).to(dev)
+    Y6 = torch.empty((n6["T"], n6["N"]), device=dev)
+    ws6 = torch.empty(q4.int4_gemm_workspace_bytes(n6["T"], n6["N"], n6["K"], n6["gs"]),
+                      dtype=torch.uint8, device=dev)
+    b6 = alg_bytes(n6["N"], n6["K"], n6["gs"], n6["T"] * n6["K"], n6["T"] * n6["N"])
+    c6 = Call(f"prefill GEMM T={n6['T']} {n6['N']}x{n6['K']}", b6,
+              lambda s: q4.int4_gemm(X6, *s, Y=Y6, workspace=ws6), lambda r: clones(w6, r), wbytes(w6))
+    c6.flops = 2 * n6["T"] * n6["N"] * n6["K"]
+    calls.append(c6)
     return calls
 
 
@@ -437,6 +453,14 @@ def main():
         next_rows[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
                              "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
                              "alg_bytes": c.nbytes, "rotating_copies": r}
+        flops = getattr(c, "flops", None)
+        if flops:
+            tf = flops / us / 1e6
+            next_rows[c.name].update({"alg_flops": flops, "TFLOPs": round(tf, 1),
+                                      "pct_fp16_mfma_peak": round(100 * tf / PEAK_FP16_TFLOPS, 1)})
+            log(f"{c.name:28s} {us:9.2f} us  {tf:8.1f} TFLOP/s ({100 * tf / PEAK_FP16_TFLOPS:5.1f}% of "
+                f"the 2.5 PFLOP/s fp16 matrix peak; two fp16 products per term)  [next row]")
+            continue
         log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
             f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)  [next row, not in the step]")
         del c

@@ -720,6 +720,10 @@ int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales,
   a.Kp = (int32_t)L.Kp;
   a.gs = group_size;
   a.G = (int32_t)(K / group_size);
+  // Split K in two when the 128 x 128 tiles alone would leave CUs idle.
+  DeviceInfo dev;
+  RETURN_IF(device_info(&dev));
+  a.S = (a.RB * a.CB < dev.cus && L.Kp / 64 >= 2) ? 2 : 1;
   hipError_t e = launch_gemm(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();

@@ -20,13 +20,16 @@
 //    scale multiplies that accumulator into the total once per group, and
 //    the total is finally multiplied by 2^(24 - e_t).
 //
-// Tiling: a block of 4 waves computes a 128 x 128 tile of Y; wave (wr, wc)
-// owns rows 64 wr .. +63 and columns 64 wc .. +63 as 4 x 4 MFMA tiles.  K is
-// streamed in stages of 64 inputs through a double-buffered LDS ring (the
-// next stage's global loads are issued before the current stage's MFMAs).
-// Blocks are mapped so that each XCD works through consecutive tiles of one
-// row block: the row block's activations stay in that XCD's L2 while its
-// columns stream past.
+// Tiling: a block of 8 waves (two per SIMD) computes a 128 x 128 tile of Y;
+// wave (wr, wc) owns rows 32 wr .. +31 and columns 64 wc .. +63 as 2 x 4
+// MFMA tiles.  K is streamed in stages of 64 inputs (activations, code
+// words, and the stage's scales and zero points) through two LDS slots; the
+// global loads run two stages ahead in two register sets.  When the tiles
+// alone would not fill the CUs, K is split in two and both halves are added
+// into Y (zeroed by the prep launch): a + b is order-independent, so the
+// result stays deterministic.  Blocks are mapped so that each XCD works
+// through consecutive work items of one row block: the row block's
+// activations stay in that XCD's L2 while its columns stream past.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,7 +51,9 @@ constexpr int kTile = 128;      // rows and columns of a block tile
 constexpr int kStageK = 64;     // inputs per LDS stage
 constexpr int kAStride = 68;    // dwords per activation row of a stage: 8 blocks x (4 hi + 4 lo) + 4 pad
 constexpr int kBStride = 10;    // dwords per weight column of a stage: 8 code words + 2 pad
-constexpr int kStageWords = kTile * kAStride + kTile * kBStride;
+constexpr int kSZWords = 512;   // scales then zero points, 2 steps x 128 columns each
+constexpr int kStageWords = kTile * kAStride + kTile * kBStride + kSZWords;
+constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords
 
 __device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
@@ -102,6 +107,8 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const int e = token_exponent(amax);
     if (tid == 0) a.fac[m] = real ? pow2f(24 - e) : 0.0f;
+    if (real && a.S > 1)  // the GEMM adds its K parts into Y
+      for (int64_t n = tid; n < a.N; n += 256) a.Y[m * a.N + n] = 0.0f;
     const float fe = pow2f(e), fo = pow2f(e - 4);
     u32x4* dst = reinterpret_cast<u32x4*>(a.xs + m * (int64_t)(a.Kp / 8) * 8);
     for (int b = tid; b < a.Kp / 8; b += 256) {
@@ -150,113 +157,112 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------ GEMM
 
-__global__ __launch_bounds__(256) void gemm_int4_kernel(GemmArgs a) {
+struct Prefetch {
+  u32x4 a[4];  // activation pieces c = tid + 512 i
+  u32x4 b;     // code words (threads 0..255)
+  uint32_t sz; // one scale or zero-point dword
+};
+
+__global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   extern __shared__ uint32_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int wr = wave & 1, wc = wave >> 1;
+  const int wr = wave & 3, wc = wave >> 2;  // rows 32 wr .. +31, columns 64 wc .. +63
   const int l16 = lane & 15, q4 = lane >> 4;
 
-  // XCD-aware tile order: XCD x (= block id mod 8) takes a contiguous run of
-  // tiles, row block major.
-  const int64_t nb = a.RB * a.CB;
+  // XCD-aware order: XCD x (= block id mod 8) takes a contiguous run of
+  // work items; items are row block major, then column block, then K part.
+  const int64_t nb = a.RB * a.CB * a.S;
   const int64_t b = blockIdx.x;
   const int64_t x8 = b & 7, i8 = b >> 3, q8 = nb >> 3, r8 = nb & 7;
-  const int64_t tile = x8 * q8 + (x8 < r8 ? x8 : r8) + i8;
-  const int64_t rb = tile / a.CB, cb = tile - rb * a.CB;
+  const int64_t item = x8 * q8 + (x8 < r8 ? x8 : r8) + i8;
+  const int64_t rb = item / (a.CB * a.S);
+  const int64_t rem = item - rb * a.CB * a.S;
+  const int64_t cb = rem / a.S;
+  const int part = (int)(rem - cb * a.S);
   const int64_t m0 = rb * kTile, n0 = cb * kTile;
+  const int nst_all = a.Kp / kStageK;
+  const int per = (nst_all + a.S - 1) / a.S;
+  const int st_begin = part * per;
+  const int st_end = st_begin + per < nst_all ? st_begin + per : nst_all;
+  if (st_begin >= st_end) return;  // an empty K part adds nothing (Y starts at 0)
+  const int nsteps = a.Kp / 32;
+  const int last_step = 2 * st_end - 1;
 
-  // Global loads of a stage.  Activations: 128 rows x 256 bytes, thread t
-  // takes 16-byte pieces t + 256 i (16 threads per row, contiguous).  Codes:
-  // 128 columns x 32 bytes, thread t takes half t % 2 of column t / 2 through
-  // a buffer resource (columns past N and words past the matrix read 0).
-  const int64_t xrow = (int64_t)a.Kp / 8 * 8;  // dwords per token row
+  // Stage loads.  Activations: 128 rows x 256 bytes, thread t takes the
+  // 16-byte pieces t + 512 i (16 threads per row).  Codes: 128 columns x 32
+  // bytes, thread t < 256 takes half t % 2 of column t / 2 through a buffer
+  // resource (columns past N and words past the matrix read 0).  Scales and
+  // zero points: thread t loads kind t / 256 (scale, zero) of step t / 128 % 2
+  // for column t % 128 from the transposed tables.
+  const int64_t xrow = a.Kp;  // dwords per token row
   const uint32_t* xsb = a.xs + m0 * xrow;
-  const int bcol = tid >> 1, bhalf = tid & 1;
+  const int bcol = (tid >> 1) & 127, bhalf = tid & 1;
   const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.q, (short)0, (int)a.qbytes, kBufferWord3);
   const uint32_t qcol_off = (uint32_t)(n0 + bcol) * (uint32_t)(a.K / 2);
+  const int szkind = tid >> 8, szstep = (tid >> 7) & 1, szcol = tid & 127;
+  const uint32_t* sztab = szkind ? a.zt : reinterpret_cast<const uint32_t*>(a.st);
 
-  u32x4 ra[8];
-  u32x4 rbw;
-  auto load_stage = [&](int st) {
-    const int64_t kw = (int64_t)st * (kStageK / 8) * 8;  // dword offset of the stage in a row
+  auto load_stage = [&](int st, Prefetch& p) {
+    const int64_t kw = (int64_t)st * (kStageK / 8) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
       const int row = c >> 4, piece = c & 15;
-      ra[i] = *reinterpret_cast<const u32x4*>(xsb + row * xrow + kw + piece * 4);
+      p.a[i] = *reinterpret_cast<const u32x4*>(xsb + row * xrow + kw + piece * 4);
     }
+    // Every thread loads (threads t and t + 256 the same piece) so that the
+    // count of loads in flight is fixed and every wait is exact.
     const uint32_t off = qcol_off + (uint32_t)(st * (kStageK / 2) + bhalf * 16);
-    rbw = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+    p.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+    const int64_t g = (int64_t)(2 * st + szstep) * 32 / a.gs;
+    p.sz = sztab[g * a.Np + n0 + szcol];
   };
-  auto store_stage = [&](int buf) {
-    uint32_t* sa = lds + buf * kStageWords;
+  auto store_stage = [&](int slot, const Prefetch& p) {
+    uint32_t* sa = lds + slot * kStageWords;
     uint32_t* sb = sa + kTile * kAStride;
+    uint32_t* ssz = sb + kTile * kBStride;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
       const int row = c >> 4, piece = c & 15;
-      *reinterpret_cast<u32x4*>(sa + row * kAStride + piece * 4) = ra[i];
+      *reinterpret_cast<u32x4*>(sa + row * kAStride + piece * 4) = p.a[i];
     }
-    u32x2* pb = reinterpret_cast<u32x2*>(sb + bcol * kBStride + bhalf * 4);
-    pb[0] = u32x2{rbw[0], rbw[1]};
-    pb[1] = u32x2{rbw[2], rbw[3]};
-  };
-
-  // Scale and zero point of the lane's four columns for a 32-input step.
-  const float* stb = a.st + n0 + 64 * wc + l16;
-  const uint32_t* ztb = a.zt + n0 + 64 * wc + l16;
-  auto load_sz = [&](int kk, float (&s)[4], uint32_t (&z)[4]) {
-    const int64_t g = (int64_t)kk * 32 / a.gs;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[j] = stb[g * a.Np + 16 * j];
-      z[j] = ztb[g * a.Np + 16 * j];
+    if (tid < 256) {
+      u32x2* pb = reinterpret_cast<u32x2*>(sb + bcol * kBStride + bhalf * 4);
+      pb[0] = u32x2{p.b[0], p.b[1]};
+      pb[1] = u32x2{p.b[2], p.b[3]};
     }
+    ssz[tid] = p.sz;
   };
 
   const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t acc[4][4], tmp[4][4];
+  f32x4_t acc[2][4], tmp[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[i][j] = z4;
       tmp[i][j] = z4;
     }
 
-  const int nst = a.Kp / kStageK;
-  const int nsteps = a.Kp / 32;
-  float sc[2][4];
-  uint32_t zc[2][4];
-  load_stage(0);
-  load_sz(0, sc[0], zc[0]);
-  load_sz(1, sc[1], zc[1]);
-  store_stage(0);
-  __syncthreads();
-
-  for (int st = 0; st < nst; ++st) {
-    const bool more = st + 1 < nst;
-    float sn[2][4];
-    uint32_t zn[2][4];
-    if (more) {
-      load_stage(st + 1);
-      load_sz(2 * st + 2, sn[0], zn[0]);
-      load_sz(2 * st + 3, sn[1], zn[1]);
-    }
-    const uint32_t* sa = lds + (st & 1) * kStageWords;
+  auto compute = [&](int slot, int st) {
+    const uint32_t* sa = lds + slot * kStageWords;
     const uint32_t* sb = sa + kTile * kAStride;
+    const uint32_t* ssz = sb + kTile * kBStride;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int kk = 2 * st + ks;
       half8_t bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = sb[(64 * wc + 16 * j + l16) * kBStride + ks * 4 + q4];
+        const int col = 64 * wc + 16 * j + l16;
+        const uint32_t w = sb[col * kBStride + ks * 4 + q4];
+        const uint32_t zh = ssz[256 + ks * 128 + col];
         const uint32_t w8 = w >> 8;
-        const half2_t z0 = as_half2(zc[ks][j]), z1 = as_half2(zc[ks][j] << 4);
+        const half2_t z0 = as_half2(zh), z1 = as_half2(zh << 4);
         u32x4 bw;
         bw[0] = __builtin_bit_cast(uint32_t, as_half2(w & 0x000F000Fu) - z0);
         bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
@@ -264,62 +270,82 @@ __global__ __launch_bounds__(256) void gemm_int4_kernel(GemmArgs a) {
         bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
         bf[j] = __builtin_bit_cast(half8_t, bw);
       }
-      u32x4 ah[4], al[4];
+      u32x4 ah[2], al[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t* pa = sa + (64 * wr + 16 * i + l16) * kAStride + (ks * 4 + q4) * 8;
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t* pa = sa + (32 * wr + 16 * i + l16) * kAStride + (ks * 4 + q4) * 8;
         ah[i] = *reinterpret_cast<const u32x4*>(pa);
         al[i] = *reinterpret_cast<const u32x4*>(pa + 4);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[i]), bf[j],
                                                              tmp[i][j], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[i]), bf[j],
                                                              tmp[i][j], 0, 0, 0);
-      // A group ends after this step: its scale multiplies the group's sums.
-      if (((kk + 1) * 32) % a.gs == 0 || kk + 1 == nsteps) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc[ks][j], tmp[i][j][r], acc[i][j][r]);
-            tmp[i][j] = z4;
-          }
-      }
-    }
-    if (more) {
-      store_stage((st + 1) & 1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
+      // A group (or this block's K part) ends after this step: its scale
+      // multiplies the sums into the total.
+      if (((kk + 1) * 32) % a.gs == 0 || kk + 1 == nsteps || kk == last_step) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          sc[h][j] = sn[h][j];
-          zc[h][j] = zn[h][j];
+          const float sc = bitsf(ssz[ks * 128 + 64 * wc + 16 * j + l16]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, tmp[i][j][r], acc[i][j][r]);
+            tmp[i][j] = z4;
+          }
         }
+      }
     }
+  };
+
+  // Two register prefetch sets: the loads of stage st + 2 are issued while
+  // stage st is computed, and stage st + 1 (loaded one iteration earlier)
+  // is written to the other LDS slot after it.  Loads are unconditional
+  // (past the part's last stage they re-read it), so the wait before each
+  // LDS write covers exactly the older set.
+  auto clamp = [&](int x) { return x < st_end ? x : st_end - 1; };
+  Prefetch p0, p1;
+  load_stage(st_begin, p0);
+  load_stage(clamp(st_begin + 1), p1);
+  store_stage(0, p0);
+  __syncthreads();
+  int st = st_begin;
+  while (true) {
+    load_stage(clamp(st + 2), p0);
+    compute(0, st);
+    store_stage(1, p1);
     __syncthreads();
+    if (++st >= st_end) break;
+    load_stage(clamp(st + 2), p1);
+    compute(1, st);
+    store_stage(0, p0);
+    __syncthreads();
+    if (++st >= st_end) break;
   }
 
-  // Y = total * 2^(24 - e_t); lane holds rows 4 (l/16) + r of each 16-row tile.
+  // Y = total * 2^(24 - e_t); with K split in two, the two halves are added
+  // into Y (zeroed by the prep launch), an order-independent sum.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + 64 * wr + 16 * i + 4 * q4 + r;
+      const int64_t row = m0 + 32 * wr + 16 * i + 4 * q4 + r;
       if (row >= a.T) continue;
       const float f = a.fac[row];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = n0 + 64 * wc + 16 * j + l16;
-        if (col < a.N) a.Y[row * a.N + col] = acc[i][j][r] * f;
+        if (col >= a.N) continue;
+        if (a.S == 1) a.Y[row * a.N + col] = acc[i][j][r] * f;
+        else unsafeAtomicAdd(a.Y + row * a.N + col, acc[i][j][r] * f);
       }
     }
 }
@@ -342,7 +368,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_int4_kernel, dim3((unsigned)(a.RB * a.CB)), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(gemm_int4_kernel, dim3((unsigned)(a.RB * a.CB * a.S)), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

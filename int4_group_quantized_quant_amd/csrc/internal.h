@@ -146,6 +146,7 @@ struct GemmArgs {
   int64_t T, N, Tp, Np, Gp, RB, CB;
   int64_t qbytes;  // N * K / 2
   int32_t K, Kp, gs, G;
+  int32_t S;  // K parts per tile (1 or 2)
 };
 
 struct GemmLayout {
