@@ -49,10 +49,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kTile = 128;      // rows and columns of a block tile
 constexpr int kStageK = 64;     // inputs per LDS stage
-constexpr int kAStride = 68;    // dwords per activation row of a stage: 8 blocks x (4 hi + 4 lo) + 4 pad
-constexpr int kBStride = 10;    // dwords per weight column of a stage: 8 code words + 2 pad
-constexpr int kSZWords = 512;   // scales then zero points, 2 steps x 128 columns each
-constexpr int kStageWords = kTile * kAStride + kTile * kBStride + kSZWords;
+// LDS stage layout: planes of 128 rows (or columns) x 16 bytes, plane stride
+// 516 dwords (4 pad).  A fragment read (16 consecutive rows of one plane per
+// quarter-wave) is contiguous; a plane-crossing write of 8 lanes lands on
+// 8 distinct bank quads.
+constexpr int kPlane = kTile * 4 + 4;
+constexpr int kAPlanes = 16;    // 8-input block b of the stage: plane 2b (hi), 2b + 1 (lo)
+constexpr int kBPlanes = 8;     // B fragment of code word w of the stage: plane w
+constexpr int kSCWords = 256;   // scales, 2 steps x 128 columns
+constexpr int kAWords = kAPlanes * kPlane;
+constexpr int kBWords = kBPlanes * kPlane;
+constexpr int kStageWords = kAWords + kBWords + kSCWords;
 constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords
 
@@ -158,11 +165,15 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
 // ------------------------------------------------------------ GEMM
 
 struct Prefetch {
-  u32x4 a[4];  // activation pieces c = tid + 512 i
-  u32x4 b;     // code words (threads 0..255)
-  uint32_t sz; // one scale or zero-point dword
+  u32x4 a[4];   // activation pieces c = tid + 512 i
+  u32x2 w;      // code words 2 (t % 4) .. +1 of column t / 4
+  uint32_t zh;  // zero point pair of that column for the words' step
+  uint32_t sc;  // scale of column t % 128 for step (t / 128) % 2 (used by t < 256)
 };
 
+// GSTEPS = group size / 32 when it is 1, 2 or 4 (group ends known at
+// compile time), 0 for any other group size.
+template <int GSTEPS>
 __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   extern __shared__ uint32_t lds[];
   const int tid = threadIdx.x;
@@ -183,27 +194,35 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   const int part = (int)(rem - cb * a.S);
   const int64_t m0 = rb * kTile, n0 = cb * kTile;
   const int nst_all = a.Kp / kStageK;
-  const int per = (nst_all + a.S - 1) / a.S;
+  // K parts cover whole groups when the group spans two stages.
+  int per = (nst_all + a.S - 1) / a.S;
+  if (GSTEPS == 4) per = (per + 1) & ~1;
   const int st_begin = part * per;
   const int st_end = st_begin + per < nst_all ? st_begin + per : nst_all;
   if (st_begin >= st_end) return;  // an empty K part adds nothing (Y starts at 0)
   const int nsteps = a.Kp / 32;
   const int last_step = 2 * st_end - 1;
+  const int gsteps = a.gs / 32;
 
-  // Stage loads.  Activations: 128 rows x 256 bytes, thread t takes the
-  // 16-byte pieces t + 512 i (16 threads per row).  Codes: 128 columns x 32
-  // bytes, thread t < 256 takes half t % 2 of column t / 2 through a buffer
-  // resource (columns past N and words past the matrix read 0).  Scales and
-  // zero points: thread t loads kind t / 256 (scale, zero) of step t / 128 % 2
-  // for column t % 128 from the transposed tables.
+  // Stage loads (all unconditional, so every wait is exact).  Activations:
+  // 128 rows x 256 bytes, thread t takes the 16-byte pieces t + 512 i.
+  // Codes: thread t takes words 2 (t % 4), +1 of column t / 4 through a
+  // buffer resource (columns past N and words past the matrix read 0), and
+  // that column's zero point for the words' step.  Scales: thread t takes
+  // column t % 128 of step (t / 128) % 2.
   const int64_t xrow = a.Kp;  // dwords per token row
   const uint32_t* xsb = a.xs + m0 * xrow;
-  const int bcol = (tid >> 1) & 127, bhalf = tid & 1;
+  const int wcol = tid >> 2, wpair = tid & 3, wstep = wpair >> 1;
   const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.q, (short)0, (int)a.qbytes, kBufferWord3);
-  const uint32_t qcol_off = (uint32_t)(n0 + bcol) * (uint32_t)(a.K / 2);
-  const int szkind = tid >> 8, szstep = (tid >> 7) & 1, szcol = tid & 127;
-  const uint32_t* sztab = szkind ? a.zt : reinterpret_cast<const uint32_t*>(a.st);
+  const uint32_t qcol_off = (uint32_t)(n0 + wcol) * (uint32_t)(a.K / 2) + (uint32_t)wpair * 8u;
+  const int scstep = (tid >> 7) & 1, sccol = tid & 127;
+  auto group_of = [&](int kk) -> int64_t {
+    if constexpr (GSTEPS == 1) return kk;
+    else if constexpr (GSTEPS == 2) return kk >> 1;
+    else if constexpr (GSTEPS == 4) return kk >> 2;
+    else return kk / gsteps;
+  };
 
   auto load_stage = [&](int st, Prefetch& p) {
     const int64_t kw = (int64_t)st * (kStageK / 8) * 8;
@@ -213,29 +232,36 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
       const int row = c >> 4, piece = c & 15;
       p.a[i] = *reinterpret_cast<const u32x4*>(xsb + row * xrow + kw + piece * 4);
     }
-    // Every thread loads (threads t and t + 256 the same piece) so that the
-    // count of loads in flight is fixed and every wait is exact.
-    const uint32_t off = qcol_off + (uint32_t)(st * (kStageK / 2) + bhalf * 16);
-    p.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
-    const int64_t g = (int64_t)(2 * st + szstep) * 32 / a.gs;
-    p.sz = sztab[g * a.Np + n0 + szcol];
+    p.w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                        qr, qcol_off + (uint32_t)(st * (kStageK / 2)), 0, 0));
+    p.zh = a.zt[group_of(2 * st + wstep) * a.Np + n0 + wcol];
+    p.sc = __builtin_bit_cast(uint32_t, a.st[group_of(2 * st + scstep) * a.Np + n0 + sccol]);
   };
+  // LDS stage: activation planes (piece p of a row's 256 bytes is plane p),
+  // B fragment planes (fragment of step ks, lane group q: plane 4 ks + q),
+  // scales [2 steps][128 columns].
   auto store_stage = [&](int slot, const Prefetch& p) {
     uint32_t* sa = lds + slot * kStageWords;
-    uint32_t* sb = sa + kTile * kAStride;
-    uint32_t* ssz = sb + kTile * kBStride;
+    uint32_t* sb = sa + kAWords;
+    uint32_t* ss = sb + kBWords;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + kThreads * i;
       const int row = c >> 4, piece = c & 15;
-      *reinterpret_cast<u32x4*>(sa + row * kAStride + piece * 4) = p.a[i];
+      *reinterpret_cast<u32x4*>(sa + piece * kPlane + row * 4) = p.a[i];
     }
-    if (tid < 256) {
-      u32x2* pb = reinterpret_cast<u32x2*>(sb + bcol * kBStride + bhalf * 4);
-      pb[0] = u32x2{p.b[0], p.b[1]};
-      pb[1] = u32x2{p.b[2], p.b[3]};
+    const half2_t z0 = as_half2(p.zh), z1 = as_half2(p.zh << 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w = p.w[h], w8 = w >> 8;
+      u32x4 bw;
+      bw[0] = __builtin_bit_cast(uint32_t, as_half2(w & 0x000F000Fu) - z0);
+      bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
+      bw[2] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x000F000Fu) - z0);
+      bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
+      *reinterpret_cast<u32x4*>(sb + (2 * wpair + h) * kPlane + wcol * 4) = bw;
     }
-    ssz[tid] = p.sz;
+    if (tid < 256) ss[tid] = p.sc;
   };
 
   const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
@@ -248,69 +274,89 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
       tmp[i][j] = z4;
     }
 
-  auto compute = [&](int slot, int st) {
-    const uint32_t* sa = lds + slot * kStageWords;
-    const uint32_t* sb = sa + kTile * kAStride;
-    const uint32_t* ssz = sb + kTile * kBStride;
+  // One 32-input step: FIRST = the step opens a group (the products start
+  // from 0), LAST = it closes one (its scale multiplies the sums into acc).
+  auto step = [&](const uint32_t* sa, const uint32_t* sb, const uint32_t* ss, int ks, bool first,
+                  bool last) {
+    u32x4 bf[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = 2 * st + ks;
-      half8_t bf[4];
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *reinterpret_cast<const u32x4*>(sb + (ks * 4 + q4) * kPlane + (64 * wc + 16 * j + l16) * 4);
+    u32x4 ah[2], al[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t* pa = sa + 2 * (ks * 4 + q4) * kPlane + (32 * wr + 16 * i + l16) * 4;
+      ah[i] = *reinterpret_cast<const u32x4*>(pa);
+      al[i] = *reinterpret_cast<const u32x4*>(pa + kPlane);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[i]),
+                                                           __builtin_bit_cast(half8_t, bf[j]),
+                                                           first ? z4 : tmp[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[i]),
+                                                           __builtin_bit_cast(half8_t, bf[j]),
+                                                           tmp[i][j], 0, 0, 0);
+    if (last) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int col = 64 * wc + 16 * j + l16;
-        const uint32_t w = sb[col * kBStride + ks * 4 + q4];
-        const uint32_t zh = ssz[256 + ks * 128 + col];
-        const uint32_t w8 = w >> 8;
-        const half2_t z0 = as_half2(zh), z1 = as_half2(zh << 4);
-        u32x4 bw;
-        bw[0] = __builtin_bit_cast(uint32_t, as_half2(w & 0x000F000Fu) - z0);
-        bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
-        bw[2] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x000F000Fu) - z0);
-        bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
-        bf[j] = __builtin_bit_cast(half8_t, bw);
+        const float sc = bitsf(ss[ks * 128 + 64 * wc + 16 * j + l16]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, tmp[i][j][r], acc[i][j][r]);
       }
-      u32x4 ah[2], al[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t* pa = sa + (32 * wr + 16 * i + l16) * kAStride + (ks * 4 + q4) * 8;
-        ah[i] = *reinterpret_cast<const u32x4*>(pa);
-        al[i] = *reinterpret_cast<const u32x4*>(pa + 4);
+    }
+  };
+  // A stage is two steps.  For GSTEPS 1 and 2 the group ends are fixed per
+  // step; GSTEPS 4 spans a stage pair (PHASE: the stage's place in it); the
+  // general case tests the step index, and every case closes the sums at
+  // the part's last step.
+  auto compute = [&](int slot, int st, int phase) {
+    const uint32_t* sa = lds + slot * kStageWords;
+    const uint32_t* sb = sa + kAWords;
+    const uint32_t* ss = sb + kBWords;
+    const int kk = 2 * st;
+    const bool end_part = kk + 1 == last_step;
+    if constexpr (GSTEPS == 1) {
+      step(sa, sb, ss, 0, true, true);
+      step(sa, sb, ss, 1, true, true);
+    } else if constexpr (GSTEPS == 2) {
+      step(sa, sb, ss, 0, true, false);
+      step(sa, sb, ss, 1, false, true);
+    } else if constexpr (GSTEPS == 4) {
+      if (phase == 0) {
+        step(sa, sb, ss, 0, true, false);
+        if (end_part) step(sa, sb, ss, 1, false, true);
+        else step(sa, sb, ss, 1, false, false);
+      } else {
+        step(sa, sb, ss, 0, false, false);
+        step(sa, sb, ss, 1, false, true);
       }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[i]), bf[j],
-                                                             tmp[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[i]), bf[j],
-                                                             tmp[i][j], 0, 0, 0);
-      // A group (or this block's K part) ends after this step: its scale
-      // multiplies the sums into the total.
-      if (((kk + 1) * 32) % a.gs == 0 || kk + 1 == nsteps || kk == last_step) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float sc = bitsf(ssz[ks * 128 + 64 * wc + 16 * j + l16]);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, tmp[i][j][r], acc[i][j][r]);
-            tmp[i][j] = z4;
-          }
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k = kk + ks;
+        const bool first = k % gsteps == 0 || k == 2 * st_begin;
+        const bool last = (k + 1) % gsteps == 0 || k + 1 == nsteps || k == last_step;
+        if (first && last) step(sa, sb, ss, ks, true, true);
+        else if (first) step(sa, sb, ss, ks, true, false);
+        else if (last) step(sa, sb, ss, ks, false, true);
+        else step(sa, sb, ss, ks, false, false);
       }
     }
   };
 
   // Two register prefetch sets: the loads of stage st + 2 are issued while
   // stage st is computed, and stage st + 1 (loaded one iteration earlier)
-  // is written to the other LDS slot after it.  Loads are unconditional
-  // (past the part's last stage they re-read it), so the wait before each
-  // LDS write covers exactly the older set.
+  // is written to the other LDS slot after it.  Past the part's last stage
+  // the loads re-read it, so the count in flight is fixed.
   auto clamp = [&](int x) { return x < st_end ? x : st_end - 1; };
   Prefetch p0, p1;
   load_stage(st_begin, p0);
@@ -320,12 +366,12 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   int st = st_begin;
   while (true) {
     load_stage(clamp(st + 2), p0);
-    compute(0, st);
+    compute(0, st, 0);
     store_stage(1, p1);
     __syncthreads();
     if (++st >= st_end) break;
     load_stage(clamp(st + 2), p1);
-    compute(1, st);
+    compute(1, st, 1);
     store_stage(0, p0);
     __syncthreads();
     if (++st >= st_end) break;
@@ -350,26 +396,37 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
     }
 }
 
+// Dynamic LDS beyond 64 KiB must be allowed once per kernel.
+template <int GSTEPS>
+hipError_t launch_gemm_kernel(dim3 grid, size_t lds, hipStream_t stream, const GemmArgs& a) {
+  static std::atomic<bool> raised{false};  // one per instantiation
+  if (!raised.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_int4_kernel<GSTEPS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised.store(true, std::memory_order_release);
+  }
+  hipLaunchKernelGGL(gemm_int4_kernel<GSTEPS>, grid, dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t gemm_lds_bytes() { return (size_t)2 * kStageWords * sizeof(uint32_t); }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  // Dynamic LDS beyond 64 KiB must be allowed once per kernel.
-  static std::atomic<bool> raised{false};
   const size_t lds = gemm_lds_bytes();
-  if (!raised.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_int4_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised.store(true, std::memory_order_release);
-  }
   const int64_t prep_blocks = a.Tp + (a.Np / 32) * ((a.Gp + 31) / 32);
   hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_int4_kernel, dim3((unsigned)(a.RB * a.CB * a.S)), dim3(kThreads), lds, stream, a);
-  return hipGetLastError();
+  const dim3 grid((unsigned)(a.RB * a.CB * a.S));
+  switch (a.gs) {
+    case 32: return launch_gemm_kernel<1>(grid, lds, stream, a);
+    case 64: return launch_gemm_kernel<2>(grid, lds, stream, a);
+    case 128: return launch_gemm_kernel<4>(grid, lds, stream, a);
+    default: return launch_gemm_kernel<0>(grid, lds, stream, a);
+  }
 }
 
 }  // namespace int4gemv
