@@ -22,8 +22,8 @@ way and reported under "next_rows"; they are not part of the step:
   normswi  silu(x . Wg) * (x . Wu), x = RMSNorm(a_a + a_b) * w_norm, [14336, 4096] (gs 128)
   embed    rows ids[T] of an int4 table [151936, 4096] dequantized, T = 1 and 4096 (gs 128);
            bytes = ids + the T rows' codes, scales and zeros + the fp32 output
-  prefill  X[512, 4096] . W[4096, 4096]^T (gs 128) on the matrix cores; reported as
-           useful TFLOP/s (2 T N K flops per call, prep launch included)
+  prefill  X[T, 4096] . W[4096, 4096]^T for T = 512 and 4096 (gs 128) on the matrix cores;
+           reported as useful TFLOP/s (2 T N K flops per call, prep launch included)
 
 Per-call durations: each call is also timed alone, in a graph of back-to-back
 calls cycling over >= 1 GiB of device copies of its buffers, with HIP events
@@ -269,18 +269,20 @@ def build_next(q4, torch, dev):
                           lambda s, ids=ids, out=out: q4.int4_embedding_gather(ids, *s, out=out),
                           lambda r: clones(w5, r), wbytes(w5)))
 
-    i6 = synth.n6_inputs()
     n6 = synth.NEXT["n6"]
+    i6 = synth.n6_inputs(max(n6["Ts"]))
     w6 = quantize(i6["W"], n6["gs"])
-    X6 = torch.from_numpy(i6["X"]).to(dev)
-    Y6 = torch.empty((n6["T"], n6["N"]), device=dev)
-    ws6 = torch.empty(q4.int4_gemm_workspace_bytes(n6["T"], n6["N"], n6["K"], n6["gs"]),
-                      dtype=torch.uint8, device=dev)
-    b6 = alg_bytes(n6["N"], n6["K"], n6["gs"], n6["T"] * n6["K"], n6["T"] * n6["N"])
-    c6 = Call(f"prefill GEMM T={n6['T']} {n6['N']}x{n6['K']}", b6,
-              lambda s: q4.int4_gemm(X6, *s, Y=Y6, workspace=ws6), lambda r: clones(w6, r), wbytes(w6))
-    c6.flops = 2 * n6["T"] * n6["N"] * n6["K"]
-    calls.append(c6)
+    for T in n6["Ts"]:
+        X6 = torch.from_numpy(i6["X"][:T].copy()).to(dev)
+        Y6 = torch.empty((T, n6["N"]), device=dev)
+        ws6 = torch.empty(q4.int4_gemm_workspace_bytes(T, n6["N"], n6["K"], n6["gs"]),
+                          dtype=torch.uint8, device=dev)
+        b6 = alg_bytes(n6["N"], n6["K"], n6["gs"], T * n6["K"], T * n6["N"])
+        c6 = Call(f"prefill GEMM T={T} {n6['N']}x{n6['K']}", b6,
+                  lambda s, X6=X6, Y6=Y6, ws6=ws6: q4.int4_gemm(X6, *s, Y=Y6, workspace=ws6),
+                  lambda r: clones(w6, r), wbytes(w6))
+        c6.flops = 2 * T * n6["N"] * n6["K"]
+        calls.append(c6)
     return calls
 
 

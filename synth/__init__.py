@@ -35,7 +35,8 @@ Next-row workloads (fused decode variants around the hot path, same recipe):
         MLP front       Wg,Wu[14336, 4096] gs 128         seeds 0x901..0x905
     n5  embedding       ids[T] uniform in [0, 151936) (T = 1 and 4096), table
         gather          [151936, 4096] gs 128               seeds 0xA01/0xA02
-    n6  prefill GEMM    X[512, 4096] N(0,1), W[4096, 4096] gs 128  seeds 0xB01/0xB02
+    n6  prefill GEMM    X[T, 4096] N(0,1) for T = 512 and 4096, W[4096, 4096] gs 128
+                                                            seeds 0xB01/0xB02
 Weights are N(0, 0.02^2) (0.02 is the standard deviation), activations N(0, 1).
 """
 from __future__ import annotations
@@ -154,7 +155,8 @@ NEXT = {
                gs=128, eps=1e-6),
     "n5": dict(name="int4 embedding gather from a [151936, 4096] gs=128 table, T = 1 and 4096",
                N=151936, K=4096, gs=128, Ts=(1, 4096)),
-    "n6": dict(name="prefill GEMM T=512 N=4096 K=4096 gs=128", T=512, N=4096, K=4096, gs=128),
+    "n6": dict(name="prefill GEMM T=512 (and 4096) N=4096 K=4096 gs=128", T=512, Ts=(512, 4096),
+               N=4096, K=4096, gs=128),
 }
 
 
@@ -194,9 +196,9 @@ def n5_inputs(N: int | None = None):
     return dict(ids=token_ids(0xA01, max(c["Ts"]), c["N"]), W=weights(0xA02, N or c["N"], c["K"]))
 
 
-def n6_inputs():
+def n6_inputs(T: int | None = None):
     c = NEXT["n6"]
-    return dict(X=lanes(0xB01, c["T"], c["K"]), W=weights(0xB02, c["N"], c["K"]))
+    return dict(X=lanes(0xB01, T or c["T"], c["K"]), W=weights(0xB02, c["N"], c["K"]))
 
 
 def c1_inputs():
