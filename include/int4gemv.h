@@ -149,15 +149,16 @@ int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, fl
                      float* y, float* residual_out, float* norm_out, void* stream);
 
 /*
- * Dual matvec: two projections that share one input vector and the same N,
- * K and gs, in one call that reads the input once ([P4]
+ * Dual matvec: two projections that share one input and the same N, K and
+ * gs, in one call that reads the input once ([P4]
  * fuseDualMatVecDecodeEntries, DualMatVecInt4: q_proj + gate_proj or
- * k_proj + v_proj of full-attention decode; [P1] fuseBatchDualMatVecEntries):
- *   y0[n] = x . w0[n],  y1[n] = x . w1[n].
- * Each output is bit-identical to int4_matvec (M = 1) of its own matrix.
- * Same local-data-share limit as int4_matvec at M = 1.
+ * k_proj + v_proj of full-attention decode; [P1] fuseBatchDualMatVecEntries,
+ * its port to M decode lanes):
+ *   y0[m][n] = X[m] . w0[n],  y1[m][n] = X[m] . w1[n],  0 <= M <= 8.
+ * X [M][K], y0 and y1 [M][N].  Each output is bit-identical to int4_matvec
+ * at the same M for its own matrix; limits as int4_matvec.
  */
-int int4_matvec_dual(const float* x,
+int int4_matvec_dual(const float* X, int32_t M,
                      const uint32_t* q0, const float* s0, const float* z0,
                      const uint32_t* q1, const float* s1, const float* z1,
                      int64_t N, int64_t K, int32_t group_size,
@@ -167,15 +168,14 @@ int int4_matvec_dual(const float* x,
  * Sigmoid-gated input matvec ([P4] fuseGatedOProjDecodeEntries: the
  * attention SigmoidGate, attn_out * sigmoid(gate), recomputed inside the
  * o_proj matvec's input load, GatedMatVecInt4; [P1]
- * fuseBatchGatedProjEntries "sigmoid"):
- *   xg[k] = a[k] * sigmoid(gate[k]),  sigmoid(t) = 1 / (1 + exp(-t)),
- *   y[n]  = xg . w[n].
- * The gate is evaluated in binary32 (with exp(-|t|), so it never
- * overflows); y is within the dot-product tolerance of the fp64 definition.
- * a and gate must be 16-byte aligned; K * 4 bytes must fit the per-block
- * local data share.
+ * fuseBatchGatedProjEntries "sigmoid", its port to M decode lanes):
+ *   xg[m][k] = a[m][k] * sigmoid(gate[m][k]),  sigmoid(t) = 1 / (1 + exp(-t)),
+ *   y[m][n]  = xg[m] . w[n],  0 <= M <= 8.
+ * a, gate [M][K] (16-byte aligned), y [M][N].  The gate is evaluated in
+ * binary32 (with exp(-|t|), so it never overflows); y is within the
+ * dot-product tolerance of the fp64 definition.  Limits as int4_matvec.
  */
-int int4_matvec_sigmoid_gated(const float* a, const float* gate,
+int int4_matvec_sigmoid_gated(const float* a, const float* gate, int32_t M,
                               const uint32_t* q, const float* scales, const float* zeros,
                               int64_t N, int64_t K, int32_t group_size,
                               float* y, void* stream);
@@ -184,12 +184,12 @@ int int4_matvec_sigmoid_gated(const float* a, const float* gate,
  * SwiGLU-gated input matvec ([P4] fuseSwiGLUGatedProjDecodeEntries: a
  * standalone SwiGLU feeding an int4 projection, e.g. the linear-attention
  * block's silu(z) * norm_out into out_proj, SwiGLUGatedMatVecInt4; [P1]
- * fuseBatchGatedProjEntries "swiglu"):
- *   xg[k] = silu(gate[k]) * up[k],  silu(t) = t / (1 + exp(-t)),
- *   y[n]  = xg . w[n].
- * Evaluation, alignment and limits as int4_matvec_sigmoid_gated.
+ * fuseBatchGatedProjEntries "swiglu", its port to M decode lanes):
+ *   xg[m][k] = silu(gate[m][k]) * up[m][k],  silu(t) = t / (1 + exp(-t)),
+ *   y[m][n]  = xg[m] . w[n],  0 <= M <= 8.
+ * Layouts, evaluation and limits as int4_matvec_sigmoid_gated.
  */
-int int4_matvec_swiglu_gated(const float* gate, const float* up,
+int int4_matvec_swiglu_gated(const float* gate, const float* up, int32_t M,
                              const uint32_t* q, const float* scales, const float* zeros,
                              int64_t N, int64_t K, int32_t group_size,
                              float* y, void* stream);

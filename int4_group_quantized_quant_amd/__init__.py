@@ -48,9 +48,9 @@ lib.int4_matvec_split4.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _
 lib.int4_matvec_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 lib.int4_matvec_norm.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i64, _i64, _i32,
                                  _vp, _vp, _vp, _vp]
-lib.int4_matvec_dual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]
-lib.int4_matvec_sigmoid_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
-lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_dual.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]
+lib.int4_matvec_sigmoid_gated.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 lib.int4_matvec_norm_swiglu.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i64, _i64, _i32, _vp, _vp, _vp]
 lib.int4_embedding_gather.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
@@ -217,42 +217,53 @@ def _pair(q0, s0, z0, q1, s1, z1, t0, t1):
     return N, K, gs
 
 
-def int4_matvec_dual(x: torch.Tensor, q0, s0, z0, q1, s1, z1, y0=None, y1=None, stream=None):
-    """(y0, y1) = (x . w0[n], x . w1[n]): two projections of one input in one call."""
+def _lanes(X: torch.Tensor, K: int, name: str):
+    """Rows of an activation tensor [K] (one lane) or [M, K]; returns (M, output shape fn)."""
+    _dev(X, name, _F32)
+    if X.shape[-1] != K or X.dim() not in (1, 2):
+        raise ValueError(f"{name} must be [{K}] or [M, {K}]")
+    M = 1 if X.dim() == 1 else X.shape[0]
+    return M, (lambda N: (N,) if X.dim() == 1 else (M, N))
+
+
+def int4_matvec_dual(X: torch.Tensor, q0, s0, z0, q1, s1, z1, y0=None, y1=None, stream=None):
+    """(y0, y1) = (X . w0^T, X . w1^T): two projections of one input ([K] or [M, K], M <= 8)."""
     N, K, gs = _pair(q0, s0, z0, q1, s1, z1, "0", "1")
-    _dev(x, "x", _F32)
-    y0 = torch.empty(N, dtype=torch.float32, device=x.device) if y0 is None else y0
-    y1 = torch.empty(N, dtype=torch.float32, device=x.device) if y1 is None else y1
+    M, shape = _lanes(X, K, "X")
+    y0 = torch.empty(shape(N), dtype=torch.float32, device=X.device) if y0 is None else y0
+    y1 = torch.empty(shape(N), dtype=torch.float32, device=X.device) if y1 is None else y1
     _dev(y0, "y0", _F32)
     _dev(y1, "y1", _F32)
-    _check(lib.int4_matvec_dual(_ptr(x), _ptr(q0), _ptr(s0), _ptr(z0), _ptr(q1), _ptr(s1),
+    _check(lib.int4_matvec_dual(_ptr(X), M, _ptr(q0), _ptr(s0), _ptr(z0), _ptr(q1), _ptr(s1),
                                 _ptr(z1), N, K, gs, _ptr(y0), _ptr(y1), _stream(stream)))
     return y0, y1
 
 
 def int4_matvec_sigmoid_gated(a: torch.Tensor, gate: torch.Tensor, q, scales, zeros, y=None,
                               stream=None) -> torch.Tensor:
-    """y[n] = (a * sigmoid(gate)) . w[n]."""
+    """y = (a * sigmoid(gate)) . w^T for a, gate [K] or [M, K] (M <= 8)."""
     N, K, gs = _weights(q, scales, zeros)
-    _dev(a, "a", _F32)
-    _dev(gate, "gate", _F32)
-    y = torch.empty(N, dtype=torch.float32, device=a.device) if y is None else y
+    M, shape = _lanes(a, K, "a")
+    if _lanes(gate, K, "gate")[0] != M or gate.dim() != a.dim():
+        raise ValueError("a and gate must have the same shape")
+    y = torch.empty(shape(N), dtype=torch.float32, device=a.device) if y is None else y
     _dev(y, "y", _F32)
-    _check(lib.int4_matvec_sigmoid_gated(_ptr(a), _ptr(gate), _ptr(q), _ptr(scales), _ptr(zeros),
-                                         N, K, gs, _ptr(y), _stream(stream)))
+    _check(lib.int4_matvec_sigmoid_gated(_ptr(a), _ptr(gate), M, _ptr(q), _ptr(scales),
+                                         _ptr(zeros), N, K, gs, _ptr(y), _stream(stream)))
     return y
 
 
 def int4_matvec_swiglu_gated(gate: torch.Tensor, up: torch.Tensor, q, scales, zeros, y=None,
                              stream=None) -> torch.Tensor:
-    """y[n] = (silu(gate) * up) . w[n]."""
+    """y = (silu(gate) * up) . w^T for gate, up [K] or [M, K] (M <= 8)."""
     N, K, gs = _weights(q, scales, zeros)
-    _dev(gate, "gate", _F32)
-    _dev(up, "up", _F32)
-    y = torch.empty(N, dtype=torch.float32, device=gate.device) if y is None else y
+    M, shape = _lanes(gate, K, "gate")
+    if _lanes(up, K, "up")[0] != M or up.dim() != gate.dim():
+        raise ValueError("gate and up must have the same shape")
+    y = torch.empty(shape(N), dtype=torch.float32, device=gate.device) if y is None else y
     _dev(y, "y", _F32)
-    _check(lib.int4_matvec_swiglu_gated(_ptr(gate), _ptr(up), _ptr(q), _ptr(scales), _ptr(zeros),
-                                        N, K, gs, _ptr(y), _stream(stream)))
+    _check(lib.int4_matvec_swiglu_gated(_ptr(gate), _ptr(up), M, _ptr(q), _ptr(scales),
+                                        _ptr(zeros), N, K, gs, _ptr(y), _stream(stream)))
     return y
 
 

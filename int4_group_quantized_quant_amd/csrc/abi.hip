@@ -184,7 +184,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   const int64_t N = a.N;
   const int nstream = mode_streams(mode);
   s->lds_max = dev.lds_block;
-  const int rows = mode == kPlain ? M : 1;
+  const int rows = M;  // activation rows staged per block (M = 1 except plain lanes)
   if (M == 1 && a.nch <= 8) {
     const int nch = a.nch;
     const int P = nch >= 8 ? 1 : 8 / nch;
@@ -228,7 +228,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // Too little LDS for the partial table and the activations: the LDS
     // kernel needs only the activations.
   }
-  if (mode == kPlain && M >= 2) {
+  if ((mode == kPlain || mode == kDual || mode_gates_input(mode)) && M >= 2) {
     // Matrix-core lanes: slices of SU = 16, 20 or 24 units, at most 8 waves
     // (two per SIMD) per block, P passes of the waves over the slices; one
     // block's columns in rounds of RT tiles whose partials fit the LDS.
@@ -244,7 +244,9 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     const int W = nsl < kSliceMaxWaves ? nsl : kSliceMaxWaves;
     const int bpc = kSliceMaxWaves / W;
     const int64_t tiles = (N + 15) / 16;
-    int64_t B = (int64_t)dev.cus * bpc;
+    // Blocks per weight stream (the dual mode runs one grid half per stream).
+    const int nstreams = mode == kDual ? 2 : 1;
+    int64_t B = (int64_t)dev.cus * bpc / nstreams;
     if (B > tiles) B = tiles;
     if (B < 1) B = 1;
     const int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
@@ -264,8 +266,8 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     s->block_threads = 64 * W;
     s->lds_bytes = slice_lds_bytes(su, cls, a.G, W, (int)rt);
     a.g_recip = a.G == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + (uint64_t)a.G - 1) / (uint64_t)a.G);
-    s->grid = (int)B;
-    a.total_waves = B * W;
+    s->grid = (int)(B * nstreams);
+    a.total_waves = B * nstreams * W;
     return INT4_OK;
   }
   const size_t lds = (size_t)rows * (size_t)a.K * sizeof(float) + (mode_has_norm(mode) ? 64 : 0);
@@ -504,15 +506,16 @@ int int4_matvec_norm(const float* a_a, const float* a_b, const float* w_norm, fl
   return run(kNorm, a, stream);
 }
 
-int int4_matvec_dual(const float* x, const uint32_t* q0, const float* s0, const float* z0,
+int int4_matvec_dual(const float* X, int32_t M, const uint32_t* q0, const float* s0, const float* z0,
                      const uint32_t* q1, const float* s1, const float* z1, int64_t N, int64_t K,
                      int32_t group_size, float* y0, float* y1, void* stream) {
   if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  if (M < 0 || M > 8) return fail(INT4_ERR_SHAPE, "M must be in [0, 8] (got %d)", (int)M);
   RETURN_IF(check_kgs(K, group_size));
-  if (N == 0) return ok();
-  if (!x || !q0 || !s0 || !z0 || !q1 || !s1 || !z1 || !y0 || !y1)
-    return fail(INT4_ERR_NULL, "x, both weight triplets, y0 and y1 are required");
-  RETURN_IF(check_align(x, 16, "x"));
+  if (N == 0 || M == 0) return ok();
+  if (!X || !q0 || !s0 || !z0 || !q1 || !s1 || !z1 || !y0 || !y1)
+    return fail(INT4_ERR_NULL, "X, both weight triplets, y0 and y1 are required");
+  RETURN_IF(check_align(X, 16, "X"));
   RETURN_IF(check_align(q0, 16, "q0"));
   RETURN_IF(check_align(q1, 16, "q1"));
   RETURN_IF(check_align(s0, 4, "s0"));
@@ -522,15 +525,15 @@ int int4_matvec_dual(const float* x, const uint32_t* q0, const float* s0, const 
   RETURN_IF(check_align(y0, 4, "y0"));
   RETURN_IF(check_align(y1, 4, "y1"));
   const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
-  const Span ins[] = {{x, (uint64_t)K * 4, "x"},
+  const Span ins[] = {{X, (uint64_t)M * K * 4, "X"},
                       {q0, (uint64_t)N * K / 2, "q0"}, {s0, G * 4, "s0"}, {z0, G * 4, "z0"},
                       {q1, (uint64_t)N * K / 2, "q1"}, {s1, G * 4, "s1"}, {z1, G * 4, "z1"}};
-  const Span outs[] = {{y0, (uint64_t)N * 4, "y0"}, {y1, (uint64_t)N * 4, "y1"}};
+  const Span outs[] = {{y0, (uint64_t)M * N * 4, "y0"}, {y1, (uint64_t)M * N * 4, "y1"}};
   RETURN_IF(check_alias(ins, 7, outs, 2));
   GemvArgs a{};
   fill_common(a, N, K, group_size);
-  a.x = x;
-  a.M = 1;
+  a.x = X;
+  a.M = M;
   a.q[0] = reinterpret_cast<const uint4*>(q0);
   a.s[0] = s0;
   a.z[0] = z0;
@@ -543,13 +546,14 @@ int int4_matvec_dual(const float* x, const uint32_t* q0, const float* s0, const 
 }
 
 // Shared by the two input-gated entry points: p and r are the two input
-// vectors (a and gate, or gate and up).
-static int input_gated(Mode mode, const float* p, const float* r, const char* pn, const char* rn,
-                const uint32_t* q, const float* scales, const float* zeros, int64_t N, int64_t K,
-                int32_t group_size, float* y, void* stream) {
+// row sets [M][K] (a and gate, or gate and up).
+static int input_gated(Mode mode, const float* p, const float* r, int32_t M, const char* pn,
+                       const char* rn, const uint32_t* q, const float* scales, const float* zeros,
+                       int64_t N, int64_t K, int32_t group_size, float* y, void* stream) {
   if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  if (M < 0 || M > 8) return fail(INT4_ERR_SHAPE, "M must be in [0, 8] (got %d)", (int)M);
   RETURN_IF(check_kgs(K, group_size));
-  if (N == 0) return ok();
+  if (N == 0 || M == 0) return ok();
   if (!p || !r || !q || !scales || !zeros || !y)
     return fail(INT4_ERR_NULL, "%s, %s, q, scales, zeros and y are required", pn, rn);
   RETURN_IF(check_align(p, 16, pn));
@@ -559,15 +563,15 @@ static int input_gated(Mode mode, const float* p, const float* r, const char* pn
   RETURN_IF(check_align(zeros, 4, "zeros"));
   RETURN_IF(check_align(y, 4, "y"));
   const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
-  const Span ins[] = {{p, (uint64_t)K * 4, pn}, {r, (uint64_t)K * 4, rn},
+  const Span ins[] = {{p, (uint64_t)M * K * 4, pn}, {r, (uint64_t)M * K * 4, rn},
                       {q, (uint64_t)N * K / 2, "q"}, {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
-  const Span outs[] = {{y, (uint64_t)N * 4, "y"}};
+  const Span outs[] = {{y, (uint64_t)M * N * 4, "y"}};
   RETURN_IF(check_alias(ins, 5, outs, 1));
   GemvArgs a{};
   fill_common(a, N, K, group_size);
   a.x = p;
   a.x2 = r;
-  a.M = 1;
+  a.M = M;
   a.q[0] = reinterpret_cast<const uint4*>(q);
   a.s[0] = scales;
   a.z[0] = zeros;
@@ -575,16 +579,16 @@ static int input_gated(Mode mode, const float* p, const float* r, const char* pn
   return run(mode, a, stream);
 }
 
-int int4_matvec_sigmoid_gated(const float* a_in, const float* gate, const uint32_t* q,
+int int4_matvec_sigmoid_gated(const float* a_in, const float* gate, int32_t M, const uint32_t* q,
                               const float* scales, const float* zeros, int64_t N, int64_t K,
                               int32_t group_size, float* y, void* stream) {
-  return input_gated(kSigIn, a_in, gate, "a", "gate", q, scales, zeros, N, K, group_size, y, stream);
+  return input_gated(kSigIn, a_in, gate, M, "a", "gate", q, scales, zeros, N, K, group_size, y, stream);
 }
 
-int int4_matvec_swiglu_gated(const float* gate, const float* up, const uint32_t* q,
+int int4_matvec_swiglu_gated(const float* gate, const float* up, int32_t M, const uint32_t* q,
                              const float* scales, const float* zeros, int64_t N, int64_t K,
                              int32_t group_size, float* y, void* stream) {
-  return input_gated(kSwiIn, gate, up, "gate", "up", q, scales, zeros, N, K, group_size, y, stream);
+  return input_gated(kSwiIn, gate, up, M, "gate", "up", q, scales, zeros, N, K, group_size, y, stream);
 }
 
 int int4_matvec_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm, float eps,

@@ -375,19 +375,22 @@ __device__ __forceinline__ float silu_f32(float t) {
   return t >= 0.0f ? t / (1.0f + e) : (t * e) / (1.0f + e);
 }
 
-// Gated input of float4 i ([P4] GatedMatVecInt4 / SwiGLUGatedMatVecInt4:
-// the elementwise gate is rebuilt inside the matvec's input load):
-// kSigIn x = a * sigmoid(gate), kSwiIn x = silu(gate) * up.
+// Gated input ([P4] GatedMatVecInt4 / SwiGLUGatedMatVecInt4: the
+// elementwise gate is rebuilt inside the matvec's input load) of one float4
+// of p = a / gate and r = gate / up: kSigIn x = a * sigmoid(gate), kSwiIn
+// x = silu(gate) * up.  gated_in4 takes float4 i of the rows x and x2.
 template <int MODE>
-__device__ __forceinline__ float4 gated_in4(const GemvArgs& a, int i) {
-  const float4 p = reinterpret_cast<const float4*>(a.x)[i];
-  const float4 r = reinterpret_cast<const float4*>(a.x2)[i];
+__device__ __forceinline__ float4 gate4(float4 p, float4 r) {
   if constexpr (MODE == kSigIn)
     return make_float4(p.x * sigmoid_f32(r.x), p.y * sigmoid_f32(r.y), p.z * sigmoid_f32(r.z),
                        p.w * sigmoid_f32(r.w));
   else
     return make_float4(silu_f32(p.x) * r.x, silu_f32(p.y) * r.y, silu_f32(p.z) * r.z,
                        silu_f32(p.w) * r.w);
+}
+template <int MODE>
+__device__ __forceinline__ float4 gated_in4(const GemvArgs& a, int i) {
+  return gate4<MODE>(reinterpret_cast<const float4*>(a.x)[i], reinterpret_cast<const float4*>(a.x2)[i]);
 }
 
 // Column epilogue shared by both kernels: `tot[st][m]` are the finished sums
@@ -996,7 +999,10 @@ struct SliceTile {
   u32x4 c[SU / 4];
 };
 
-template <int SU, int GS, int DEPTH>
+// MODE: kPlain; kDual (the first half of the blocks runs stream 0 into
+// out[0], the second half stream 1 into out[1]); kSigIn / kSwiIn (each
+// lane's input is the elementwise gate of rows x and x2).
+template <int SU, int GS, int DEPTH, int MODE>
 __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
   extern __shared__ float4 lds4[];
   constexpr int NJ = SU / 4;  // load instructions per tile
@@ -1018,8 +1024,11 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   const int wave = uniform_int(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int nsl = (U + SU - 1) / SU;
-  const int64_t cb = uniform_i64((int64_t)blockIdx.x * N / gridDim.x);
-  const int64_t ce = uniform_i64(((int64_t)blockIdx.x + 1) * N / gridDim.x);
+  const int nbk = MODE == kDual ? (int)gridDim.x / 2 : (int)gridDim.x;
+  const int stream = MODE == kDual && (int)blockIdx.x >= nbk ? 1 : 0;
+  const int64_t bk = (int64_t)blockIdx.x - (int64_t)stream * nbk;
+  const int64_t cb = uniform_i64(bk * N / nbk);
+  const int64_t ce = uniform_i64((bk + 1) * N / nbk);
   const int ntile = (int)((ce - cb + 15) >> 4);
   const int RT = a.rt;
 
@@ -1028,9 +1037,10 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   float* part = reinterpret_cast<float*>(lds + W * kStage);
   uint32_t* s_tab = lds + W * kStage + RT * W * 128;
   uint32_t* z_tab = s_tab + RT * 16 * GP;
-  const char* qbase = reinterpret_cast<const char*>(a.q[0]);
-  const char* sbase = reinterpret_cast<const char*>(a.s[0]);
-  const char* zbase = reinterpret_cast<const char*>(a.z[0]);
+  const char* qbase = reinterpret_cast<const char*>(a.q[stream]);
+  const char* sbase = reinterpret_cast<const char*>(a.s[stream]);
+  const char* zbase = reinterpret_cast<const char*>(a.z[stream]);
+  float* const yout = a.out[stream];
 
   // Load layout: instruction j, lane l carries unit t of column col, where
   // 64j + l = SU*col + t.  The same unit goes to stage dword col*CS + 4t.
@@ -1115,9 +1125,15 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
 #pragma unroll
         for (int tt = 0; tt < H; ++tt) {
           const int u = u0 + H * half + tt;
-          const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * K + 32 * (u < U ? u : U - 1) + 8 * hi4);
+          const int64_t off = (int64_t)m * K + 32 * (u < U ? u : U - 1) + 8 * hi4;
+          const float4* src = reinterpret_cast<const float4*>(a.x + off);
           xp[tt] = src[0];  // units past K (clamped address) are masked below
           xq[tt] = src[1];
+          if constexpr (mode_gates_input(MODE)) {
+            const float4* src2 = reinterpret_cast<const float4*>(a.x2 + off);
+            xp[tt] = gate4<MODE>(xp[tt], src2[0]);
+            xq[tt] = gate4<MODE>(xq[tt], src2[1]);
+          }
         }
       }
       if (first_pass) {
@@ -1331,7 +1347,7 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
         const float* pp = part + ((size_t)(i * W) * 8 + mm) * 16 + c;
         float y = pp[0];
         for (int w = 1; w < W; ++w) y += pp[(size_t)w * 128];
-        a.out[0][(int64_t)mm * N + col] = y;
+        yout[(int64_t)mm * N + col] = y;
       }
     }
     __syncthreads();
@@ -1393,25 +1409,36 @@ hipError_t dispatch_lds_m(const GemvArgs& a, const LaunchShape& s, hipStream_t s
   return s.ncol == 1 ? launch_lds<kPlain, M, 1>(a, s, st, occ) : launch_lds<kPlain, M, 2>(a, s, st, occ);
 }
 
-template <int SU, int DEPTH>
+template <int SU, int DEPTH, int MODE>
 hipError_t dispatch_slice_su(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
   static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised0{false};
   switch (slice_class(a.U / a.G)) {
-    case 1: return launch_or_query(gemv_slice_kernel<SU, 1, DEPTH>, raised1, a, s, st, occ);
-    case 2: return launch_or_query(gemv_slice_kernel<SU, 2, DEPTH>, raised2, a, s, st, occ);
-    case 4: return launch_or_query(gemv_slice_kernel<SU, 4, DEPTH>, raised4, a, s, st, occ);
-    default: return launch_or_query(gemv_slice_kernel<SU, 0, DEPTH>, raised0, a, s, st, occ);
+    case 1: return launch_or_query(gemv_slice_kernel<SU, 1, DEPTH, MODE>, raised1, a, s, st, occ);
+    case 2: return launch_or_query(gemv_slice_kernel<SU, 2, DEPTH, MODE>, raised2, a, s, st, occ);
+    case 4: return launch_or_query(gemv_slice_kernel<SU, 4, DEPTH, MODE>, raised4, a, s, st, occ);
+    default: return launch_or_query(gemv_slice_kernel<SU, 0, DEPTH, MODE>, raised0, a, s, st, occ);
   }
 }
 
-hipError_t dispatch_slice(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
-  if (a.su == 24) return dispatch_slice_su<24, 2>(a, s, st, occ);
-  if (a.su == 20) return dispatch_slice_su<20, 3>(a, s, st, occ);
-  return dispatch_slice_su<16, 3>(a, s, st, occ);
+template <int MODE>
+hipError_t dispatch_slice_mode(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if (a.su == 24) return dispatch_slice_su<24, 2, MODE>(a, s, st, occ);
+  if (a.su == 20) return dispatch_slice_su<20, 3, MODE>(a, s, st, occ);
+  return dispatch_slice_su<16, 3, MODE>(a, s, st, occ);
+}
+
+hipError_t dispatch_slice(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  switch (mode) {
+    case kPlain: return dispatch_slice_mode<kPlain>(a, s, st, occ);
+    case kDual: return dispatch_slice_mode<kDual>(a, s, st, occ);
+    case kSigIn: return dispatch_slice_mode<kSigIn>(a, s, st, occ);
+    case kSwiIn: return dispatch_slice_mode<kSwiIn>(a, s, st, occ);
+    default: return hipErrorInvalidValue;  // no matrix-core form of this mode
+  }
 }
 
 hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
-  if (s.variant == kVariantSlice) return dispatch_slice(a, s, st, occ);
+  if (s.variant == kVariantSlice) return dispatch_slice(mode, a, s, st, occ);
   if (s.variant == kVariantReg) {
     switch (mode) {
       case kSplit4: return dispatch_reg<kSplit4>(a, s, st, occ);

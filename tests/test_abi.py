@@ -156,10 +156,12 @@ H_ = 0x80000000
 
 
 def test_next_variants_empty_calls_are_no_ops(lib):
-    assert lib.int4_matvec_dual(None, None, None, None, None, None, None, 0, 256, 64,
+    assert lib.int4_matvec_dual(None, 1, None, None, None, None, None, None, 0, 256, 64,
                                 None, None, None) == OK
-    assert lib.int4_matvec_sigmoid_gated(None, None, None, None, None, 0, 256, 64, None, None) == OK
-    assert lib.int4_matvec_swiglu_gated(None, None, None, None, None, 0, 256, 64, None, None) == OK
+    assert lib.int4_matvec_dual(None, 0, None, None, None, None, None, None, 16, 256, 64,
+                                None, None, None) == OK
+    assert lib.int4_matvec_sigmoid_gated(None, None, 1, None, None, None, 0, 256, 64, None, None) == OK
+    assert lib.int4_matvec_swiglu_gated(None, None, 0, None, None, None, 16, 256, 64, None, None) == OK
     assert lib.int4_matvec_norm_swiglu(None, None, None, ctypes.c_float(1e-6), None, None, None,
                                        None, None, None, 0, 256, 64, None, None, None) == OK
 
@@ -167,23 +169,30 @@ def test_next_variants_empty_calls_are_no_ops(lib):
 def test_next_variants_shape_null_align_alias(lib):
     N, K, gs = 16, 256, 64
     # shapes
-    assert lib.int4_matvec_dual(A, B, C, D, E, F, G_, N, K, 48, H_, H_ + 0x1000, None) == SHAPE
-    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1000, B, C, D, N, 96, 64, E, None) == SHAPE
-    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B, C, D, -1, K, gs, E, None) == SHAPE
+    assert lib.int4_matvec_dual(A, 1, B, C, D, E, F, G_, N, K, 48, H_, H_ + 0x1000, None) == SHAPE
+    assert lib.int4_matvec_dual(A, 9, B, C, D, E, F, G_, N, K, gs, H_, H_ + 0x1000, None) == SHAPE
+    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1000, 1, B, C, D, N, 96, 64, E, None) == SHAPE
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, 1, B, C, D, -1, K, gs, E, None) == SHAPE
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, -1, B, C, D, N, K, gs, E, None) == SHAPE
     # nulls
-    assert lib.int4_matvec_dual(A, B, C, D, E, F, G_, N, K, gs, H_, None, None) == NULL
-    assert lib.int4_matvec_sigmoid_gated(A, None, B, C, D, N, K, gs, E, None) == NULL
-    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B, C, D, N, K, gs, None, None) == NULL
+    assert lib.int4_matvec_dual(A, 1, B, C, D, E, F, G_, N, K, gs, H_, None, None) == NULL
+    assert lib.int4_matvec_sigmoid_gated(A, None, 1, B, C, D, N, K, gs, E, None) == NULL
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, 1, B, C, D, N, K, gs, None, None) == NULL
     assert lib.int4_matvec_norm_swiglu(A, A + 0x1000, A + 0x2000, ctypes.c_float(1e-6),
                                        B, C, D, None, F, G_, N, K, gs, H_, None, None) == NULL
     # alignment: the second input vector must be 16-byte aligned too
-    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1004, B, C, D, N, K, gs, E, None) == ALIGN
-    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B + 4, C, D, N, K, gs, E, None) == ALIGN
-    assert lib.int4_matvec_dual(A, B, C, D, E + 8, F, G_, N, K, gs, H_, H_ + 0x1000, None) == ALIGN
+    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1004, 1, B, C, D, N, K, gs, E, None) == ALIGN
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, 1, B + 4, C, D, N, K, gs, E, None) == ALIGN
+    assert lib.int4_matvec_dual(A, 1, B, C, D, E + 8, F, G_, N, K, gs, H_, H_ + 0x1000, None) == ALIGN
     # aliasing: outputs against each other and against either input vector
-    assert lib.int4_matvec_dual(A, B, C, D, E, F, G_, N, K, gs, H_, H_ + 8, None) == ALIAS
-    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1000, B, C, D, N, K, gs, A + 0x1010, None) == ALIAS
-    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, B, C, D, N, K, gs, A + 16, None) == ALIAS
+    assert lib.int4_matvec_dual(A, 1, B, C, D, E, F, G_, N, K, gs, H_, H_ + 8, None) == ALIAS
+    # with M = 4 lanes y0 spans 4*N floats, so y1 right after N floats overlaps it
+    assert lib.int4_matvec_dual(A, 4, B, C, D, E, F, G_, N, K, gs, H_, H_ + 4 * N, None) == ALIAS
+    assert lib.int4_matvec_sigmoid_gated(A, A + 0x1000, 1, B, C, D, N, K, gs, A + 0x1010, None) == ALIAS
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x1000, 1, B, C, D, N, K, gs, A + 16, None) == ALIAS
+    # with M = 2 lanes, y inside the second row of up [2][K] overlaps it
+    assert lib.int4_matvec_swiglu_gated(A, A + 0x10000, 2, B, C, D, N, K, gs, A + 0x10000 + 4 * K + 64,
+                                        None) == ALIAS
     assert lib.int4_matvec_norm_swiglu(A, A + 0x1000, A + 0x2000, ctypes.c_float(1e-6),
                                        B, C, D, E, F, G_, N, K, gs, H_, H_ + 16, None) == ALIAS
     # eps

@@ -303,3 +303,61 @@ def test_n5_embedding_gather_full(q4):
     ref = oracle.embedding(pos, *r, c["K"], c["gs"])
     assert out.shape == (T, c["K"])
     np.testing.assert_array_equal(bits(out), bits(ref))
+
+
+# ------------------------------------------------------------------ M decode lanes (batch ports)
+
+LANE_SHAPES = [(129, 1024, 128), (300, 5120, 64), (77, 2080, 32), (45, 2304, 96)]
+
+
+@pytest.mark.parametrize("M", [2, 3, 8])
+@pytest.mark.parametrize("N,K,gs", LANE_SHAPES)
+def test_dual_lanes(q4, M, N, K, gs):
+    q0, s0, z0 = quantized(0xF800 + N, N, K, gs)
+    q1, s1, z1 = quantized(0xF801 + N, N, K, gs)
+    X = synth.lanes(0xF802 + M, M, K)
+    Xd, *w = to_dev(X, q0.view(np.int32), s0, z0, q1.view(np.int32), s1, z1)
+    y0, y1 = q4.int4_matvec_dual(Xd, *w)
+    y0, y1 = host(y0), host(y1)
+    assert y0.shape == (M, N) and y1.shape == (M, N)
+    for m in range(M):
+        ref = oracle.dual(X[m], q0, s0, z0, q1, s1, z1, K, gs)
+        assert_dot_close(y0[m], ref["y0"], ref["b0"], f"dual lanes y0 m={m}")
+        assert_dot_close(y1[m], ref["y1"], ref["b1"], f"dual lanes y1 m={m}")
+    # Each output is int4_matvec at the same M for its own matrix, bit for bit.
+    np.testing.assert_array_equal(bits(y0), bits(host(q4.int4_matvec(Xd, *w[:3]))))
+    np.testing.assert_array_equal(bits(y1), bits(host(q4.int4_matvec(Xd, *w[3:]))))
+
+
+@pytest.mark.parametrize("M", [2, 5, 8])
+@pytest.mark.parametrize("N,K,gs", LANE_SHAPES)
+def test_input_gated_lanes(q4, M, N, K, gs):
+    q, s, z = quantized(0xF900 + N, N, K, gs)
+    P = synth.lanes(0xF901 + M, M, K)
+    R = (2.0 * synth.lanes(0xF902 + M, M, K)).astype(np.float32)
+    Pd, Rd, *w = to_dev(P, R, q.view(np.int32), s, z)
+    ys = host(q4.int4_matvec_sigmoid_gated(Pd, Rd, *w))
+    yw = host(q4.int4_matvec_swiglu_gated(Pd, Rd, *w))
+    assert ys.shape == (M, N) and yw.shape == (M, N)
+    for m in range(M):
+        rs = oracle.sigmoid_gated(P[m], R[m], q, s, z, K, gs)
+        rw = oracle.swiglu_gated(P[m], R[m], q, s, z, K, gs)
+        assert_dot_close(ys[m], rs["y"], rs["B"], f"sigmoid-gated lanes m={m}")
+        assert_dot_close(yw[m], rw["y"], rw["B"], f"swiglu-gated lanes m={m}")
+    # Lanes never interact: the first lane alone (M = 2 with a zero second
+    # lane) gives the same bits as lane 0 of the full call.
+    P2 = np.stack([P[0], np.zeros(K, np.float32)])
+    R2 = np.stack([R[0], np.zeros(K, np.float32)])
+    y2 = host(q4.int4_matvec_sigmoid_gated(*to_dev(P2, R2), *w))
+    np.testing.assert_array_equal(bits(y2[0]), bits(ys[0]))
+
+
+def test_lanes_variants_reject_nine_lanes(q4):
+    N, K, gs = 20, 512, 64
+    q, s, z = quantized(0xFA00, N, K, gs)
+    X = synth.lanes(0xFA01, 9, K)
+    Xd, *w = to_dev(X, q.view(np.int32), s, z)
+    with pytest.raises(q4.Int4Error):
+        q4.int4_matvec_dual(Xd, *w, *w)
+    with pytest.raises(q4.Int4Error):
+        q4.int4_matvec_swiglu_gated(Xd, Xd, *w)
