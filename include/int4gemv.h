@@ -128,6 +128,21 @@ int int4_matvec_gated(const float* x,
                       int64_t N, int64_t K, int32_t group_size, float* h, void* stream);
 
 /*
+ * The SiLU-gated gate/up matvec for M decode lanes in one launch ([P1]
+ * fuseBatchSwiGLUMLPEntries: gate + up + SwiGLU as one fused batched GEMM
+ * of the lockstep batch decode):
+ *   H[m][n] = silu(X[m] . w_gate[n]) * (X[m] . w_up[n]),  0 <= M <= 8.
+ * X [M][K], H [M][N].  M = 1 is int4_matvec_gated.  For M >= 2 the gate and
+ * up sums are bit-identical to int4_matvec at the same M; the scale and
+ * zero-point tables of both matrices share the local data share, so K/gs
+ * is limited to about half of int4_matvec's M >= 2 limit.
+ */
+int int4_matvec_gated_lanes(const float* X, int32_t M,
+                            const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+                            const uint32_t* q_up, const float* s_up, const float* z_up,
+                            int64_t N, int64_t K, int32_t group_size, float* H, void* stream);
+
+/*
  * Residual-add + RMSNorm prefixed matvec ([P4] WGSL_NORM_MATVEC_INT4,
  * NORM_MATVEC_INT4_SPEC with params [K, N, gs, eps]):
  *   r[k]   = a_a[k] + a_b[k]                          (binary32)

@@ -22,7 +22,7 @@ __all__ = [
     "Int4Error", "int4_quantize_pack", "int4_matvec", "int4_matvec_split4",
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
     "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
-    "int4_gemm_workspace_bytes", "lib", "LIB_PATH",
+    "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "lib", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -54,6 +54,8 @@ lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i
 lib.int4_matvec_norm_swiglu.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i64, _i64, _i32, _vp, _vp, _vp]
 lib.int4_embedding_gather.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_gated_lanes.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_matvec_gated_lanes.restype = ctypes.c_int
 lib.int4_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_gemm.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, ctypes.c_size_t, _vp]
@@ -327,3 +329,16 @@ def int4_gemm(X: torch.Tensor, q, scales, zeros, Y=None, workspace=None, stream=
     _check(lib.int4_gemm(_ptr(X), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
                          _ptr(workspace), workspace.numel(), _stream(stream)))
     return Y
+
+
+def int4_matvec_gated_lanes(X: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, H=None,
+                            stream=None) -> torch.Tensor:
+    """H = silu(X . w_gate^T) * (X . w_up^T) for X [M, K] (M <= 8), one launch."""
+    N, K, gs = _pair(q_gate, s_gate, z_gate, q_up, s_up, z_up, "_gate", "_up")
+    M, shape = _lanes(X, K, "X")
+    H = torch.empty(shape(N), dtype=torch.float32, device=X.device) if H is None else H
+    _dev(H, "H", _F32)
+    _check(lib.int4_matvec_gated_lanes(_ptr(X), M, _ptr(q_gate), _ptr(s_gate), _ptr(z_gate),
+                                       _ptr(q_up), _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(H),
+                                       _stream(stream)))
+    return H

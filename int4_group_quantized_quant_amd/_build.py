@@ -35,10 +35,7 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(HERE, "csrc"), *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,9 +44,25 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
         sys.stderr.write(err + "\n")
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+        raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd[-3:])}")
     if verbose and err.strip():
         sys.stderr.write(err + "\n")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile each source to an object in parallel, then link the shared library."""
+    import concurrent.futures
+    import tempfile
+
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    with tempfile.TemporaryDirectory(prefix="int4gemv_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *inc, "-c", src, "-o", obj]
+                for src, obj in zip(SOURCES, objs)]
+        with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB_PATH + ".tmp"
+        _run([hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -228,7 +228,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // Too little LDS for the partial table and the activations: the LDS
     // kernel needs only the activations.
   }
-  if ((mode == kPlain || mode == kDual || mode_gates_input(mode)) && M >= 2) {
+  if ((mode == kPlain || mode == kDual || mode == kGated || mode_gates_input(mode)) && M >= 2) {
     // Matrix-core lanes: slices of SU = 16, 20 or 24 units, at most 8 waves
     // (two per SIMD) per block, P passes of the waves over the slices; one
     // block's columns in rounds of RT tiles whose partials fit the LDS.
@@ -251,8 +251,9 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     if (B < 1) B = 1;
     const int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
     const size_t budget = dev.lds_cu / (size_t)bpc < dev.lds_block ? dev.lds_cu / (size_t)bpc : dev.lds_block;
-    const size_t fixed = slice_lds_bytes(su, cls, a.G, W, 0);
-    const size_t per_tile = slice_lds_bytes(su, cls, a.G, W, 1) - fixed;
+    const int nv = mode == kGated ? 2 : 1;  // both streams of a tile in one block
+    const size_t fixed = slice_lds_bytes(su, cls, a.G, W, 0, nv);
+    const size_t per_tile = slice_lds_bytes(su, cls, a.G, W, 1, nv) - fixed;
     if (fixed + per_tile > budget)
       return fail(INT4_ERR_SHAPE, "matrix-core lanes need %zu bytes of LDS per block; %zu available",
                   fixed + per_tile, budget);
@@ -264,7 +265,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     s->ncol = 16;
     s->depth = 1;
     s->block_threads = 64 * W;
-    s->lds_bytes = slice_lds_bytes(su, cls, a.G, W, (int)rt);
+    s->lds_bytes = slice_lds_bytes(su, cls, a.G, W, (int)rt, nv);
     a.g_recip = a.G == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + (uint64_t)a.G - 1) / (uint64_t)a.G);
     s->grid = (int)(B * nstreams);
     a.total_waves = B * nstreams * W;
@@ -460,6 +461,45 @@ int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gat
   a.s[1] = s_up;
   a.z[1] = z_up;
   a.out[0] = h;
+  return run(kGated, a, stream);
+}
+
+int int4_matvec_gated_lanes(const float* X, int32_t M, const uint32_t* q_gate, const float* s_gate,
+                            const float* z_gate, const uint32_t* q_up, const float* s_up,
+                            const float* z_up, int64_t N, int64_t K, int32_t group_size, float* H,
+                            void* stream) {
+  if (N < 0) return fail(INT4_ERR_SHAPE, "N must be >= 0 (got %lld)", (long long)N);
+  if (M < 0 || M > 8) return fail(INT4_ERR_SHAPE, "M must be in [0, 8] (got %d)", (int)M);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0 || M == 0) return ok();
+  if (!X || !q_gate || !s_gate || !z_gate || !q_up || !s_up || !z_up || !H)
+    return fail(INT4_ERR_NULL, "X, both weight triplets and H are required");
+  RETURN_IF(check_align(X, 16, "X"));
+  RETURN_IF(check_align(q_gate, 16, "q_gate"));
+  RETURN_IF(check_align(q_up, 16, "q_up"));
+  RETURN_IF(check_align(s_gate, 4, "s_gate"));
+  RETURN_IF(check_align(z_gate, 4, "z_gate"));
+  RETURN_IF(check_align(s_up, 4, "s_up"));
+  RETURN_IF(check_align(z_up, 4, "z_up"));
+  RETURN_IF(check_align(H, 4, "H"));
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{X, (uint64_t)M * K * 4, "X"},
+                      {q_gate, (uint64_t)N * K / 2, "q_gate"}, {s_gate, G * 4, "s_gate"},
+                      {z_gate, G * 4, "z_gate"},
+                      {q_up, (uint64_t)N * K / 2, "q_up"}, {s_up, G * 4, "s_up"}, {z_up, G * 4, "z_up"}};
+  const Span outs[] = {{H, (uint64_t)M * N * 4, "H"}};
+  RETURN_IF(check_alias(ins, 7, outs, 1));
+  GemvArgs a{};
+  fill_common(a, N, K, group_size);
+  a.x = X;
+  a.M = M;
+  a.q[0] = reinterpret_cast<const uint4*>(q_gate);
+  a.s[0] = s_gate;
+  a.z[0] = z_gate;
+  a.q[1] = reinterpret_cast<const uint4*>(q_up);
+  a.s[1] = s_up;
+  a.z[1] = z_up;
+  a.out[0] = H;
   return run(kGated, a, stream);
 }
 

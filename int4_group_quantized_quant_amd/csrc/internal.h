@@ -97,9 +97,11 @@ __host__ __device__ constexpr int slice_stage_words(int su) { return 16 * slice_
 __host__ __device__ constexpr int slice_table_stride(int G, int su, int cls) {
   return (G + slice_groups(su, cls)) | 1;
 }
-inline size_t slice_lds_bytes(int su, int cls, int G, int waves, int rt) {
-  return ((size_t)waves * slice_stage_words(su) + (size_t)rt * waves * 128 +
-          (size_t)2 * rt * 16 * slice_table_stride(G, su, cls)) * sizeof(float);
+// nv: weight streams per column tile (2 for the gated lanes), each with its
+// own partials and tables.
+inline size_t slice_lds_bytes(int su, int cls, int G, int waves, int rt, int nv = 1) {
+  return ((size_t)waves * slice_stage_words(su) + (size_t)nv * rt * waves * 128 +
+          (size_t)nv * 2 * rt * 16 * slice_table_stride(G, su, cls)) * sizeof(float);
 }
 
 struct LaunchShape {

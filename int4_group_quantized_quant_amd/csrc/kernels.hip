@@ -1001,7 +1001,9 @@ struct SliceTile {
 
 // MODE: kPlain; kDual (the first half of the blocks runs stream 0 into
 // out[0], the second half stream 1 into out[1]); kSigIn / kSwiIn (each
-// lane's input is the elementwise gate of rows x and x2).
+// lane's input is the elementwise gate of rows x and x2); kGated (each block
+// runs both streams over its columns: a round's tiles of stream 0, then of
+// stream 1, and the round's outputs are silu(g) * u).
 template <int SU, int GS, int DEPTH, int MODE>
 __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
   extern __shared__ float4 lds4[];
@@ -1011,6 +1013,7 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   constexpr int H = SU / 2;  // units each half of a row's lanes converts
   constexpr int NB = 5;      // table chunks per thread loaded ahead of the activations
   static_assert(DEPTH == 2 || DEPTH == 3, "the ring below holds two or three tiles");
+  constexpr int NV = MODE == kGated ? 2 : 1;  // weight streams per column tile
   const int M = a.M;
   const int K = a.K;
   const int U = a.U;
@@ -1035,12 +1038,13 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   uint32_t* lds = reinterpret_cast<uint32_t*>(lds4);
   uint32_t* stage = lds + wave * kStage;
   float* part = reinterpret_cast<float*>(lds + W * kStage);
-  uint32_t* s_tab = lds + W * kStage + RT * W * 128;
-  uint32_t* z_tab = s_tab + RT * 16 * GP;
-  const char* qbase = reinterpret_cast<const char*>(a.q[stream]);
-  const char* sbase = reinterpret_cast<const char*>(a.s[stream]);
-  const char* zbase = reinterpret_cast<const char*>(a.z[stream]);
-  float* const yout = a.out[stream];
+  // Tables of stream v: s_tab + v * RT * 16 * GP (and z_tab likewise).
+  uint32_t* s_tab = lds + W * kStage + NV * RT * W * 128;
+  uint32_t* z_tab = s_tab + NV * RT * 16 * GP;
+  auto qbase = [&](int v) { return reinterpret_cast<const char*>(a.q[NV == 2 ? v : stream]); };
+  auto sbase = [&](int v) { return reinterpret_cast<const char*>(a.s[NV == 2 ? v : stream]); };
+  auto zbase = [&](int v) { return reinterpret_cast<const char*>(a.z[NV == 2 ? v : stream]); };
+  float* const yout = a.out[NV == 2 ? 0 : stream];
 
   // Load layout: instruction j, lane l carries unit t of column col, where
   // 64j + l = SU*col + t.  The same unit goes to stage dword col*CS + 4t.
@@ -1068,11 +1072,16 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
     const int ncr = (int)((ce < c_lo + 16 * rn ? ce : c_lo + 16 * rn) - c_lo);
     const int nel = ncr * G;
     const int nchunk = (nel + 3) >> 2;
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(sbase + c_lo * (int64_t)G * 4), (short)0, nel * 4,
-                                                      kBufferWord3);
-    const auto rz = __builtin_amdgcn_make_buffer_rsrc((void*)(zbase + c_lo * (int64_t)G * 4), (short)0, nel * 4,
-                                                      kBufferWord3);
-    auto table_put = [&](int c, u32x4 sv, u32x4 zv) {
+    const int vn = NV * rn;  // tiles of the round over all streams
+    auto table_rsrc = [&](const char* base) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + c_lo * (int64_t)G * 4), (short)0, nel * 4,
+                                               kBufferWord3);
+    };
+    const auto rs = table_rsrc(sbase(0));
+    const auto rz = table_rsrc(zbase(0));
+    auto table_put = [&](int c, u32x4 sv, u32x4 zv, int v = 0) {
+      uint32_t* st_ = s_tab + v * RT * 16 * GP;
+      uint32_t* zt_ = z_tab + v * RT * 16 * GP;
       if (c >= nchunk) return;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1087,8 +1096,8 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
             g += G;
           }
           const uint32_t zi = (uint32_t)bitsf(zv[k]);
-          s_tab[col * GP + g] = sv[k];
-          z_tab[col * GP + g] = zi | (zi << 16);
+          st_[col * GP + g] = sv[k];
+          zt_[col * GP + g] = zi | (zi << 16);
         }
       }
     };
@@ -1099,11 +1108,13 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
       tsv[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadNonTemporal));
       tzv[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, kLoadNonTemporal));
     }
-    for (int col = wave; col < ncr; col += W)
-      if (lane < GP - G) {
-        s_tab[col * GP + G + lane] = 0u;
-        z_tab[col * GP + G + lane] = 0u;
-      }
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      for (int col = wave; col < ncr; col += W)
+        if (lane < GP - G) {
+          s_tab[v * RT * 16 * GP + col * GP + G + lane] = 0u;
+          z_tab[v * RT * 16 * GP + col * GP + G + lane] = 0u;
+        }
 
     bool first_pass = true;
     for (int sl = wave; sl < nsl; sl += W) {
@@ -1156,17 +1167,29 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
           const u32x4 zv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)c * 16u, 0, kLoadNonTemporal));
           table_put(c, sv, zv);
         }
+        if constexpr (NV == 2) {  // the up stream's table
+          const auto rs1 = table_rsrc(sbase(1));
+          const auto rz1 = table_rsrc(zbase(1));
+          for (int c = tid; c < nchunk; c += (int)blockDim.x) {
+            const u32x4 sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs1, (uint32_t)c * 16u, 0, kLoadNonTemporal));
+            const u32x4 zv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz1, (uint32_t)c * 16u, 0, kLoadNonTemporal));
+            table_put(c, sv, zv, 1);
+          }
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_s_barrier();
       }
 
-      // Tile ti of the block; tiles past the round read nothing (an empty
-      // buffer range), so every load is unconditional.
-      auto load = [&](int ti, SliceTile<SU>& r) {
-        const bool live = ti < r0 + rn;
-        const int64_t col0 = cb + 16 * (int64_t)(live ? ti : r0);
+      // Tile vt of the round (stream vt / rn, column tile vt % rn); tiles
+      // past the round read nothing (an empty buffer range), so every load
+      // is unconditional.
+      auto load = [&](int vt, SliceTile<SU>& r) {
+        const bool live = vt < vn;
+        const int v = NV == 2 && live && vt >= rn ? 1 : 0;
+        const int ti = live ? vt - v * rn : 0;
+        const int64_t col0 = cb + 16 * (int64_t)(r0 + ti);
         const int ncols = live ? (ce - col0 < 16 ? (int)(ce - col0) : 16) : 0;
-        const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + col0 * (int64_t)U * 16), (short)0,
+        const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(qbase(v) + col0 * (int64_t)U * 16), (short)0,
                                                           ncols * U * 16, kBufferWord3);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
@@ -1183,7 +1206,7 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
       // operand is built, when the activations' registers are free.
       SliceTile<SU> ring[DEPTH];
 #pragma unroll
-      for (int d = 0; d + 1 < DEPTH; ++d) load(r0 + d, ring[d]);
+      for (int d = 0; d + 1 < DEPTH; ++d) load(d, ring[d]);
       __builtin_amdgcn_sched_barrier(0);
 
       // The slice's A operand.  The row maximum is reduced over the row's 8
@@ -1238,17 +1261,19 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
           f[r] = pow2f(24 - (rbase ? e_hi : e_lo));
         }
       }
-      load(r0 + DEPTH - 1, ring[DEPTH - 1]);
+      load(DEPTH - 1, ring[DEPTH - 1]);
       __builtin_amdgcn_sched_barrier(0);
       const int rem0 = u0 - h0 * gsu;  // unit-in-group of the slice's first unit
 
-      auto compute = [&](int i) {
+      auto compute = [&](int vt) {
         const uint32_t* cs = stage + lo16 * CS + hi4;
-        // The lane's column in the round (the round's last one past its
-        // end) and the slice's first group.
+        // The tile's stream and column tile; the lane's column in the round
+        // (the round's last one past its end) and the slice's first group.
+        const int vs = NV == 2 && vt >= rn ? 1 : 0;
+        const int i = vt - vs * rn;
         const int colr = 16 * i + lo16 < ncr ? 16 * i + lo16 : ncr - 1;
-        const uint32_t* ts = s_tab + colr * GP + h0;
-        const uint32_t* tz = z_tab + colr * GP + h0;
+        const uint32_t* ts = s_tab + vs * RT * 16 * GP + colr * GP + h0;
+        const uint32_t* tz = z_tab + vs * RT * 16 * GP + colr * GP + h0;
         uint32_t wd[SU];
 #pragma unroll
         for (int t = 0; t < SU; ++t) wd[t] = cs[4 * t];
@@ -1310,7 +1335,7 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) v[rr] = add_swap32(acc[rr], acc[rr]) * f[rr];
         if (hi4 < 2) {
-          float* pp = part + ((size_t)(i * W + wave) * 8 + 4 * hi4) * 16 + lo16;
+          float* pp = part + ((size_t)(vt * W + wave) * 8 + 4 * hi4) * 16 + lo16;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) pp[16 * rr] = first_pass ? v[rr] : pp[16 * rr] + v[rr];
         }
@@ -1320,13 +1345,13 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
       // (tiles past the round read nothing), one back edge, so each stage
       // write waits only for its own slot; only the compute is skipped past
       // the round's last tile.
-      for (int i = 0; i < rn; i += DEPTH) {
+      for (int i = 0; i < vn; i += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
           write_stage(ring[d]);
-          load(r0 + i + d + DEPTH, ring[d]);
+          load(i + d + DEPTH, ring[d]);
           __builtin_amdgcn_sched_barrier(0);
-          if (i + d < rn) compute(i + d);
+          if (i + d < vn) compute(i + d);
         }
       }
       // The refills past the round are still in flight; let them land before
@@ -1347,6 +1372,12 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
         const float* pp = part + ((size_t)(i * W) * 8 + mm) * 16 + c;
         float y = pp[0];
         for (int w = 1; w < W; ++w) y += pp[(size_t)w * 128];
+        if constexpr (NV == 2) {  // y is g; u from the up stream's tile rn + i
+          const float* pu = part + ((size_t)((rn + i) * W) * 8 + mm) * 16 + c;
+          float u = pu[0];
+          for (int w = 1; w < W; ++w) u += pu[(size_t)w * 128];
+          y = silu_f32(y) * u;
+        }
         yout[(int64_t)mm * N + col] = y;
       }
     }
@@ -1433,6 +1464,7 @@ hipError_t dispatch_slice(Mode mode, const GemvArgs& a, const LaunchShape& s, hi
     case kDual: return dispatch_slice_mode<kDual>(a, s, st, occ);
     case kSigIn: return dispatch_slice_mode<kSigIn>(a, s, st, occ);
     case kSwiIn: return dispatch_slice_mode<kSwiIn>(a, s, st, occ);
+    case kGated: return dispatch_slice_mode<kGated>(a, s, st, occ);
     default: return hipErrorInvalidValue;  // no matrix-core form of this mode
   }
 }

@@ -361,3 +361,43 @@ def test_lanes_variants_reject_nine_lanes(q4):
         q4.int4_matvec_dual(Xd, *w, *w)
     with pytest.raises(q4.Int4Error):
         q4.int4_matvec_swiglu_gated(Xd, Xd, *w)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+@pytest.mark.parametrize("N,K,gs", LANE_SHAPES)
+def test_gated_lanes(q4, M, N, K, gs):
+    qg, sg, zg = quantized(0xFB00 + N, N, K, gs)
+    qu, su, zu = quantized(0xFB01 + N, N, K, gs)
+    X = synth.lanes(0xFB02 + M, M, K)
+    Xd, *w = to_dev(X, qg.view(np.int32), sg, zg, qu.view(np.int32), su, zu)
+    H = host(q4.int4_matvec_gated_lanes(Xd, *w))
+    assert H.shape == (M, N)
+    for m in range(M):
+        ref = oracle.gated(X[m], qg, sg, zg, qu, su, zu, K, gs)
+        tol = gated_tolerance(ref)
+        err = np.abs(H[m].astype(np.float64) - ref["h"])
+        assert np.all(err <= tol), f"gated lanes m={m}: max err/tol {np.max(err / tol)}"
+    # g and u are int4_matvec's sums at the same M, bit for bit: only
+    # silu(g) * u rounds.
+    g = host(q4.int4_matvec(Xd, *w[:3])).astype(np.float64)
+    u = host(q4.int4_matvec(Xd, *w[3:])).astype(np.float64)
+    assert close_ulps(H, g / (1.0 + np.exp(-g)) * u)
+    if M == 1:
+        np.testing.assert_array_equal(bits(H[0]), bits(host(q4.int4_matvec_gated(Xd[0], *w))))
+
+
+def test_gated_lanes_table_limit(q4):
+    # Both streams' scale / zero tables share the LDS: 512 groups per column
+    # fit the plain lanes call but not the gated one.
+    N, K, gs = 40, 16384, 32
+    rng = np.random.default_rng(0xFB10)
+    q = rng.integers(0, 2**32, (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    s = np.full((N, K // gs), 1e-3, np.float32)
+    z = rng.integers(0, 16, (N, K // gs)).astype(np.float32)
+    X = synth.lanes(0xFB11, 2, K)
+    Xd, qd, sd, zd = to_dev(X, q.view(np.int32), s, z)
+    Y = host(q4.int4_matvec(Xd, qd, sd, zd))
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    assert_dot_close(Y, Y_ref, B, "plain lanes at 512 groups")
+    with pytest.raises(q4.Int4Error):
+        q4.int4_matvec_gated_lanes(Xd, qd, sd, zd, qd, sd, zd)
