@@ -16,7 +16,8 @@ N*(K/gs)*8 + fp32 activations in + fp32 outputs out (what the method must move).
 
 Next-row calls (the fused variants beside the hot path) are timed the same
 way and reported under "next_rows"; they are not part of the step:
-  dual     x[4096] . W0, W1 [4096, 4096]                                 (gs 128)
+  dual     x[4096] . W0, W1 [4096, 4096]                                 (gs 128), and M = 4 lanes
+  gated4   silu(X . Wg) * (X . Wu) for M = 4 lanes, the c3 gate/up weights (gs 128)
   sig      (a * sigmoid(gate))[4096] . W[4096, 4096]                      (gs 128)
   swiglu   (silu(gate) * up)[8192] . W[4096, 8192]                        (gs 128)
   normswi  silu(x . Wg) * (x . Wu), x = RMSNorm(a_a + a_b) * w_norm, [14336, 4096] (gs 128)
@@ -229,6 +230,14 @@ def build_next(q4, torch, dev):
                       lambda s: q4.int4_matvec_dual(x1, *s, y0=y1[0], y1=y1[1]),
                       lambda r: clones(w1, r), wbytes(w1)))
 
+    # M = 4 decode lanes of the same calls (matrix-core kernel).
+    X1 = torch.from_numpy(synth.lanes(0x604, 4, n1["K"])).to(dev)
+    Y1 = (torch.empty((4, n1["N"]), device=dev), torch.empty((4, n1["N"]), device=dev))
+    b1m = 2 * alg_bytes(n1["N"], n1["K"], n1["gs"], 0, 4 * n1["N"]) + 4 * 4 * n1["K"]
+    calls.append(Call(f"dual M=4 2x{n1['N']}x{n1['K']}", b1m,
+                      lambda s: q4.int4_matvec_dual(X1, *s, y0=Y1[0], y1=Y1[1]),
+                      lambda r: clones(w1, r), wbytes(w1)))
+
     i2 = synth.n2_inputs()
     w2 = quantize(i2["W"], n2["gs"])
     a2 = [torch.from_numpy(i2[k]).to(dev) for k in ("a", "gate")]
@@ -246,6 +255,17 @@ def build_next(q4, torch, dev):
     calls.append(Call(f"swiglu-gated {n3['N']}x{n3['K']}", b3,
                       lambda s: q4.int4_matvec_swiglu_gated(*a3, *s, y=y3),
                       lambda r: clones(w3, r), wbytes(w3)))
+
+    i3g = synth.c3_inputs()
+    c3 = synth.CONFIGS["c3"]
+    w3g = (*quantize(i3g["Wg"], c3["gs"]), *quantize(i3g["Wu"], c3["gs"]))
+    del i3g
+    X3 = torch.from_numpy(synth.lanes(0x305, 4, c3["K"])).to(dev)
+    H3 = torch.empty((4, c3["N"]), device=dev)
+    b3m = 2 * alg_bytes(c3["N"], c3["K"], c3["gs"], 0, 0) + 4 * 4 * c3["K"] + 4 * 4 * c3["N"]
+    calls.append(Call(f"gated M=4 2x{c3['N']}x{c3['K']}", b3m,
+                      lambda s: q4.int4_matvec_gated_lanes(X3, *s, H=H3),
+                      lambda r: clones(w3g, r), wbytes(w3g)))
 
     i4 = synth.n4_inputs()
     w4 = (*quantize(i4["Wg"], n4["gs"]), *quantize(i4["Wu"], n4["gs"]))
