@@ -724,7 +724,7 @@ int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales,
   if ((uint64_t)N * (uint64_t)K / 2 >= ((uint64_t)1 << 31))
     return fail(INT4_ERR_SHAPE, "N*K/2 = %llu bytes of codes exceed 2^31", (unsigned long long)N * K / 2);
   const GemmLayout L = gemm_layout(T, N, K, group_size);
-  if ((uint64_t)L.Tp * (uint64_t)L.Kp * 4 >= ((uint64_t)1 << 40) || L.Tp / 128 * (L.Np / 128) >= ((int64_t)1 << 31))
+  if ((uint64_t)L.Tp * (uint64_t)L.Kp * 4 >= ((uint64_t)1 << 40) || L.Tp / 128 * (L.Np / 128) >= ((int64_t)1 << 30))
     return fail(INT4_ERR_SHAPE, "T=%lld is larger than supported", (long long)T);
   if (!X || !q || !scales || !zeros || !Y) return fail(INT4_ERR_NULL, "X, q, scales, zeros and Y are required");
   if (!workspace) return fail(INT4_ERR_NULL, "workspace is required (int4_gemm_workspace_bytes)");
@@ -758,7 +758,11 @@ int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales,
   a.Np = L.Np;
   a.Gp = L.Gp;
   a.RB = L.Tp / 128;
-  a.CB = L.Np / 128;
+  // 128 x 256 tiles halve the activation bytes each CU loads per product
+  // (the activations are re-read once per column tile); they need enough
+  // row blocks to keep the CUs busy, so short prompts use 128 x 128.
+  a.BN = gemm_block_cols(L.Tp, group_size);
+  a.CB = (N + a.BN - 1) / a.BN;
   a.qbytes = (int64_t)(N * K / 2);
   a.K = (int32_t)K;
   a.Kp = (int32_t)L.Kp;

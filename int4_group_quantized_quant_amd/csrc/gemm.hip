@@ -47,7 +47,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kTile = 128;      // rows and columns of a block tile
+constexpr int kTile = 128;      // rows of a block tile
 constexpr int kStageK = 64;     // inputs per LDS stage
 // LDS stage layout: planes of 128 rows (or columns) x 16 bytes, plane stride
 // 516 dwords (4 pad).  A fragment read (16 consecutive rows of one plane per
@@ -56,10 +56,7 @@ constexpr int kStageK = 64;     // inputs per LDS stage
 constexpr int kPlane = kTile * 4 + 4;
 constexpr int kAPlanes = 16;    // 8-input block b of the stage: plane 2b (hi), 2b + 1 (lo)
 constexpr int kBPlanes = 8;     // B fragment of code word w of the stage: plane w
-constexpr int kSCWords = 256;   // scales, 2 steps x 128 columns
 constexpr int kAWords = kAPlanes * kPlane;
-constexpr int kBWords = kBPlanes * kPlane;
-constexpr int kStageWords = kAWords + kBWords + kSCWords;
 constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords
 
@@ -164,22 +161,41 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------ GEMM
 
+// Block tile 128 x BN (BN = 128 or 256): WC = BN / 64 waves across the
+// columns, 8 / WC across the rows, each wave 64 columns x (128 / (8 / WC))
+// rows as RW x 4 MFMA tiles.
+template <int BN>
+struct TileShape {
+  static constexpr int WC = BN / 64;
+  static constexpr int WR = 8 / WC;
+  static constexpr int RW = 128 / WR / 16;         // 16-row MFMA tiles per wave
+  static constexpr int BPlane = BN * 4 + 4;        // dwords per B-fragment plane
+  static constexpr int BWords = kBPlanes * BPlane;
+  static constexpr int SCWords = 2 * BN;           // scales, 2 steps x BN columns
+  static constexpr int StageWords = kAWords + BWords + SCWords;
+  static constexpr int WPT = BN / 64;              // code words per thread per stage (2 or 4)
+};
+
+template <int BN>
 struct Prefetch {
-  u32x4 a[4];   // activation pieces c = tid + 512 i
-  u32x2 w;      // code words 2 (t % 4) .. +1 of column t / 4
-  uint32_t zh;  // zero point pair of that column for the words' step
-  uint32_t sc;  // scale of column t % 128 for step (t / 128) % 2 (used by t < 256)
+  u32x4 a[4];                   // activation pieces c = tid + 512 i
+  uint32_t w[TileShape<BN>::WPT];  // code words of one column, one step
+  uint32_t zh;                  // that column's zero-point pair for the step
+  uint32_t sc;                  // one scale of the stage
 };
 
 // GSTEPS = group size / 32 when it is 1, 2 or 4 (group ends known at
 // compile time), 0 for any other group size.
-template <int GSTEPS>
-__global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
+template <int GSTEPS, int BN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_int4_kernel(GemmArgs a) {
+  using TS = TileShape<BN>;
+  constexpr int RW = TS::RW;
   extern __shared__ uint32_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-  const int wr = wave & 3, wc = wave >> 2;  // rows 32 wr .. +31, columns 64 wc .. +63
+  const int wr = wave % TS::WR, wc = wave / TS::WR;  // rows 16 RW wr .., columns 64 wc ..
   const int l16 = lane & 15, q4 = lane >> 4;
 
   // XCD-aware order: XCD x (= block id mod 8) takes a contiguous run of
@@ -192,11 +208,15 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   const int64_t rem = item - rb * a.CB * a.S;
   const int64_t cb = rem / a.S;
   const int part = (int)(rem - cb * a.S);
-  const int64_t m0 = rb * kTile, n0 = cb * kTile;
+  const int64_t m0 = rb * kTile, n0 = cb * BN;
   const int nst_all = a.Kp / kStageK;
-  // K parts cover whole groups when the group spans two stages.
+  // Sums are closed once per stage when a stage never straddles a group
+  // (GSTEPS 2, and GSTEPS 4 on the wide tile, where the second register
+  // set of a group spanning two stages would not fit); otherwise per group.
+  constexpr bool kStageFlush = GSTEPS == 2 || (GSTEPS == 4 && BN == 256);
+  // K parts cover whole groups when a group's sums span two stages.
   int per = (nst_all + a.S - 1) / a.S;
-  if (GSTEPS == 4) per = (per + 1) & ~1;
+  if (GSTEPS == 4 && !kStageFlush) per = (per + 1) & ~1;
   const int st_begin = part * per;
   const int st_end = st_begin + per < nst_all ? st_begin + per : nst_all;
   if (st_begin >= st_end) return;  // an empty K part adds nothing (Y starts at 0)
@@ -206,17 +226,20 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
 
   // Stage loads (all unconditional, so every wait is exact).  Activations:
   // 128 rows x 256 bytes, thread t takes the 16-byte pieces t + 512 i.
-  // Codes: thread t takes words 2 (t % 4), +1 of column t / 4 through a
-  // buffer resource (columns past N and words past the matrix read 0), and
-  // that column's zero point for the words' step.  Scales: thread t takes
-  // column t % 128 of step (t / 128) % 2.
+  // Codes: the stage's 8 words of each column are split into WPT-word runs,
+  // one per thread, through a buffer resource (columns past N and words past
+  // the matrix read 0), with that column's zero point for the run's step.
+  // Scales: thread t takes column t % BN of step t / BN (BN = 128: threads
+  // t < 256 store).
   const int64_t xrow = a.Kp;  // dwords per token row
   const uint32_t* xsb = a.xs + m0 * xrow;
-  const int wcol = tid >> 2, wpair = tid & 3, wstep = wpair >> 1;
+  constexpr int RUNS = 8 / TS::WPT;  // runs per column (4 or 2)
+  const int wcol = tid / RUNS, wrun = tid % RUNS;
+  const int wstep = wrun * TS::WPT / 4;
   const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.q, (short)0, (int)a.qbytes, kBufferWord3);
-  const uint32_t qcol_off = (uint32_t)(n0 + wcol) * (uint32_t)(a.K / 2) + (uint32_t)wpair * 8u;
-  const int scstep = (tid >> 7) & 1, sccol = tid & 127;
+  const uint32_t qcol_off = (uint32_t)(n0 + wcol) * (uint32_t)(a.K / 2) + (uint32_t)(wrun * TS::WPT * 4);
+  const int scstep = (tid / BN) & 1, sccol = tid % BN;
   auto group_of = [&](int kk) -> int64_t {
     if constexpr (GSTEPS == 1) return kk;
     else if constexpr (GSTEPS == 2) return kk >> 1;
@@ -224,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
     else return kk / gsteps;
   };
 
-  auto load_stage = [&](int st, Prefetch& p) {
+  auto load_stage = [&](int st, Prefetch<BN>& p) {
     const int64_t kw = (int64_t)st * (kStageK / 8) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -232,18 +255,26 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
       const int row = c >> 4, piece = c & 15;
       p.a[i] = *reinterpret_cast<const u32x4*>(xsb + row * xrow + kw + piece * 4);
     }
-    p.w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                        qr, qcol_off + (uint32_t)(st * (kStageK / 2)), 0, 0));
+    const uint32_t off = qcol_off + (uint32_t)(st * (kStageK / 2));
+    if constexpr (TS::WPT == 2) {
+      const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qr, off, 0, 0));
+      p.w[0] = v[0];
+      p.w[1] = v[1];
+    } else {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+#pragma unroll
+      for (int h = 0; h < 4; ++h) p.w[h] = v[h];
+    }
     p.zh = a.zt[group_of(2 * st + wstep) * a.Np + n0 + wcol];
     p.sc = __builtin_bit_cast(uint32_t, a.st[group_of(2 * st + scstep) * a.Np + n0 + sccol]);
   };
   // LDS stage: activation planes (piece p of a row's 256 bytes is plane p),
   // B fragment planes (fragment of step ks, lane group q: plane 4 ks + q),
-  // scales [2 steps][128 columns].
-  auto store_stage = [&](int slot, const Prefetch& p) {
-    uint32_t* sa = lds + slot * kStageWords;
+  // scales [2 steps][BN columns].
+  auto store_stage = [&](int slot, const Prefetch<BN>& p) {
+    uint32_t* sa = lds + slot * TS::StageWords;
     uint32_t* sb = sa + kAWords;
-    uint32_t* ss = sb + kBWords;
+    uint32_t* ss = sb + TS::BWords;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + kThreads * i;
@@ -252,22 +283,22 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
     }
     const half2_t z0 = as_half2(p.zh), z1 = as_half2(p.zh << 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < TS::WPT; ++h) {
       const uint32_t w = p.w[h], w8 = w >> 8;
       u32x4 bw;
       bw[0] = __builtin_bit_cast(uint32_t, as_half2(w & 0x000F000Fu) - z0);
       bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
       bw[2] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x000F000Fu) - z0);
       bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
-      *reinterpret_cast<u32x4*>(sb + (2 * wpair + h) * kPlane + wcol * 4) = bw;
+      *reinterpret_cast<u32x4*>(sb + (wrun * TS::WPT + h) * TS::BPlane + wcol * 4) = bw;
     }
-    if (tid < 256) ss[tid] = p.sc;
+    if (tid < TS::SCWords) ss[tid] = p.sc;
   };
 
   const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t acc[2][4], tmp[2][4];
+  f32x4_t acc[RW][4], tmp[RW][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RW; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[i][j] = z4;
@@ -281,34 +312,33 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
     u32x4 bf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const u32x4*>(sb + (ks * 4 + q4) * kPlane + (64 * wc + 16 * j + l16) * 4);
-    u32x4 ah[2], al[2];
+      bf[j] = *reinterpret_cast<const u32x4*>(sb + (ks * 4 + q4) * TS::BPlane + (64 * wc + 16 * j + l16) * 4);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t* pa = sa + 2 * (ks * 4 + q4) * kPlane + (32 * wr + 16 * i + l16) * 4;
-      ah[i] = *reinterpret_cast<const u32x4*>(pa);
-      al[i] = *reinterpret_cast<const u32x4*>(pa + kPlane);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t* pa = sa + 2 * (ks * 4 + q4) * kPlane + (16 * RW * wr + 16 * i + l16) * 4;
+      const u32x4 ah = *reinterpret_cast<const u32x4*>(pa);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah[i]),
+        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah),
                                                            __builtin_bit_cast(half8_t, bf[j]),
                                                            first ? z4 : tmp[i][j], 0, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t* pa = sa + 2 * (ks * 4 + q4) * kPlane + (16 * RW * wr + 16 * i + l16) * 4;
+      const u32x4 al = *reinterpret_cast<const u32x4*>(pa + kPlane);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al[i]),
+        tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al),
                                                            __builtin_bit_cast(half8_t, bf[j]),
                                                            tmp[i][j], 0, 0, 0);
+    }
     if (last) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sc = bitsf(ss[ks * 128 + 64 * wc + 16 * j + l16]);
+        const float sc = bitsf(ss[ks * BN + 64 * wc + 16 * j + l16]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < RW; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, tmp[i][j][r], acc[i][j][r]);
       }
@@ -319,15 +349,15 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   // general case tests the step index, and every case closes the sums at
   // the part's last step.
   auto compute = [&](int slot, int st, int phase) {
-    const uint32_t* sa = lds + slot * kStageWords;
+    const uint32_t* sa = lds + slot * TS::StageWords;
     const uint32_t* sb = sa + kAWords;
-    const uint32_t* ss = sb + kBWords;
+    const uint32_t* ss = sb + TS::BWords;
     const int kk = 2 * st;
     const bool end_part = kk + 1 == last_step;
     if constexpr (GSTEPS == 1) {
       step(sa, sb, ss, 0, true, true);
       step(sa, sb, ss, 1, true, true);
-    } else if constexpr (GSTEPS == 2) {
+    } else if constexpr (kStageFlush) {
       step(sa, sb, ss, 0, true, false);
       step(sa, sb, ss, 1, false, true);
     } else if constexpr (GSTEPS == 4) {
@@ -358,32 +388,54 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
   // is written to the other LDS slot after it.  Past the part's last stage
   // the loads re-read it, so the count in flight is fixed.
   auto clamp = [&](int x) { return x < st_end ? x : st_end - 1; };
-  Prefetch p0, p1;
-  load_stage(st_begin, p0);
-  load_stage(clamp(st_begin + 1), p1);
-  store_stage(0, p0);
-  __syncthreads();
-  int st = st_begin;
-  while (true) {
-    load_stage(clamp(st + 2), p0);
-    compute(0, st, 0);
-    store_stage(1, p1);
-    __syncthreads();
-    if (++st >= st_end) break;
-    load_stage(clamp(st + 2), p1);
-    compute(1, st, 1);
+  if constexpr (BN == 128) {
+    Prefetch<BN> p0, p1;
+    load_stage(st_begin, p0);
+    load_stage(clamp(st_begin + 1), p1);
     store_stage(0, p0);
     __syncthreads();
-    if (++st >= st_end) break;
+    int st = st_begin;
+    while (true) {
+      load_stage(clamp(st + 2), p0);
+      compute(0, st, 0);
+      store_stage(1, p1);
+      __syncthreads();
+      if (++st >= st_end) break;
+      load_stage(clamp(st + 2), p1);
+      compute(1, st, 1);
+      store_stage(0, p0);
+      __syncthreads();
+      if (++st >= st_end) break;
+    }
+  } else {
+    // The wide tile holds twice the accumulators: one register set, loads
+    // one stage ahead (a stage's products take twice as long to hide them).
+    Prefetch<BN> p0;
+    load_stage(st_begin, p0);
+    store_stage(0, p0);
+    __syncthreads();
+    int st = st_begin;
+    while (true) {
+      load_stage(clamp(st + 1), p0);
+      compute(0, st, 0);
+      store_stage(1, p0);
+      __syncthreads();
+      if (++st >= st_end) break;
+      load_stage(clamp(st + 1), p0);
+      compute(1, st, 1);
+      store_stage(0, p0);
+      __syncthreads();
+      if (++st >= st_end) break;
+    }
   }
 
   // Y = total * 2^(24 - e_t); with K split in two, the two halves are added
   // into Y (zeroed by the prep launch), an order-independent sum.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RW; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + 32 * wr + 16 * i + 4 * q4 + r;
+      const int64_t row = m0 + 16 * RW * wr + 16 * i + 4 * q4 + r;
       if (row >= a.T) continue;
       const float f = a.fac[row];
 #pragma unroll
@@ -397,36 +449,53 @@ __global__ __launch_bounds__(kThreads) void gemm_int4_kernel(GemmArgs a) {
 }
 
 // Dynamic LDS beyond 64 KiB must be allowed once per kernel.
-template <int GSTEPS>
-hipError_t launch_gemm_kernel(dim3 grid, size_t lds, hipStream_t stream, const GemmArgs& a) {
+template <int GSTEPS, int BN>
+hipError_t launch_gemm_kernel(dim3 grid, hipStream_t stream, const GemmArgs& a) {
   static std::atomic<bool> raised{false};  // one per instantiation
+  const size_t lds = gemm_lds_bytes(BN);
   if (!raised.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_int4_kernel<GSTEPS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_int4_kernel<GSTEPS, BN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     raised.store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(gemm_int4_kernel<GSTEPS>, grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((gemm_int4_kernel<GSTEPS, BN>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_128(dim3 grid, hipStream_t stream, const GemmArgs& a) {
+  switch (a.gs) {
+    case 32: return launch_gemm_kernel<1, 128>(grid, stream, a);
+    case 64: return launch_gemm_kernel<2, 128>(grid, stream, a);
+    case 128: return launch_gemm_kernel<4, 128>(grid, stream, a);
+    default: return launch_gemm_kernel<0, 128>(grid, stream, a);
+  }
+}
+
+// The wide tile is built for group sizes 64 and 128 only (gemm_block_cols).
+hipError_t launch_gemm_256(dim3 grid, hipStream_t stream, const GemmArgs& a) {
+  switch (a.gs) {
+    case 64: return launch_gemm_kernel<2, 256>(grid, stream, a);
+    case 128: return launch_gemm_kernel<4, 256>(grid, stream, a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-size_t gemm_lds_bytes() { return (size_t)2 * kStageWords * sizeof(uint32_t); }
+int gemm_block_cols(int64_t Tp, int32_t gs) { return Tp >= 1024 && (gs == 64 || gs == 128) ? 256 : 128; }
+
+size_t gemm_lds_bytes(int bn) {
+  return (size_t)2 * (bn == 256 ? TileShape<256>::StageWords : TileShape<128>::StageWords) * sizeof(uint32_t);
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = gemm_lds_bytes();
   const int64_t prep_blocks = a.Tp + (a.Np / 32) * ((a.Gp + 31) / 32);
   hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.RB * a.CB * a.S));
-  switch (a.gs) {
-    case 32: return launch_gemm_kernel<1>(grid, lds, stream, a);
-    case 64: return launch_gemm_kernel<2>(grid, lds, stream, a);
-    case 128: return launch_gemm_kernel<4>(grid, lds, stream, a);
-    default: return launch_gemm_kernel<0>(grid, lds, stream, a);
-  }
+  return a.BN == 256 ? launch_gemm_256(grid, stream, a) : launch_gemm_128(grid, stream, a);
 }
 
 }  // namespace int4gemv

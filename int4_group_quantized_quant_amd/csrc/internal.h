@@ -133,8 +133,8 @@ int max_ncol(Mode mode, int M, int variant);
 //   fac  [Tp] 2^(24 - e_t) per token row (0 for the pad rows)
 //   st   [Gp][Np] scales, transposed; zt [Gp][Np] zero points as fp16
 //        subnormal pairs (zero | zero << 16), transposed; 0 outside the matrix
-// with Tp, Np = T, N rounded up to 128, Kp = K rounded up to 64,
-// Gp = ceil(Kp / gs).
+// with Tp = T rounded up to 128, Np = N rounded up to 256, Kp = K rounded
+// up to 64, Gp = ceil(Kp / gs).
 struct GemmArgs {
   const float* X;     // [T][K]
   const float* s;     // [N][G]
@@ -148,7 +148,8 @@ struct GemmArgs {
   int64_t T, N, Tp, Np, Gp, RB, CB;
   int64_t qbytes;  // N * K / 2
   int32_t K, Kp, gs, G;
-  int32_t S;  // K parts per tile (1 or 2)
+  int32_t S;   // K parts per tile (1 or 2)
+  int32_t BN;  // columns per block tile (128 or 256)
 };
 
 struct GemmLayout {
@@ -161,7 +162,7 @@ inline size_t gemm_align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline GemmLayout gemm_layout(int64_t T, int64_t N, int64_t K, int32_t gs) {
   GemmLayout L;
   L.Tp = (T + 127) / 128 * 128;
-  L.Np = (N + 127) / 128 * 128;
+  L.Np = (N + 255) / 256 * 256;
   L.Kp = (K + 63) / 64 * 64;
   L.Gp = (L.Kp + gs - 1) / gs;
   L.xs_off = 0;
@@ -172,8 +173,13 @@ inline GemmLayout gemm_layout(int64_t T, int64_t N, int64_t K, int32_t gs) {
   return L;
 }
 
-// Dynamic LDS of the GEMM kernel (two stages).
-size_t gemm_lds_bytes();
+// Columns per block tile: 256 (half the activation bytes per product) when
+// there are enough row blocks to fill the CUs and the group size is 64 or
+// 128, else 128.
+int gemm_block_cols(int64_t Tp, int32_t gs);
+
+// Dynamic LDS of the GEMM kernel (two stages) for block tiles 128 x bn.
+size_t gemm_lds_bytes(int bn);
 
 // The prep launch (split activations, transposed scale / zero tables) and
 // the GEMM launch, in stream order.

@@ -219,9 +219,9 @@ def test_gemm_workspace_and_validation(lib):
     lib.int4_gemm_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
     T, N, K, gs = 5, 77, 96, 96
     need = lib.int4_gemm_workspace_bytes(T, N, K, gs)
-    # Tp=128, Kp=128, Np=128, Gp=2: split activations 128*128*4, factors 128*4,
+    # Tp=128, Kp=128, Np=256, Gp=2: split activations 128*128*4, factors 128*4,
     # two transposed tables 2*128*4 each, every region rounded up to 256 bytes.
-    assert need == 128 * 128 * 4 + 512 + 1024 + 1024
+    assert need == 128 * 128 * 4 + 512 + 2048 + 2048
     assert lib.int4_gemm_workspace_bytes(0, N, K, gs) == 0
     W = 0x90000000
     sz = ctypes.c_size_t

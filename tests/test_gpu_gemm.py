@@ -119,3 +119,24 @@ def test_prefill_full_size_sampled(q4):
     Y = host(q4.int4_gemm(torch.from_numpy(inp["X"]).cuda(), qd, sd, zd))
     Y_ref, B = oracle.matvec(inp["X"][rows], q, s, z, K, gs)
     assert_dot_close(Y[np.ix_(rows, cols)], Y_ref, B, "prefill full size")
+
+
+@pytest.mark.parametrize("T,N,K,gs", [(1100, 300, 2048, 128), (1030, 520, 1024, 64), (2048, 4096, 1024, 128)])
+def test_gemm_wide_tiles(q4, T, N, K, gs):
+    # T >= 1024 with gs 64 / 128 runs 128 x 256 block tiles (the first two
+    # with K split in two, the last without); sampled rows, every column.
+    q, s, z = quantized(0x6500 + T, N, K, gs)
+    X = synth.lanes(0x6501 + T, T, K)
+    Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
+    rng = np.random.default_rng(T)
+    rows = np.array(sorted(set(rng.choice(T, 20, replace=False).tolist()) | {0, 127, 128, T - 1}))
+    Y_ref, B = oracle.matvec(X[rows], q, s, z, K, gs)
+    assert_dot_close(Y[rows], Y_ref, B, f"gemm wide T={T} N={N} K={K} gs={gs}")
+
+
+def test_gemm_wide_tiles_integer_exact(q4):
+    rng = np.random.default_rng(0x6600)
+    T, N, K, gs = 1040, 260, 512, 64
+    q, s, z, X, exact = integer_problem(rng, N, K, gs, M=T)
+    Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
+    np.testing.assert_array_equal(Y, exact.astype(np.float32))
