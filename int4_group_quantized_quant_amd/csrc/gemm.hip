@@ -98,12 +98,31 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
     const int64_t m = blockIdx.x;
     const bool real = m < a.T;
     const float* x = a.X + m * (int64_t)a.K;
+    const int nblk = a.Kp / 8;       // 8-input blocks of the row
+    const int nreal = a.K / 8;       // blocks inside K
+    u32x4* dst = reinterpret_cast<u32x4*>(a.xs + m * (int64_t)nblk * 8);
+    // Rows of up to 512 blocks (K <= 4096) stay in registers between the
+    // maximum and the split: thread t holds blocks t and t + 256.
+    const bool in_regs = nblk <= 512;
+    float4 v[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = tid + 256 * h;
+      const bool ok = in_regs && real && b < nreal;
+      v[2 * h] = ok ? reinterpret_cast<const float4*>(x)[2 * b] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[2 * h + 1] = ok ? reinterpret_cast<const float4*>(x)[2 * b + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float amax = 0.0f;
-    if (real)
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    } else if (real) {
       for (int i = tid; i < (a.K >> 2); i += 256) {
-        const float4 v = reinterpret_cast<const float4*>(x)[i];
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        const float4 w = reinterpret_cast<const float4*>(x)[i];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w))));
       }
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     if ((tid & 63) == 0) red[tid >> 6] = amax;
@@ -114,20 +133,29 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
     if (real && a.S > 1)  // the GEMM adds its K parts into Y
       for (int64_t n = tid; n < a.N; n += 256) a.Y[m * a.N + n] = 0.0f;
     const float fe = pow2f(e), fo = pow2f(e - 4);
-    u32x4* dst = reinterpret_cast<u32x4*>(a.xs + m * (int64_t)(a.Kp / 8) * 8);
-    for (int b = tid; b < a.Kp / 8; b += 256) {
-      uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
-      if (real && 8 * b < a.K) {
-        const float4 p = reinterpret_cast<const float4*>(x)[2 * b];
-        const float4 r = reinterpret_cast<const float4*>(x)[2 * b + 1];
-        // slots 0..7 = inputs 0, 4, 1, 5, 2, 6, 3, 7; odd inputs times 2^-4
-        split2(p.x * fe, r.x * fe, h[0], l[0]);
-        split2(p.y * fo, r.y * fo, h[1], l[1]);
-        split2(p.z * fe, r.z * fe, h[2], l[2]);
-        split2(p.w * fo, r.w * fo, h[3], l[3]);
-      }
+    // slots 0..7 = inputs 0, 4, 1, 5, 2, 6, 3, 7; odd inputs times 2^-4
+    auto split_block = [&](int b, float4 p, float4 r) {
+      uint32_t h[4], l[4];
+      split2(p.x * fe, r.x * fe, h[0], l[0]);
+      split2(p.y * fo, r.y * fo, h[1], l[1]);
+      split2(p.z * fe, r.z * fe, h[2], l[2]);
+      split2(p.w * fo, r.w * fo, h[3], l[3]);
       dst[2 * b] = u32x4{h[0], h[1], h[2], h[3]};
       dst[2 * b + 1] = u32x4{l[0], l[1], l[2], l[3]};
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = tid + 256 * h;
+        if (b < nblk) split_block(b, v[2 * h], v[2 * h + 1]);  // zeros past K and in pad rows
+      }
+    } else {
+      for (int b = tid; b < nblk; b += 256) {
+        const bool ok = real && b < nreal;
+        const float4 p = ok ? reinterpret_cast<const float4*>(x)[2 * b] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 r = ok ? reinterpret_cast<const float4*>(x)[2 * b + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        split_block(b, p, r);
+      }
     }
     return;
   }
