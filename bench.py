@@ -62,7 +62,8 @@ PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 MALL_ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "norm_lmhead_151936x4096_traffic.md")
-KERNEL_SRC = os.path.join(ROOT, "int4_group_quantized_quant_amd", "csrc", "kernels.hip")
+KERNEL_SRC = [os.path.join(ROOT, "int4_group_quantized_quant_amd", "csrc", f)
+              for f in ("kernels.hip", "device_common.h")]
 
 
 def log(msg: str) -> None:
@@ -74,10 +75,13 @@ def alg_bytes(N, K, gs, in_floats, out_floats):
 
 
 def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the kernel source with comments and
-    blank space removed, so comment edits keep a counter summary valid."""
-    with open(KERNEL_SRC) as f:
-        src = f.read()
+    """sha256 (first 16 hex digits) of the norm kernel's sources (kernels.hip
+    and the device helpers it includes) with comments and blank space
+    removed, so comment edits keep a counter summary valid."""
+    src = ""
+    for path in KERNEL_SRC:
+        with open(path) as f:
+            src += f.read()
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())

@@ -30,23 +30,11 @@
 // result stays deterministic.  Blocks are mapped so that each XCD works
 // through consecutive work items of one row block: the row block's
 // activations stay in that XCD's L2 while its columns stream past.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <atomic>
-
-#include "internal.h"
+#include "device_common.h"
 
 namespace int4gemv {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kWave = 64;
 constexpr int kTile = 128;      // rows of a block tile
 constexpr int kStageK = 64;     // inputs per LDS stage
 // LDS stage layout: planes of 128 rows (or columns) x 16 bytes, plane stride
@@ -58,21 +46,6 @@ constexpr int kAPlanes = 16;    // 8-input block b of the stage: plane 2b (hi), 
 constexpr int kBPlanes = 8;     // B fragment of code word w of the stage: plane w
 constexpr int kAWords = kAPlanes * kPlane;
 constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords
-
-__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
-__device__ __forceinline__ half2_t as_half2(uint32_t b) { return __builtin_bit_cast(half2_t, b); }
-__device__ __forceinline__ float pow2f(int e) { return bitsf((uint32_t)(e + 127) << 23); }
-
-// e for a token row whose largest magnitude is amax: amax * 2^e < 2^14.
-__device__ __forceinline__ int token_exponent(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  const int biased = (int)((fbits(amax) >> 23) & 0xFFu);
-  const int E = biased == 0 ? -126 : biased - 126;  // amax < 2^E
-  const int e = 14 - E;
-  return e < -100 ? -100 : (e > 100 ? 100 : e);
-}
 
 // hi and lo of two binary32 values as fp16 pairs, both rounded toward zero.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
@@ -128,7 +101,7 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(GemmArgs a) {
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const int e = token_exponent(amax);
+    const int e = row_exponent(amax);
     if (tid == 0) a.fac[m] = real ? pow2f(24 - e) : 0.0f;
     if (real && a.S > 1)  // the GEMM adds its K parts into Y
       for (int64_t n = tid; n < a.N; n += 256) a.Y[m * a.N + n] = 0.0f;

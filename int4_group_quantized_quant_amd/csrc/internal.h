@@ -107,7 +107,7 @@ inline size_t slice_lds_bytes(int su, int cls, int G, int waves, int rt, int nv 
 struct LaunchShape {
   int variant;        // Variant
   int ncol;           // columns per wave step (1, 2 or 4)
-  int depth;          // register kernel: steps of loads in flight ahead of compute (1 or 2)
+  int depth;          // register kernel: steps of loads in flight ahead of compute (1)
   int block_threads;  // threads per block (multiple of 64)
   int grid;           // blocks
   size_t lds_bytes;   // dynamic LDS per block
@@ -120,6 +120,11 @@ hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& shape, h
 
 // Resident blocks per CU of the kernel `launch_gemv` would run for this shape.
 hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& shape, int* blocks_per_cu);
+
+// The matrix-core lanes kernel (slice.hip) for modes kPlain, kDual, kGated,
+// kSigIn and kSwiIn; launches, or with `occupancy` set only queries.
+hipError_t dispatch_slice(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t stream,
+                          int* occupancy);
 
 // Largest `ncol` instantiated for (mode, M, variant).
 int max_ncol(Mode mode, int M, int variant);
