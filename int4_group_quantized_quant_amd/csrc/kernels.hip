@@ -695,78 +695,101 @@ __device__ __forceinline__ float clamp_code(float v) {
 // read once and no LDS or barrier is involved.  The arithmetic is the same
 // binary32 sequence as quantize_pack_kernel (min/max are exact in any
 // order; a +0/-0 tie cannot change scale or zero).
-template <int WPT>
+// Each wave handles R consecutive batches of 64 / TPG groups; the next
+// batch's loads are issued before the current batch is quantized, so a wave
+// keeps two batches of inputs in flight.
+template <int WPT, int R>
 __global__ __launch_bounds__(256) void quantize_pack_wave_kernel(const float* __restrict__ W,
                                                                  int64_t total_groups, int gs, int tpg,
                                                                  uint32_t* __restrict__ q,
                                                                  float* __restrict__ scales,
                                                                  float* __restrict__ zeros) {
   const int lane = threadIdx.x & 63;
-  const int gpw = 64 / tpg;  // groups per wave
-  const int64_t grp = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * gpw + lane / tpg;
+  const int gpw = 64 / tpg;  // groups per wave and batch
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t grp0 = wave_id * gpw * R + lane / tpg;
   const int part = lane & (tpg - 1);
   const int wpg = gs >> 3;
-  const bool live = grp < total_groups;
-  const float* wg = W + (live ? grp : 0) * gs;
 
-  float v[WPT][8];
-  float lo = INFINITY, hi = -INFINITY;
+  // The batch's inputs: words part + j * tpg of the lane's group (a dead
+  // group reads group 0 and is never stored).
+  auto load = [&](int64_t grp, float (&v)[WPT][8]) {
+    const float* wg = W + (grp < total_groups ? grp : 0) * gs;
 #pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const int wi = part + j * tpg;
-    const bool has = live && wi < wpg;
-    const int wc = has ? wi : 0;
-    const float4 a0 = reinterpret_cast<const float4*>(wg)[2 * wc];
-    const float4 a1 = reinterpret_cast<const float4*>(wg)[2 * wc + 1];
-    v[j][0] = a0.x; v[j][1] = a0.y; v[j][2] = a0.z; v[j][3] = a0.w;
-    v[j][4] = a1.x; v[j][5] = a1.y; v[j][6] = a1.z; v[j][7] = a1.w;
-    if (has) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (v[j][e] < lo) lo = v[j][e];
-        if (v[j][e] > hi) hi = v[j][e];
-      }
+    for (int j = 0; j < WPT; ++j) {
+      const int wi = part + j * tpg;
+      const int wc = wi < wpg ? wi : 0;
+      const float4 a0 = reinterpret_cast<const float4*>(wg)[2 * wc];
+      const float4 a1 = reinterpret_cast<const float4*>(wg)[2 * wc + 1];
+      v[j][0] = a0.x; v[j][1] = a0.y; v[j][2] = a0.z; v[j][3] = a0.w;
+      v[j][4] = a1.x; v[j][5] = a1.y; v[j][6] = a1.z; v[j][7] = a1.w;
     }
-  }
-  for (int o = tpg >> 1; o >= 1; o >>= 1) {
-    const float lo2 = __shfl_xor(lo, o, 64);
-    const float hi2 = __shfl_xor(hi, o, 64);
-    if (lo2 < lo) lo = lo2;
-    if (hi2 > hi) hi = hi2;
-  }
-  if (!live) return;
-  float scale;
-  if (hi > lo) {
-    const float range = hi - lo;
-    scale = range / 15.0f;
-  } else {
-    scale = fabsf(hi) / 15.0f;
-  }
-  float zero = 0.0f;
-  if (scale == 0.0f) {
-    scale = 0.0f;
-  } else {
-    const float neg_lo = -lo;
-    zero = clamp_code(rintf(neg_lo / scale));
-  }
-  if (part == 0) {
-    scales[grp] = scale;
-    zeros[grp] = zero;
-  }
+  };
+  auto quantize = [&](int64_t grp, const float (&v)[WPT][8]) {
+    float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const int wi = part + j * tpg;
-    if (wi < wpg) {
-      uint32_t word = 0u;
-      if (scale != 0.0f) {
+    for (int j = 0; j < WPT; ++j) {
+      if (part + j * tpg < wpg) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float code = clamp_code(rintf(v[j][e] / scale) + zero);
-          word |= (uint32_t)code << (4 * e);
+          if (v[j][e] < lo) lo = v[j][e];
+          if (v[j][e] > hi) hi = v[j][e];
         }
       }
-      q[grp * wpg + wi] = word;
     }
+    for (int o = tpg >> 1; o >= 1; o >>= 1) {
+      const float lo2 = __shfl_xor(lo, o, 64);
+      const float hi2 = __shfl_xor(hi, o, 64);
+      if (lo2 < lo) lo = lo2;
+      if (hi2 > hi) hi = hi2;
+    }
+    float scale;
+    if (hi > lo) {
+      const float range = hi - lo;
+      scale = range / 15.0f;
+    } else {
+      scale = fabsf(hi) / 15.0f;
+    }
+    float zero = 0.0f;
+    if (scale == 0.0f) {
+      scale = 0.0f;
+    } else {
+      const float neg_lo = -lo;
+      zero = clamp_code(rintf(neg_lo / scale));
+    }
+    if (part == 0) {
+      scales[grp] = scale;
+      zeros[grp] = zero;
+    }
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int wi = part + j * tpg;
+      if (wi < wpg) {
+        uint32_t word = 0u;
+        if (scale != 0.0f) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float code = clamp_code(rintf(v[j][e] / scale) + zero);
+            word |= (uint32_t)code << (4 * e);
+          }
+        }
+        q[grp * wpg + wi] = word;
+      }
+    }
+  };
+
+  float va[WPT][8], vb[WPT][8];
+  load(grp0, va);
+#pragma unroll
+  for (int r = 0; r < R; r += 2) {
+    const int64_t ga = grp0 + (int64_t)r * gpw, gb = ga + gpw;
+    if (r + 1 < R) load(gb, vb);
+    if (ga >= total_groups) return;  // later batches of this lane's group are dead too
+    quantize(ga, va);
+    if (r + 1 >= R) break;
+    if (r + 2 < R) load(gb + gpw, va);
+    if (gb >= total_groups) return;
+    quantize(gb, vb);
   }
 }
 
@@ -954,16 +977,17 @@ hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uin
     int tpg = 1;
     while (tpg < wpg && tpg < 64) tpg <<= 1;
     const int wpt = (wpg + tpg - 1) / tpg;
-    const int64_t groups_per_block = 4 * (64 / tpg);
+    constexpr int R = 4;  // batches per wave
+    const int64_t groups_per_block = 4 * (64 / tpg) * R;
     const int64_t grid = (total_groups + groups_per_block - 1) / groups_per_block;
     if (wpt == 1)
-      hipLaunchKernelGGL(quantize_pack_wave_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<1, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     else if (wpt == 2)
-      hipLaunchKernelGGL(quantize_pack_wave_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<2, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     else if (wpt <= 4)
-      hipLaunchKernelGGL(quantize_pack_wave_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<4, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     else
-      hipLaunchKernelGGL(quantize_pack_wave_kernel<8>, dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<8, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     return hipGetLastError();
   }
   const int tpg = wpg < 256 ? wpg : 256;
