@@ -491,7 +491,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the int4 matvec path here has no multi-GPU "
-              "mode (column sharding is described in DESIGN.md); run with --gpus 1.",
+              "mode (it would shard by output columns, with no reduction); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
