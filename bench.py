@@ -18,6 +18,7 @@ Next-row calls (the fused variants beside the hot path) are timed the same
 way and reported under "next_rows"; they are not part of the step:
   dual     x[4096] . W0, W1 [4096, 4096]                                 (gs 128), and M = 4 lanes
   gated4   silu(X . Wg) * (X . Wu) for M = 4 lanes, the c3 gate/up weights (gs 128)
+  mlp      gated + down in one launch (int4_mlp), the c3 weights            (gs 128)
   sig      (a * sigmoid(gate))[4096] . W[4096, 4096]                      (gs 128)
   swiglu   (silu(gate) * up)[8192] . W[4096, 8192]                        (gs 128)
   normswi  silu(x . Wg) * (x . Wu), x = RMSNorm(a_a + a_b) * w_norm, [14336, 4096] (gs 128)
@@ -270,7 +271,19 @@ def build_next(q4, torch, dev):
     i3g = synth.c3_inputs()
     c3 = synth.CONFIGS["c3"]
     w3g = (*quantize(i3g["Wg"], c3["gs"]), *quantize(i3g["Wu"], c3["gs"]))
+    w3d = quantize(i3g["Wd"], c3["gs"])
+    x3 = torch.from_numpy(i3g["x"]).to(dev)
     del i3g
+    # The whole MLP block (gated pass + down projection) in one launch; the
+    # bytes are those of the two separate calls (h written, then read).
+    h3m = torch.empty(c3["N"], device=dev)
+    y3m = torch.empty(c3["Nd"], device=dev)
+    ws3 = torch.zeros(q4.int4_mlp_workspace_bytes() // 4, dtype=torch.int32, device=dev)
+    b3f = (2 * alg_bytes(c3["N"], c3["K"], c3["gs"], 0, 0) + 4 * c3["K"] + 4 * c3["N"]
+           + alg_bytes(c3["Nd"], c3["Kd"], c3["gs"], c3["Kd"], c3["Nd"]))
+    calls.append(Call(f"MLP fused 2x{c3['N']}x{c3['K']} + {c3['Nd']}x{c3['Kd']}", b3f,
+                      lambda s: q4.int4_mlp(x3, *s, h=h3m, y=y3m, workspace=ws3),
+                      lambda r: clones((*w3g, *w3d), r), wbytes((*w3g, *w3d))))
     X3 = torch.from_numpy(synth.lanes(0x305, 4, c3["K"])).to(dev)
     H3 = torch.empty((4, c3["N"]), device=dev)
     b3m = 2 * alg_bytes(c3["N"], c3["K"], c3["gs"], 0, 0) + 4 * 4 * c3["K"] + 4 * 4 * c3["N"]

@@ -143,6 +143,39 @@ int int4_matvec_gated_lanes(const float* X, int32_t M,
                             int64_t N, int64_t K, int32_t group_size, float* H, void* stream);
 
 /*
+ * The whole decode MLP block in one launch: the gated gate/up matvec, then
+ * the down projection of its output ([P2] generateGepardBackboneGraph: the
+ * layer's gate and up MatMulInt4 nodes, the SwiGLU node and the down
+ * MatMulInt4 node; [P1] fuseSwiGLUDecodeEntries fuses the first three):
+ *   h[f] = silu(x . w_gate[f]) * (x . w_up[f]),   0 <= f < F,
+ *   y[d] = h . w_down[d],                         0 <= d < D.
+ * x [D], h [F] (written), y [D].  w_gate and w_up are F columns of D
+ * inputs, w_down is D columns of F inputs; all three use group_size, which
+ * must divide both D and F.  h is bit-identical to int4_matvec_gated and y
+ * to int4_matvec on that h.  h must be 16-byte aligned (it is the down
+ * projection's input).
+ *
+ * workspace: at least int4_mlp_workspace_bytes() bytes of device memory,
+ * 16-byte aligned, owned by the caller, all ZERO before its first use and
+ * then left as the calls leave it: it holds a call counter and one flag per
+ * block, through which the down projection waits until every part of h is
+ * written.  Calls that share a workspace must not overlap in time.  The
+ * wait assumes the launch's blocks are all resident at once (the grid is
+ * one block per compute unit); a block that waits about a second gives up
+ * and sets word 1 of the workspace to 1, and the outputs are then
+ * undefined.  Shapes the fused launch does not cover (very small F or D, or
+ * K beyond the one-lane register kernel) run as the two separate calls,
+ * with the same results, and leave the workspace untouched.
+ */
+size_t int4_mlp_workspace_bytes(void);
+int int4_mlp(const float* x,
+             const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+             const uint32_t* q_up, const float* s_up, const float* z_up,
+             const uint32_t* q_down, const float* s_down, const float* z_down,
+             int64_t D, int64_t F, int32_t group_size, float* h, float* y,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Residual-add + RMSNorm prefixed matvec ([P4] WGSL_NORM_MATVEC_INT4,
  * NORM_MATVEC_INT4_SPEC with params [K, N, gs, eps]):
  *   r[k]   = a_a[k] + a_b[k]                          (binary32)

@@ -22,7 +22,8 @@ __all__ = [
     "Int4Error", "int4_quantize_pack", "int4_matvec", "int4_matvec_split4",
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
     "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
-    "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "lib", "LIB_PATH",
+    "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "int4_mlp", "int4_mlp_workspace_bytes",
+    "lib", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -59,6 +60,10 @@ lib.int4_matvec_gated_lanes.restype = ctypes.c_int
 lib.int4_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_gemm.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, ctypes.c_size_t, _vp]
+lib.int4_mlp_workspace_bytes.argtypes = []
+lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
+lib.int4_mlp.argtypes = [_vp] * 10 + [_i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.int4_mlp.restype = ctypes.c_int
 for _fn in (lib.int4_gemm, lib.int4_embedding_gather, lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
             lib.int4_matvec_gated, lib.int4_matvec_norm, lib.int4_matvec_dual,
             lib.int4_matvec_sigmoid_gated, lib.int4_matvec_swiglu_gated,
@@ -342,3 +347,38 @@ def int4_matvec_gated_lanes(X: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up,
                                        _ptr(q_up), _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(H),
                                        _stream(stream)))
     return H
+
+
+def int4_mlp_workspace_bytes() -> int:
+    """Bytes of zeroed device workspace int4_mlp needs."""
+    return int(lib.int4_mlp_workspace_bytes())
+
+
+def int4_mlp(x: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, q_down, s_down, z_down,
+             h=None, y=None, workspace=None, stream=None):
+    """(h, y): h = silu(x . w_gate^T) * (x . w_up^T) [F], y = h . w_down^T [D], one launch.
+
+    workspace: an int32 device tensor of at least int4_mlp_workspace_bytes()
+    bytes, zeroed before its first use and then kept as the calls leave it
+    (calls sharing it must not overlap).  A fresh zeroed one is made when
+    not given.
+    """
+    F, D, gs = _pair(q_gate, s_gate, z_gate, q_up, s_up, z_up, "_gate", "_up")
+    D2, F2, gs2 = _weights(q_down, s_down, z_down, "_down")
+    if (D2, F2, gs2) != (D, F, gs):
+        raise ValueError(f"down weights must be [{D}, {F}/8] with group size {gs}")
+    _dev(x, "x", _F32)
+    if x.numel() != D:
+        raise ValueError(f"x must hold D = {D} floats")
+    h = torch.empty(F, dtype=torch.float32, device=x.device) if h is None else h
+    y = torch.empty(D, dtype=torch.float32, device=x.device) if y is None else y
+    _dev(h, "h", _F32)
+    _dev(y, "y", _F32)
+    if workspace is None:
+        workspace = torch.zeros(int4_mlp_workspace_bytes() // 4, dtype=torch.int32, device=x.device)
+    _dev(workspace, "workspace", (torch.int32, torch.uint32, torch.uint8))
+    _check(lib.int4_mlp(_ptr(x), _ptr(q_gate), _ptr(s_gate), _ptr(z_gate), _ptr(q_up), _ptr(s_up),
+                        _ptr(z_up), _ptr(q_down), _ptr(s_down), _ptr(z_down), D, F, gs, _ptr(h),
+                        _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(stream)))
+    return h, y

@@ -293,6 +293,40 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
   return INT4_OK;
 }
 
+// Resident blocks per CU of the fused MLP kernel for one shape, cached like
+// cached_occupancy.
+int mlp_occupancy(const GemvArgs& gu, int ncol1, const GemvArgs& dn, int ncol2, const LaunchShape& s,
+                  int* bpc) {
+  struct Key {
+    int dev, ncol1, ncol2, threads;
+    size_t lds;
+    bool operator<(const Key& o) const {
+      return std::tie(dev, ncol1, ncol2, threads, lds) < std::tie(o.dev, o.ncol1, o.ncol2, o.threads, o.lds);
+    }
+  };
+  static std::mutex mu;
+  static std::map<Key, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const Key key{dev, ncol1, ncol2, s.block_threads, s.lds_bytes};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *bpc = it->second;
+      return INT4_OK;
+    }
+  }
+  int v = 0;
+  e = launch_mlp(gu, ncol1, dn, ncol2, s, nullptr, nullptr, &v);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = v;
+  *bpc = v;
+  return INT4_OK;
+}
+
 uint64_t group_magic(int32_t gs) {
   const uint64_t d = (uint64_t)(gs / 32);
   return (((uint64_t)1 << 40) + d - 1) / d;
@@ -462,6 +496,90 @@ int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gat
   a.z[1] = z_up;
   a.out[0] = h;
   return run(kGated, a, stream);
+}
+
+size_t int4_mlp_workspace_bytes(void) { return kMlpWorkspaceBytes; }
+
+int int4_mlp(const float* x, const uint32_t* q_gate, const float* s_gate, const float* z_gate,
+             const uint32_t* q_up, const float* s_up, const float* z_up, const uint32_t* q_down,
+             const float* s_down, const float* z_down, int64_t D, int64_t F, int32_t group_size, float* h,
+             float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  RETURN_IF(check_kgs(D, group_size));
+  RETURN_IF(check_kgs(F, group_size));
+  if (!x || !q_gate || !s_gate || !z_gate || !q_up || !s_up || !z_up || !q_down || !s_down || !z_down || !h || !y)
+    return fail(INT4_ERR_NULL, "x, the three weight triplets, h and y are required");
+  if (!workspace) return fail(INT4_ERR_NULL, "workspace is required (int4_mlp_workspace_bytes, zeroed)");
+  if (workspace_bytes < int4_mlp_workspace_bytes())
+    return fail(INT4_ERR_SHAPE, "workspace holds %zu bytes; the call needs %zu", workspace_bytes,
+                int4_mlp_workspace_bytes());
+  RETURN_IF(check_align(x, 16, "x"));
+  RETURN_IF(check_align(q_gate, 16, "q_gate"));
+  RETURN_IF(check_align(q_up, 16, "q_up"));
+  RETURN_IF(check_align(q_down, 16, "q_down"));
+  RETURN_IF(check_align(s_gate, 4, "s_gate"));
+  RETURN_IF(check_align(z_gate, 4, "z_gate"));
+  RETURN_IF(check_align(s_up, 4, "s_up"));
+  RETURN_IF(check_align(z_up, 4, "z_up"));
+  RETURN_IF(check_align(s_down, 4, "s_down"));
+  RETURN_IF(check_align(z_down, 4, "z_down"));
+  RETURN_IF(check_align(h, 16, "h"));
+  RETURN_IF(check_align(y, 4, "y"));
+  RETURN_IF(check_align(workspace, 16, "workspace"));
+  const uint64_t Gf = (uint64_t)F * (uint64_t)(D / group_size);  // gate/up groups
+  const uint64_t Gd = (uint64_t)D * (uint64_t)(F / group_size);  // down groups
+  const uint64_t qb = (uint64_t)F * (uint64_t)D / 2;               // bytes of codes per matrix
+  const Span ins[] = {{x, (uint64_t)D * 4, "x"},
+                      {q_gate, qb, "q_gate"}, {s_gate, Gf * 4, "s_gate"}, {z_gate, Gf * 4, "z_gate"},
+                      {q_up, qb, "q_up"}, {s_up, Gf * 4, "s_up"}, {z_up, Gf * 4, "z_up"},
+                      {q_down, qb, "q_down"}, {s_down, Gd * 4, "s_down"}, {z_down, Gd * 4, "z_down"}};
+  const Span outs[] = {{h, (uint64_t)F * 4, "h"}, {y, (uint64_t)D * 4, "y"},
+                       {workspace, int4_mlp_workspace_bytes(), "workspace"}};
+  RETURN_IF(check_alias(ins, 10, outs, 3));
+
+  GemvArgs gu{};
+  fill_common(gu, F, D, group_size);
+  gu.x = x;
+  gu.M = 1;
+  gu.q[0] = reinterpret_cast<const uint4*>(q_gate);
+  gu.s[0] = s_gate;
+  gu.z[0] = z_gate;
+  gu.q[1] = reinterpret_cast<const uint4*>(q_up);
+  gu.s[1] = s_up;
+  gu.z[1] = z_up;
+  gu.out[0] = h;
+  GemvArgs dn{};
+  fill_common(dn, D, F, group_size);
+  dn.x = h;
+  dn.M = 1;
+  dn.q[0] = reinterpret_cast<const uint4*>(q_down);
+  dn.s[0] = s_down;
+  dn.z[0] = z_down;
+  dn.out[0] = y;
+  LaunchShape s1{}, s2{};
+  RETURN_IF(plan(kGated, gu, &s1));
+  RETURN_IF(plan(kPlain, dn, &s2));
+  hipStream_t st = (hipStream_t)stream;
+  // One launch when both passes run the register kernel on the same grid
+  // and that grid is resident at once; the passes then keep the shapes of
+  // the standalone calls, so their results are the same bits.
+  if (s1.variant == kVariantReg && s2.variant == kVariantReg && s1.grid == s2.grid && s1.grid <= kMlpMaxBlocks) {
+    LaunchShape s = s1;
+    s.block_threads = s1.block_threads > s2.block_threads ? s1.block_threads : s2.block_threads;
+    s.lds_bytes = s1.lds_bytes > s2.lds_bytes ? s1.lds_bytes : s2.lds_bytes;
+    DeviceInfo dev;
+    RETURN_IF(device_info(&dev));
+    int bpc = 0;
+    RETURN_IF(mlp_occupancy(gu, s1.ncol, dn, s2.ncol, s, &bpc));
+    if ((int64_t)bpc * dev.cus >= s.grid) {
+      hipError_t e = launch_mlp(gu, s1.ncol, dn, s2.ncol, s, static_cast<uint32_t*>(workspace), st, nullptr);
+      if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+      return ok();
+    }
+  }
+  hipError_t e = launch_gemv(kGated, gu, s1, st);
+  if (e == hipSuccess) e = launch_gemv(kPlain, dn, s2, st);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int int4_matvec_gated_lanes(const float* X, int32_t M, const uint32_t* q_gate, const float* s_gate,

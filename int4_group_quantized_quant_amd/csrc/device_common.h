@@ -67,6 +67,7 @@ __device__ __forceinline__ float add_swap16(float a, float b) {
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
 constexpr int kLoadNonTemporal = 2;       // cache policy: streamed, no reuse expected
+constexpr int kLoadDeviceCoherent = 16;   // cache policy: device scope, coherent across the L2 caches
 
 // ------------------------------------------------------------ elementwise gates
 

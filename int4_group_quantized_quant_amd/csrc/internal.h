@@ -121,6 +121,19 @@ hipError_t launch_gemv(Mode mode, const GemvArgs& a, const LaunchShape& shape, h
 // Resident blocks per CU of the kernel `launch_gemv` would run for this shape.
 hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& shape, int* blocks_per_cu);
 
+// The fused MLP (gated pass, grid-wide wait, down pass) in one launch of
+// the register kernel's passes: `gate_up` and `down` are planned as the
+// standalone kGated and kPlain register-kernel calls with the same grid;
+// `shape` holds that grid and the larger block and LDS of the two.
+// `ws` is the caller's workspace (kMlpWorkspaceBytes, zeroed before its
+// first use): a call counter, a timeout flag and one flag per block, for
+// grids of at most kMlpMaxBlocks.  With `occupancy` set only queries the
+// resident blocks per CU.
+constexpr size_t kMlpWorkspaceBytes = 8192;
+constexpr int kMlpMaxBlocks = (int)(kMlpWorkspaceBytes / 4) - 32;
+hipError_t launch_mlp(const GemvArgs& gate_up, int ncol_gate_up, const GemvArgs& down, int ncol_down,
+                      const LaunchShape& shape, uint32_t* ws, hipStream_t stream, int* occupancy);
+
 // The matrix-core lanes kernel (slice.hip) for modes kPlain, kDual, kGated,
 // kSigIn and kSwiIn; launches, or with `occupancy` set only queries.
 hipError_t dispatch_slice(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStream_t stream,

@@ -312,7 +312,7 @@ __device__ __forceinline__ float4 gated_in4(const GemvArgs& a, int i) {
 // of column `col` (stream st: 0 = the weights / gate / first projection,
 // 1 = up / second projection).  `inv` is inv_rms for the norm modes and
 // unused otherwise.
-template <int M, int MODE>
+template <int M, int MODE, bool kPublish = false>
 __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
                                              const float (&tot)[mode_streams(MODE)][M],
                                              float inv) {
@@ -337,6 +337,10 @@ __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
     const float g = tot[0][0] * inv;
     const float u = tot[1][0] * inv;
     a.out[0][col] = silu_f32(g) * u;
+  } else if constexpr (kPublish) {
+    // Stored at device scope: read back by other blocks of the same launch.
+    __hip_atomic_store(a.out[0] + col, silu_f32(tot[0][0]) * tot[1][0], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   } else {
     a.out[0][col] = silu_f32(tot[0][0]) * tot[1][0];
   }
@@ -345,15 +349,27 @@ __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
 // ------------------------------------------------------------ register kernel
 
 
-template <int M, int NCOL, int MODE, int DEPTH>
-__global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
+// The activations of a pass are ready when it starts (a kernel's own inputs).
+struct InputsReady {
+  __device__ void operator()() const {}
+};
+
+// One pass of the register kernel over its columns.  `part` is the block's
+// LDS: [cols of the block][NSTREAM][M][nch] partials, one float per wave,
+// then the staged activations (x_lds_offset).  The block may hold more waves
+// than the pass's P rows of nch waves; the extra waves own no columns.
+// `inputs_ready` is called by every thread before the activations are read:
+// with InputsReady the staging goes first; otherwise the first step of
+// weight loads is issued before the call, so that they stream while it
+// waits, and the activations (written by other blocks of the launch) are
+// read at device scope.  kPublish stores the outputs at device scope.
+template <int M, int NCOL, int MODE, bool kPublish, class Ready>
+__device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready inputs_ready) {
   constexpr int NSTREAM = mode_streams(MODE);
   constexpr int NSLOT = NCOL * NSTREAM;
   constexpr int V = M * NSLOT;
   constexpr int NZ = (V + 3) / 4;
-  // [cols of the block][NSTREAM][M][nch], one float per wave, then the
-  // staged activations (x_lds_offset)
-  extern __shared__ float part[];
+  constexpr bool kWaits = !__is_same(Ready, InputsReady);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_int(threadIdx.x >> 6);
@@ -364,9 +380,9 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   const int64_t R = (int64_t)gridDim.x * P;
   const int64_t blk_begin = uniform_i64((int64_t)blockIdx.x * P * a.N / R);
   const int64_t blk_end = uniform_i64(((int64_t)blockIdx.x * P + P) * a.N / R);
-  const int64_t row = (int64_t)blockIdx.x * P + p;
+  const int64_t row = (int64_t)blockIdx.x * P + (p < P ? p : 0);
   const int64_t c_begin = uniform_i64(row * a.N / R);
-  const int64_t c_end = uniform_i64((row + 1) * a.N / R);
+  const int64_t c_end = p < P ? uniform_i64((row + 1) * a.N / R) : c_begin;
   const int u = c * a.cw + lane;
   const bool active = lane < a.cw && u < a.U;
   const uint32_t qoff = (uint32_t)(active ? u : 0) * 16u;
@@ -379,6 +395,25 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   // inputs in registers for the sweep.
   float4* xl = reinterpret_cast<float4*>(part + x_lds_offset(a.part_floats));
   const int n4 = a.K >> 2;
+  // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
+  // before step i is computed.  With inputs at hand, the first weight loads
+  // go out after the activation loads (the memory counter is in order, so
+  // the staging would otherwise wait for them) and overlap the barrier;
+  // with inputs still being produced, they go out first and overlap the
+  // wait.  Every load is unconditional: steps past the wave's last column
+  // re-read that column, and a wave without columns has an empty buffer
+  // range, whose loads return 0 without touching memory.
+  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
+  const uint32_t last = c_end > c_begin ? (uint32_t)(c_end - c_begin - 1) : 0u;
+  // One step of loads in flight ahead of the arithmetic: two or three
+  // measured slower on every call shape (more requests outstanding per CU
+  // only add contention for the memory pipeline).
+  constexpr int DEPTH = 1;
+  Step<NSLOT> s0, s1;
+  if constexpr (kWaits) {
+    load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+    inputs_ready();
+  }
   if constexpr (mode_has_norm(MODE)) {
     // Per-thread share of sum_k r_k^2, then the wave's total in its slot.
     float ssq = 0.0f;
@@ -396,6 +431,12 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
     if (lane == 0) scratch[wave] = wsum;
   } else if constexpr (mode_gates_input(MODE)) {
     for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(i & 7) * a.U + (i >> 3)] = gated_in4<MODE>(a, i);
+  } else if constexpr (kWaits) {
+    static_assert(M == 1, "a waiting pass reads one activation row");
+    const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, n4 * 16, kBufferWord3);
+    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+      xl[((i & 7)) * a.U + (i >> 3)] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)i * 16u, 0, kLoadDeviceCoherent));
   } else {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -403,21 +444,7 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
       for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(m * 8 + (i & 7)) * a.U + (i >> 3)] = src[i];
     }
   }
-  // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
-  // before step i is computed.  The first weight loads go out once the
-  // activation loads have returned (the memory counter is in order, so the
-  // staging would otherwise wait for them) and overlap the barrier.
-  // Every load is unconditional: steps past the wave's last column re-read
-  // that column, and a wave without columns has an empty buffer range, whose
-  // loads return 0 without touching memory.
-  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
-  const uint32_t last = c_end > c_begin ? (uint32_t)(c_end - c_begin - 1) : 0u;
-  // One step of loads in flight ahead of the arithmetic: two or three
-  // measured slower on every call shape (more requests outstanding per CU
-  // only add contention for the memory pipeline).
-  static_assert(DEPTH == 1, "the ring below holds two steps");
-  Step<NSLOT> s0, s1;
-  load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+  if constexpr (!kWaits) load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
   __syncthreads();
   float x[M][32];
 #pragma unroll
@@ -504,8 +531,88 @@ __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
         for (int cc = 1; cc < nch; ++cc) s += pp[cc];
         tot[st][m] = s;
       }
-    store_column<M, MODE>(a, blk_begin + j, tot, inv);
+    store_column<M, MODE, kPublish>(a, blk_begin + j, tot, inv);
   }
+}
+
+template <int M, int NCOL, int MODE, int DEPTH>
+__global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
+  static_assert(DEPTH == 1, "the register pass keeps one step of loads in flight");
+  extern __shared__ float part[];
+  reg_pass<M, NCOL, MODE, false>(a, part, InputsReady{});
+}
+
+// ------------------------------------------------------------ fused MLP
+
+// Polls before a block stops waiting for the others (about a second): a
+// grid whose blocks are not all resident at once must not hang the device.
+constexpr uint32_t kGridWaitPolls = 1u << 20;
+
+// The fused MLP's workspace, 32-bit words: [0] the call count (epoch),
+// [1] the timeout flag, [kMlpFlags + b] the epoch block b last published.
+constexpr int kMlpFlags = 32;
+static_assert(kMlpWorkspaceBytes / 4 - kMlpFlags == kMlpMaxBlocks, "one flag per block");
+
+// Waits until every block of the grid has published this call's epoch in
+// its flag.  The flags and the activations behind them were stored at
+// device scope, and the activations stores completed before each flag was
+// written; the waiting pass reads them at device scope, so no cache
+// maintenance is needed.  Wave 0 polls all flags at once; on a timeout it
+// records the failure in word 1 and goes on.
+struct GridWait {
+  uint32_t* ws;
+  uint32_t epoch;
+  __device__ void operator()() const {
+    if (threadIdx.x < 64) {
+      const uint32_t* flags = ws + kMlpFlags;
+      const int nb = (int)gridDim.x;
+      for (uint32_t polls = 0;; ++polls) {
+        bool done = true;
+        for (int b0 = 4 * (int)threadIdx.x; b0 < nb; b0 += 256) {
+          // Four loads in flight at once (indices past the grid re-read the
+          // last flag).
+          uint32_t f[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            f[j] = __hip_atomic_load(flags + (b0 + j < nb ? b0 + j : nb - 1), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) done &= f[j] == epoch;
+        }
+        if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+        if (polls == kGridWaitPolls) {
+          if (threadIdx.x == 0) __hip_atomic_store(ws + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// h = silu(x Wg^T) * (x Wu^T), then y = h Wd^T, in one persistent grid:
+// every block runs its columns of the gated pass, stores them at device
+// scope, waits for those stores to complete and publishes the call's epoch
+// in its flag; its first step of down-projection weights is loaded while it
+// waits for every flag, and the down pass then stages the whole of h.
+// Block 0 advances the stored epoch once it has seen every flag (by then
+// every block has read it).  No read-modify-write: all blocks' atomics on
+// one word would be serialized at the memory.
+template <int NCOL1, int NCOL2>
+__global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs down, uint32_t* ws) {
+  extern __shared__ float part[];
+  // Wave 0 publishes and polls; it alone needs the epoch.
+  uint32_t epoch = 0;
+  if (threadIdx.x < 64) epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  reg_pass<1, NCOL1, kGated, true>(gate_up, part, InputsReady{});
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores of h have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(ws + kMlpFlags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  reg_pass<1, NCOL2, kPlain, false>(down, part, GridWait{ws, epoch});
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(ws, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ LDS kernel
@@ -877,6 +984,19 @@ hipError_t launch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t strea
   return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, 1>, raised1, a, s, stream, occupancy);
 }
 
+template <int NCOL1, int NCOL2>
+hipError_t launch_mlp_t(const GemvArgs& gate_up, const GemvArgs& down, const LaunchShape& s, uint32_t* ws,
+                        hipStream_t stream, int* occupancy) {
+  static std::atomic<bool> raised{false};
+  const auto kern = mlp_reg_kernel<NCOL1, NCOL2>;
+  hipError_t e = raise_lds_once(kern, raised, s);
+  if (e != hipSuccess) return e;
+  if (occupancy)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, kern, s.block_threads, s.lds_bytes);
+  hipLaunchKernelGGL(kern, dim3(s.grid), dim3(s.block_threads), s.lds_bytes, stream, gate_up, down, ws);
+  return hipGetLastError();
+}
+
 template <int MODE, int M, int NCOL>
 hipError_t launch_lds(const GemvArgs& a, const LaunchShape& s, hipStream_t stream, int* occupancy) {
   static std::atomic<bool> raised{false};
@@ -946,6 +1066,20 @@ int max_ncol(Mode mode, int M, int variant) {
     return M == 1 ? 4 : 2;
   }
   return mode == kPlain ? 2 : 1;
+}
+
+hipError_t launch_mlp(const GemvArgs& gate_up, int ncol_gate_up, const GemvArgs& down, int ncol_down,
+                      const LaunchShape& s, uint32_t* ws, hipStream_t stream, int* occupancy) {
+  if (s.depth != 1) return hipErrorInvalidValue;
+  const bool g2 = ncol_gate_up != 1;
+  switch (ncol_down) {
+    case 1: return g2 ? launch_mlp_t<2, 1>(gate_up, down, s, ws, stream, occupancy)
+                      : launch_mlp_t<1, 1>(gate_up, down, s, ws, stream, occupancy);
+    case 2: return g2 ? launch_mlp_t<2, 2>(gate_up, down, s, ws, stream, occupancy)
+                      : launch_mlp_t<1, 2>(gate_up, down, s, ws, stream, occupancy);
+    default: return g2 ? launch_mlp_t<2, 4>(gate_up, down, s, ws, stream, occupancy)
+                       : launch_mlp_t<1, 4>(gate_up, down, s, ws, stream, occupancy);
+  }
 }
 
 hipError_t gemv_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* blocks_per_cu) {

@@ -236,3 +236,38 @@ def test_gemm_workspace_and_validation(lib):
     assert lib.int4_gemm(A, T, B, C, D, N, K, gs, W + 64, W, sz(need), None) == ALIAS  # Y inside workspace
     assert lib.int4_gemm(A, T, B, C, D, 1 << 20, 1 << 12, 128, E, W, sz(1 << 40), None) == SHAPE  # N*K/2 >= 2^31
     assert "2^31" in _err(lib)
+
+
+def test_mlp_workspace_and_validation(lib):
+    lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
+    need = lib.int4_mlp_workspace_bytes()
+    assert need >= 12
+    sz = ctypes.c_size_t
+    Dm, Fm, gs = 256, 512, 128
+    base = 0x100000000
+    x, qg, sg, zg, qu, su, zu, qd, sd, zd, h, y, ws = (base + i * 0x10000000 for i in range(13))
+
+    def call(**kw):
+        a = dict(x=x, qg=qg, sg=sg, zg=zg, qu=qu, su=su, zu=zu, qd=qd, sd=sd, zd=zd, D=Dm, F=Fm, gs=gs,
+                 h=h, y=y, ws=ws, wsb=need)
+        a.update(kw)
+        return lib.int4_mlp(a["x"], a["qg"], a["sg"], a["zg"], a["qu"], a["su"], a["zu"], a["qd"], a["sd"],
+                            a["zd"], a["D"], a["F"], a["gs"], a["h"], a["y"], a["ws"], sz(a["wsb"]), None)
+
+    assert call(gs=48) == SHAPE
+    assert call(F=Fm + 32) == SHAPE          # F not a multiple of the group size
+    assert call(D=64) == SHAPE               # D below the group size
+    assert call(x=None) == NULL
+    assert call(zd=None) == NULL
+    assert call(h=None) == NULL
+    assert call(ws=None) == NULL
+    assert "workspace" in _err(lib)
+    assert call(wsb=need - 1) == SHAPE
+    assert call(h=h + 4) == ALIGN            # h is the down projection's input: 16-byte aligned
+    assert call(x=x + 8) == ALIGN
+    assert call(qd=qd + 4) == ALIGN
+    assert call(ws=ws + 2) == ALIGN
+    assert call(y=x) == ALIAS                # y over x
+    assert call(h=qd) == ALIAS               # h over the down codes
+    assert call(ws=h + 16) == ALIAS          # workspace inside h
+    assert call(y=h + 64) == ALIAS           # y inside h
