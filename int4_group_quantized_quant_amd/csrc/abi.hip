@@ -234,13 +234,22 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     // block's columns in rounds of RT tiles whose partials fit the LDS.
     const int U = a.U;
     int su = 16;
+    int mix24 = 0;
     if (U > kSliceMaxWaves * 16) {
       const int P = (U + kSliceMaxWaves * 24 - 1) / (kSliceMaxWaves * 24);
       const int per_wave = ((U + P - 1) / P + kSliceMaxWaves - 1) / kSliceMaxWaves;
       su = per_wave <= 16 ? 16 : (per_wave <= 20 ? 20 : 24);
+      if (P == 1 && su == 20) {
+        // One pass of 20-unit slices would split a cache line of every
+        // column between two waves; slices of 24 and 16 units (3 and 2
+        // lines) cover U instead, every wave holding one:
+        // 24 n + 16 (8 - n) >= U, and the last wave starts at 112 + 8 n < U.
+        mix24 = (U - kSliceMaxWaves * 16 + 7) / 8;
+        su = 24;
+      }
     }
     const int cls = slice_class(U / a.G);
-    const int nsl = (U + su - 1) / su;
+    const int nsl = mix24 > 0 ? kSliceMaxWaves : (U + su - 1) / su;
     const int W = nsl < kSliceMaxWaves ? nsl : kSliceMaxWaves;
     const int bpc = kSliceMaxWaves / W;
     const int64_t tiles = (N + 15) / 16;
@@ -261,6 +270,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     if (rt > tiles_per_block) rt = tiles_per_block;
     a.rt = (int32_t)rt;
     a.su = su;
+    a.mix24 = mix24;
     s->variant = kVariantSlice;
     s->ncol = 16;
     s->depth = 1;

@@ -55,7 +55,9 @@ struct GemvArgs {
   int32_t part_floats;  // floats of the per-block partial table (register kernel)
   int32_t M;            // lanes (kPlain)
   int32_t rt;           // tiles of 16 columns per round (matrix-core kernel)
-  int32_t su;           // units per K slice (matrix-core kernel)
+  int32_t su;           // units per K slice (matrix-core kernel; 24 when mixed)
+  int32_t mix24;        // matrix-core kernel: > 0 runs one slice per wave, this many
+                        // waves of 24 units and the rest of 16 (whole cache lines)
   uint32_t g_recip;     // ceil(2^32 / G), 0 when G = 1 (matrix-core kernel's table copy)
 };
 

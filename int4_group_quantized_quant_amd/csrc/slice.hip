@@ -55,12 +55,17 @@ struct SliceTile {
 // lane's input is the elementwise gate of rows x and x2); kGated (each block
 // runs both streams over its columns: a round's tiles of stream 0, then of
 // stream 1, and the round's outputs are silu(g) * u).
-template <int SU, int GS, int DEPTH, int MODE>
-__global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
-  extern __shared__ float4 lds4[];
+// One wave's share of the kernel: slices of SU units starting at units
+// u_first, u_first + u_step, ... below U, over every round of the block's
+// tiles.  SUS is the largest slice size of the launch: it sets the per-wave
+// LDS stage and the table stride, which all waves of a block share.  Every
+// wave runs the same rounds and reaches the same barriers in each, whatever
+// its SU.
+template <int SU, int SUS, int GS, int DEPTH, int MODE>
+__device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int u_first, int u_step) {
   constexpr int NJ = SU / 4;  // load instructions per tile
   constexpr int CS = slice_code_stride(SU);
-  constexpr int kStage = slice_stage_words(SU);
+  constexpr int kStage = slice_stage_words(SUS);
   constexpr int H = SU / 2;  // units each half of a row's lanes converts
   constexpr int NB = 5;      // table chunks per thread loaded ahead of the activations
   static_assert(DEPTH == 2 || DEPTH == 3, "the ring below holds two or three tiles");
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   const int K = a.K;
   const int U = a.U;
   const int G = a.G;
-  const int GP = slice_table_stride(G, SU, GS);
+  const int GP = slice_table_stride(G, SUS, GS);
   const int gsu = U / G;
   const int64_t N = a.N;
   const int lane = threadIdx.x & 63;
@@ -77,7 +82,6 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   const int lo16 = lane & 15;  // matrix layout: column
   const int wave = uniform_int(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
-  const int nsl = (U + SU - 1) / SU;
   const int nbk = MODE == kDual ? (int)gridDim.x / 2 : (int)gridDim.x;
   const int stream = MODE == kDual && (int)blockIdx.x >= nbk ? 1 : 0;
   const int64_t bk = (int64_t)blockIdx.x - (int64_t)stream * nbk;
@@ -168,8 +172,7 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
         }
 
     bool first_pass = true;
-    for (int sl = wave; sl < nsl; sl += W) {
-      const int u0 = SU * sl;
+    for (int u0 = u_first; u0 < U; u0 += u_step) {
       const int h0 = u0 / gsu;
 
       // Activations of the slice for lane (g, i): row m = i & 7, units
@@ -436,6 +439,39 @@ __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArg
   }
 }
 
+template <int SU, int GS, int DEPTH, int MODE>
+__global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
+  extern __shared__ float4 lds4[];
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  slice_wave<SU, SU, GS, DEPTH, MODE>(a, lds4, SU * wave, SU * W);
+}
+
+// One slice per wave of two sizes, whole cache lines each: waves
+// [0, a.mix24) take 24 units (384 bytes of a column), the others 16 units
+// (256 bytes), so no two waves split a line of a column.  Waves w and
+// w + 4 share a SIMD, so with four of each every SIMD holds 40 units.
+template <int GS, int MODE>
+__global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_mixed_kernel(GemvArgs a) {
+  extern __shared__ float4 lds4[];
+  const int wave = uniform_int(threadIdx.x >> 6);
+  const int na = a.mix24;
+  constexpr int kOnce = 1 << 30;  // one slice per wave
+  if (wave < na) slice_wave<24, 24, GS, 2, MODE>(a, lds4, 24 * wave, kOnce);
+  else slice_wave<16, 24, GS, 3, MODE>(a, lds4, 24 * na + 16 * (wave - na), kOnce);
+}
+
+template <int MODE>
+hipError_t dispatch_slice_mixed(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised0{false};
+  switch (slice_class(a.U / a.G)) {
+    case 1: return launch_or_query(gemv_slice_mixed_kernel<1, MODE>, raised1, a, s, st, occ);
+    case 2: return launch_or_query(gemv_slice_mixed_kernel<2, MODE>, raised2, a, s, st, occ);
+    case 4: return launch_or_query(gemv_slice_mixed_kernel<4, MODE>, raised4, a, s, st, occ);
+    default: return launch_or_query(gemv_slice_mixed_kernel<0, MODE>, raised0, a, s, st, occ);
+  }
+}
+
 template <int SU, int DEPTH, int MODE>
 hipError_t dispatch_slice_su(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
   static std::atomic<bool> raised1{false}, raised2{false}, raised4{false}, raised0{false};
@@ -449,6 +485,7 @@ hipError_t dispatch_slice_su(const GemvArgs& a, const LaunchShape& s, hipStream_
 
 template <int MODE>
 hipError_t dispatch_slice_mode(const GemvArgs& a, const LaunchShape& s, hipStream_t st, int* occ) {
+  if (a.mix24 > 0) return dispatch_slice_mixed<MODE>(a, s, st, occ);
   if (a.su == 24) return dispatch_slice_su<24, 2, MODE>(a, s, st, occ);
   if (a.su == 20) return dispatch_slice_su<20, 3, MODE>(a, s, st, occ);
   return dispatch_slice_su<16, 3, MODE>(a, s, st, occ);
