@@ -330,6 +330,75 @@ def build_next(q4, torch, dev):
     return calls
 
 
+def build_shards(q4, torch, dev):
+    """One GPU's share of every call of the step under an 8-way split
+    (synth.SHARD8): the same kernels at the shapes one of eight GPUs would
+    run.  The down projection's partial y would be summed across GPUs (one
+    16 KB all-reduce, not built here: one GPU only)."""
+    sh = synth.SHARD8
+    c2, c3, c4, c5 = (synth.CONFIGS[k] for k in ("c2", "c3", "c4", "c5"))
+    w = synth.shard8_inputs()
+    calls = []
+
+    def quantize(W, gs):
+        return q4.int4_quantize_pack(torch.from_numpy(W).to(dev), gs)
+
+    def clones(tensors, r):
+        sets = [tuple(tensors)]
+        for _ in range(r - 1):
+            sets.append(tuple(t.clone() for t in tensors))
+        return sets
+
+    def wbytes(ws):
+        return sum(t.numel() * 4 for t in ws)
+
+    s2 = sh["split4"]
+    w2 = quantize(w["W2"], s2["gs"])
+    x2 = torch.from_numpy(synth.normal_f32(0x201, c2["K"])).to(dev)
+    o2 = tuple(torch.empty(n, device=dev) for n in (s2["n0"], s2["n1"] - s2["n0"], s2["n2"] - s2["n1"],
+                                                     s2["N"] - s2["n2"]))
+    calls.append(Call(f"split4 {s2['N']}x{s2['K']}", alg_bytes(s2["N"], s2["K"], s2["gs"], s2["K"], s2["N"]),
+                      lambda s: q4.int4_matvec_split4(x2, *s, s2["n0"], s2["n1"], s2["n2"], outs=o2),
+                      lambda r: clones(w2, r), wbytes(w2)))
+    sg, sd = sh["gated"], sh["down"]
+    wgu = (*quantize(w["Wg"], sg["gs"]), *quantize(w["Wu"], sg["gs"]))
+    x3 = torch.from_numpy(synth.normal_f32(0x301, c3["K"])).to(dev)
+    h3 = torch.empty(sg["N"], device=dev)
+    calls.append(Call(f"gated 2x{sg['N']}x{sg['K']}",
+                      2 * alg_bytes(sg["N"], sg["K"], sg["gs"], 0, 0) + 4 * sg["K"] + 4 * sg["N"],
+                      lambda s: q4.int4_matvec_gated(x3, *s, h=h3), lambda r: clones(wgu, r), wbytes(wgu)))
+    wd = quantize(w["Wd"], sd["gs"])
+    y3 = torch.empty(sd["N"], device=dev)
+    calls.append(Call(f"down (K share) {sd['N']}x{sd['K']}",
+                      alg_bytes(sd["N"], sd["K"], sd["gs"], sd["K"], sd["N"]),
+                      lambda s: q4.int4_matvec(h3, *s, Y=y3), lambda r: clones(wd, r), wbytes(wd)))
+    s4 = sh["lmhead"]
+    w4 = quantize(w["W4"], s4["gs"])
+    i4 = {k: torch.from_numpy(v).to(dev) for k, v in (
+        ("a_a", synth.normal_f32(0x401, c4["K"])), ("a_b", synth.normal_f32(0x402, c4["K"])),
+        ("w_norm", synth.uniform_f32(0x403, c4["K"], 0.5, 1.5)))}
+    y4 = torch.empty(s4["N"], device=dev)
+    r4 = torch.empty(s4["K"], device=dev)
+    n4 = torch.empty(s4["K"], device=dev)
+    calls.append(Call(f"norm LM head {s4['N']}x{s4['K']}",
+                      alg_bytes(s4["N"], s4["K"], s4["gs"], 3 * s4["K"], s4["N"] + 2 * s4["K"]),
+                      lambda s: q4.int4_matvec_norm(i4["a_a"], i4["a_b"], i4["w_norm"], s4["eps"], *s, y=y4,
+                                                    residual_out=r4, norm_out=n4),
+                      lambda r: clones(w4, r), wbytes(w4)))
+    s5 = sh["lanes"]
+    w5 = quantize(w["W5"], s5["gs"])
+    X5 = torch.from_numpy(synth.lanes(0x501, 8, c5["K"])).to(dev)
+    for M in s5["Ms"]:
+        wM = tuple(t.clone() for t in w5)
+        XM = X5[:M].contiguous()
+        YM = torch.empty((M, s5["N"]), device=dev)
+        calls.append(Call(f"lanes M={M} {s5['N']}x{s5['K']}",
+                          alg_bytes(s5["N"], s5["K"], s5["gs"], M * s5["K"], M * s5["N"]),
+                          lambda s, XM=XM, YM=YM: q4.int4_matvec(XM, *s, Y=YM),
+                          lambda r, wM=wM: clones(wM, r), wbytes(wM)))
+    return calls
+
+
 # ---------------------------------------------------------------- timing
 
 def capture(torch, fn):
@@ -504,8 +573,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the int4 matvec path here has no multi-GPU "
-              "mode (it would shard by output columns, with no reduction); run with --gpus 1.",
-              file=sys.stderr)
+              "mode (it would shard by output columns, and the MLP down projection by K with "
+              "one small all-reduce per layer; the JSON reports one GPU's share of an 8-way "
+              "split); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -553,6 +623,40 @@ def main():
         log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
             f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)  [next row, not in the step]")
         del c
+    torch.cuda.empty_cache()
+
+    # One GPU's share of the step under an 8-way split: each call alone, then
+    # the shard calls captured together as one step (not the metric).
+    log("one GPU's share of each call under an 8-way split")
+    shard_calls = build_shards(q4, torch, dev)
+    shard_rows = {}
+    for c in shard_calls:
+        us, r = time_call(torch, c)
+        shard_rows[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
+                              "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
+                              "alg_bytes": c.nbytes, "rotating_copies": r}
+        log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
+            f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)  [1/8 share]")
+    shard_sets = [c.sets_fn(1)[0] for c in shard_calls]
+    shard_graph = capture(torch, lambda: [c.fn(s) for c, s in zip(shard_calls, shard_sets)])
+    for _ in range(3):
+        shard_graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(50):
+        shard_graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    shard_us = e0.elapsed_time(e1) * 1e3 / 50
+    shard_bytes = sum(c.nbytes for c in shard_calls)
+    log(f"1/8 share of the step: {shard_us:.1f} us, {shard_bytes / 1e6:.1f} MB")
+    shard = {"shards": 8, "split": "columns for split4 (each range in eighths), gate/up, the LM head "
+                                   "and the lanes; K for down (its partial y needs one 16 KB "
+                                   "all-reduce across GPUs, not built: one GPU only)",
+             "step_us": round(shard_us, 2), "step_alg_bytes": shard_bytes,
+             "step_GBps": round(shard_bytes / shard_us / 1e3, 1), "per_call": shard_rows}
+    del shard_graph, shard_sets, shard_calls
     torch.cuda.empty_cache()
 
     # The step graph.
@@ -605,6 +709,7 @@ def main():
         "cpu_baseline": cpu,
         "per_call": per_call,
         "next_rows": next_rows,
+        "one_gpu_share_of_8": shard,
         "streaming_read_context": streaming_read_context(torch, dev),
         "quantize_pack": {"elements": quant["elements"], "seconds": round(quant["seconds"], 5),
                           "GBps_fp32_in": round(4 * quant["elements"] / quant["seconds"] / 1e9, 1),

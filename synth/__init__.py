@@ -160,6 +160,32 @@ NEXT = {
 }
 
 
+# One GPU's share of each call of the decode step under an 8-way split:
+# split4, gate/up, the LM head and the lanes by output columns (each range
+# of split4 in eighths), the down projection by K (its partial y would be
+# summed across GPUs).  The activations are the full replicated vectors.
+SHARD8 = {
+    "split4": dict(N=832, K=4096, gs=128, n0=512, n1=640, n2=768),
+    "gated": dict(N=1792, K=4096, gs=128),
+    "down": dict(N=4096, K=1792, gs=128),
+    "lmhead": dict(N=18992, K=4096, gs=128, eps=1e-6),
+    "lanes": dict(N=3200, K=5120, gs=64, Ms=(1, 2, 4, 8)),
+}
+
+
+def shard8_inputs():
+    """Seeded weights of every shard-shaped call (activations: the configs' own vectors)."""
+    s = SHARD8
+    return dict(
+        W2=weights(0xC01, s["split4"]["N"], s["split4"]["K"]),
+        Wg=weights(0xC02, s["gated"]["N"], s["gated"]["K"]),
+        Wu=weights(0xC03, s["gated"]["N"], s["gated"]["K"]),
+        Wd=weights(0xC04, s["down"]["N"], s["down"]["K"]),
+        W4=weights(0xC05, s["lmhead"]["N"], s["lmhead"]["K"]),
+        W5=weights(0xC06, s["lanes"]["N"], s["lanes"]["K"]),
+    )
+
+
 def n1_inputs():
     c = NEXT["n1"]
     return dict(x=normal_f32(0x601, c["K"]), W0=weights(0x602, c["N"], c["K"]),

@@ -132,3 +132,54 @@ def test_c5_lanes(q4, M):
     Y = q4.int4_matvec(torch.from_numpy(inp["X"]).cuda(), qd, sd, zd)
     Y_ref, B = oracle.matvec(inp["X"], q, s, z, K, gs)
     assert_dot_close(host(Y)[:, cols], Y_ref, B, f"c5 M={M}")
+
+
+def test_one_gpu_share_of_8(q4):
+    """Every call of the step at one GPU's share of an 8-way split (columns;
+    K for the down projection), the shapes bench.py times as that share."""
+    import torch
+    sh = synth.SHARD8
+    w = synth.shard8_inputs()
+
+    def quant(W, gs):
+        return oracle.quantize_pack(W, gs)
+
+    def dev(*arrs):
+        return [torch.from_numpy(np.ascontiguousarray(a.view(np.int32) if a.dtype == np.uint32 else a)).cuda()
+                for a in arrs]
+
+    s2 = sh["split4"]
+    w2 = quant(w["W2"], s2["gs"])
+    x2 = synth.normal_f32(0x201, s2["K"])
+    outs = q4.int4_matvec_split4(*dev(x2, *w2), s2["n0"], s2["n1"], s2["n2"])
+    assert [o.numel() for o in outs] == [512, 128, 128, 64]
+    y_ref, B = oracle.matvec(x2, *w2, s2["K"], s2["gs"])
+    assert_dot_close(np.concatenate([host(o) for o in outs]), y_ref, B, "split4 share")
+
+    sg, sd = sh["gated"], sh["down"]
+    wg, wu, wd = quant(w["Wg"], sg["gs"]), quant(w["Wu"], sg["gs"]), quant(w["Wd"], sd["gs"])
+    x3 = synth.normal_f32(0x301, sg["K"])
+    h = q4.int4_matvec_gated(*dev(x3, *wg, *wu))
+    ref = oracle.gated(x3, *wg, *wu, sg["K"], sg["gs"])
+    hh = host(h)
+    assert np.all(np.abs(hh.astype(np.float64) - ref["h"]) <= gated_tolerance(ref)), "gated share"
+    y = q4.int4_matvec(h, *dev(*wd))
+    y_ref, B = oracle.matvec(hh, *wd, sd["K"], sd["gs"])
+    assert_dot_close(host(y), y_ref, B, "down K share")
+
+    s4 = sh["lmhead"]
+    w4 = quant(w["W4"], s4["gs"])
+    a = [synth.normal_f32(0x401, s4["K"]), synth.normal_f32(0x402, s4["K"]),
+         synth.uniform_f32(0x403, s4["K"], 0.5, 1.5)]
+    y, r, n = q4.int4_matvec_norm(*dev(*a), s4["eps"], *dev(*w4))
+    ref = oracle.norm(*a, s4["eps"], *w4, s4["K"], s4["gs"])
+    assert_dot_close(host(y), ref["y"], ref["B"], "LM head share")
+    np.testing.assert_array_equal(host(r), ref["residual"])
+
+    s5 = sh["lanes"]
+    w5 = quant(w["W5"], s5["gs"])
+    for M in (1, 2, 8):
+        X = synth.lanes(0x501, M, s5["K"])
+        Y = q4.int4_matvec(*dev(X, *w5))
+        Y_ref, B = oracle.matvec(X, *w5, s5["K"], s5["gs"])
+        assert_dot_close(host(Y), Y_ref, B, f"lanes share M={M}")
