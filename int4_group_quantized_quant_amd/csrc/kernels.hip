@@ -316,6 +316,7 @@ template <int M, int MODE, bool kPublish = false>
 __device__ __forceinline__ void store_column(const GemvArgs& a, int64_t col,
                                              const float (&tot)[mode_streams(MODE)][M],
                                              float inv) {
+  static_assert(!kPublish || MODE == kGated, "only the gated pass publishes its outputs");
   if constexpr (MODE == kPlain) {
 #pragma unroll
     for (int m = 0; m < M; ++m) a.out[0][(int64_t)m * a.N + col] = tot[0][m];
@@ -435,7 +436,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
     static_assert(M == 1, "a waiting pass reads one activation row");
     const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, n4 * 16, kBufferWord3);
     for (int i = threadIdx.x; i < n4; i += blockDim.x)
-      xl[((i & 7)) * a.U + (i >> 3)] = __builtin_bit_cast(
+      xl[(i & 7) * a.U + (i >> 3)] = __builtin_bit_cast(
           float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)i * 16u, 0, kLoadDeviceCoherent));
   } else {
 #pragma unroll
