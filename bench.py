@@ -579,6 +579,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (the JSON then carries cpu_baseline null)")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip the 1/8-share calls (the JSON then carries one_gpu_share_of_8 null); "
+                         "a kernel trace then holds only the full-size launches of each kernel")
     ap.add_argument("--counter-probe", action="store_true",
                     help="only launch the LM-head norm call and a plain 256 MiB device copy, "
                          "5 times each, for rocprofv3 --pmc runs (prints no JSON)")
@@ -639,39 +642,41 @@ def main():
 
     # One GPU's share of the step under an 8-way split: each call alone, then
     # the shard calls captured together as one step (not the metric).
-    log("one GPU's share of each call under an 8-way split")
-    shard_calls = build_shards(q4, torch, dev)
-    shard_rows = {}
-    for c in shard_calls:
-        us, r = time_call(torch, c)
-        shard_rows[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
-                              "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
-                              "alg_bytes": c.nbytes, "rotating_copies": r}
-        tag = "[1/8 share]" if getattr(c, "in_step", True) else "[1/8 share, not in the share step]"
-        log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
-            f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)  {tag}")
-    shard_calls = [c for c in shard_calls if getattr(c, "in_step", True)]
-    shard_sets = [c.sets_fn(1)[0] for c in shard_calls]
-    shard_graph = capture(torch, lambda: [c.fn(s) for c, s in zip(shard_calls, shard_sets)])
-    for _ in range(3):
-        shard_graph.replay()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(50):
-        shard_graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    shard_us = e0.elapsed_time(e1) * 1e3 / 50
-    shard_bytes = sum(c.nbytes for c in shard_calls)
-    log(f"1/8 share of the step: {shard_us:.1f} us, {shard_bytes / 1e6:.1f} MB")
-    shard = {"shards": 8, "split": "columns for split4 (each range in eighths), gate/up, the LM head "
-                                   "and the lanes; K for down (its partial y needs one 16 KB "
-                                   "all-reduce across GPUs, not built: one GPU only)",
-             "step_us": round(shard_us, 2), "step_alg_bytes": shard_bytes,
-             "step_GBps": round(shard_bytes / shard_us / 1e3, 1), "per_call": shard_rows}
-    del shard_graph, shard_sets, shard_calls
-    torch.cuda.empty_cache()
+    shard = None
+    shard_calls = [] if args.no_shards else build_shards(q4, torch, dev)
+    if shard_calls:
+        log("one GPU's share of each call under an 8-way split")
+        shard_rows = {}
+        for c in shard_calls:
+            us, r = time_call(torch, c)
+            shard_rows[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
+                                  "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
+                                  "alg_bytes": c.nbytes, "rotating_copies": r}
+            tag = "[1/8 share]" if getattr(c, "in_step", True) else "[1/8 share, not in the share step]"
+            log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
+                f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)  {tag}")
+        shard_calls = [c for c in shard_calls if getattr(c, "in_step", True)]
+        shard_sets = [c.sets_fn(1)[0] for c in shard_calls]
+        shard_graph = capture(torch, lambda: [c.fn(s) for c, s in zip(shard_calls, shard_sets)])
+        for _ in range(3):
+            shard_graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(50):
+            shard_graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        shard_us = e0.elapsed_time(e1) * 1e3 / 50
+        shard_bytes = sum(c.nbytes for c in shard_calls)
+        log(f"1/8 share of the step: {shard_us:.1f} us, {shard_bytes / 1e6:.1f} MB")
+        shard = {"shards": 8, "split": "columns for split4 (each range in eighths), gate/up, the LM head "
+                                       "and the lanes; K for down (its partial y needs one 16 KB "
+                                       "all-reduce across GPUs, not built: one GPU only)",
+                 "step_us": round(shard_us, 2), "step_alg_bytes": shard_bytes,
+                 "step_GBps": round(shard_bytes / shard_us / 1e3, 1), "per_call": shard_rows}
+        del shard_graph, shard_sets, shard_calls
+        torch.cuda.empty_cache()
 
     # The step graph.
     sets = [c.sets_fn(1)[0] for c in calls]
