@@ -1,9 +1,10 @@
 """Python binding of libint4gemv.so, the int4 group-quantized matvec library
 for MI355X (gfx950).  The C ABI is declared in include/int4gemv.h.
 
-This module only marshals arguments: it checks dtypes, devices and
-contiguity of torch tensors, allocates outputs with torch when the caller
-passes none, and calls the C entry point of the same name on torch's current
+This module only marshals arguments: it checks dtypes, devices,
+contiguity and element counts of torch tensors (the C ABI takes bare
+pointers, so a short buffer would otherwise be read or written past its
+end), allocates outputs with torch when the caller passes none, and calls the C entry point of the same name on torch's current
 HIP stream.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback.  If the library has not been built, the
 import fails.
@@ -107,6 +108,12 @@ def _dev(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
     return t
 
 
+def _size(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
+    if t.numel() != n:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call needs {n}")
+    return t
+
+
 _F32 = (torch.float32,)
 _CODES = (torch.int32, torch.uint32)
 
@@ -130,14 +137,16 @@ def int4_quantize_pack(W: torch.Tensor, group_size: int, q=None, scales=None, ze
                        stream=None):
     """W float32 [N, K] -> (q int32 [N, K/8], scales [N, K/gs], zeros [N, K/gs])."""
     _dev(W, "W", _F32)
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
     N, K = W.shape
     G = K // group_size if group_size > 0 else 0
     q = torch.empty((N, K // 8), dtype=torch.int32, device=W.device) if q is None else q
     scales = torch.empty((N, G), dtype=torch.float32, device=W.device) if scales is None else scales
     zeros = torch.empty((N, G), dtype=torch.float32, device=W.device) if zeros is None else zeros
-    _dev(q, "q", _CODES)
-    _dev(scales, "scales", _F32)
-    _dev(zeros, "zeros", _F32)
+    _size(_dev(q, "q", _CODES), N * (K // 8), "q")
+    _size(_dev(scales, "scales", _F32), N * G, "scales")
+    _size(_dev(zeros, "zeros", _F32), N * G, "zeros")
     _check(lib.int4_quantize_pack(_ptr(W), N, K, group_size, _ptr(q), _ptr(scales), _ptr(zeros),
                                   _stream(stream)))
     return q, scales, zeros
@@ -149,11 +158,11 @@ def int4_matvec(X: torch.Tensor, q, scales, zeros, Y=None, stream=None) -> torch
     _dev(X, "X", _F32)
     squeeze = X.dim() == 1
     M = 1 if squeeze else X.shape[0]
-    if X.shape[-1] != K:
-        raise ValueError(f"X has {X.shape[-1]} inputs, the weights {K}")
+    if X.dim() not in (1, 2) or X.shape[-1] != K:
+        raise ValueError(f"X must be [{K}] or [M, {K}]")
     if Y is None:
         Y = torch.empty((N,) if squeeze else (M, N), dtype=torch.float32, device=X.device)
-    _dev(Y, "Y", _F32)
+    _size(_dev(Y, "Y", _F32), M * N, "Y")
     _check(lib.int4_matvec(_ptr(X), M, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
                            _stream(stream)))
     return Y
@@ -163,9 +172,9 @@ def int4_matvec_split4(x: torch.Tensor, q, scales, zeros, n0: int, n1: int, n2: 
                        outs=None, stream=None):
     """One matvec over N columns routed to (out0[n0], out1[n1-n0], out2[n2-n1], out3[N-n2])."""
     N, K, gs = _weights(q, scales, zeros)
-    _dev(x, "x", _F32)
+    _size(_dev(x, "x", _F32), K, "x")
+    sizes = [n0, n1 - n0, n2 - n1, N - n2]
     if outs is None:
-        sizes = [n0, n1 - n0, n2 - n1, N - n2]
         outs = [torch.empty(max(sz, 0), dtype=torch.float32, device=x.device) for sz in sizes]
     ptrs = []
     for i, o in enumerate(outs):
@@ -173,6 +182,8 @@ def int4_matvec_split4(x: torch.Tensor, q, scales, zeros, n0: int, n1: int, n2: 
             ptrs.append(None)
         else:
             _dev(o, f"out{i}", _F32)
+            if sizes[i] >= 0:  # an unordered split is the library's INT4_ERR_ARG
+                _size(o, sizes[i], f"out{i}")
             ptrs.append(_ptr(o) if o.numel() else None)
     _check(lib.int4_matvec_split4(_ptr(x), _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs,
                                   n0, n1, n2, *ptrs, _stream(stream)))
@@ -186,9 +197,9 @@ def int4_matvec_gated(x: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up,
     N2, K2, gs2 = _weights(q_up, s_up, z_up, "_up")
     if (N, K, gs) != (N2, K2, gs2):
         raise ValueError("gate and up weights must share N, K and group size")
-    _dev(x, "x", _F32)
+    _size(_dev(x, "x", _F32), K, "x")
     h = torch.empty(N, dtype=torch.float32, device=x.device) if h is None else h
-    _dev(h, "h", _F32)
+    _size(_dev(h, "h", _F32), N, "h")
     _check(lib.int4_matvec_gated(_ptr(x), _ptr(q_gate), _ptr(s_gate), _ptr(z_gate), _ptr(q_up),
                                  _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(h), _stream(stream)))
     return h
@@ -200,16 +211,16 @@ def int4_matvec_norm(a_a: torch.Tensor, a_b: torch.Tensor, w_norm: torch.Tensor,
     """y = (RMSNorm(a_a + a_b) * w_norm) . w  -> (y, residual_out or None, norm_out or None)."""
     N, K, gs = _weights(q, scales, zeros)
     for t, name in ((a_a, "a_a"), (a_b, "a_b"), (w_norm, "w_norm")):
-        _dev(t, name, _F32)
+        _size(_dev(t, name, _F32), K, name)
     dev = a_a.device
     y = torch.empty(N, dtype=torch.float32, device=dev) if y is None else y
     if residual_out is None and want_residual:
         residual_out = torch.empty(K, dtype=torch.float32, device=dev)
     if norm_out is None and want_norm:
         norm_out = torch.empty(K, dtype=torch.float32, device=dev)
-    for t, name in ((y, "y"), (residual_out, "residual_out"), (norm_out, "norm_out")):
+    for t, name, n in ((y, "y", N), (residual_out, "residual_out", K), (norm_out, "norm_out", K)):
         if t is not None:
-            _dev(t, name, _F32)
+            _size(_dev(t, name, _F32), n, name)
     _check(lib.int4_matvec_norm(_ptr(a_a), _ptr(a_b), _ptr(w_norm), float(eps), _ptr(q),
                                 _ptr(scales), _ptr(zeros), N, K, gs,
                                 _ptr(y) if N else None, _ptr(residual_out), _ptr(norm_out),
@@ -239,8 +250,8 @@ def int4_matvec_dual(X: torch.Tensor, q0, s0, z0, q1, s1, z1, y0=None, y1=None, 
     M, shape = _lanes(X, K, "X")
     y0 = torch.empty(shape(N), dtype=torch.float32, device=X.device) if y0 is None else y0
     y1 = torch.empty(shape(N), dtype=torch.float32, device=X.device) if y1 is None else y1
-    _dev(y0, "y0", _F32)
-    _dev(y1, "y1", _F32)
+    _size(_dev(y0, "y0", _F32), M * N, "y0")
+    _size(_dev(y1, "y1", _F32), M * N, "y1")
     _check(lib.int4_matvec_dual(_ptr(X), M, _ptr(q0), _ptr(s0), _ptr(z0), _ptr(q1), _ptr(s1),
                                 _ptr(z1), N, K, gs, _ptr(y0), _ptr(y1), _stream(stream)))
     return y0, y1
@@ -254,7 +265,7 @@ def int4_matvec_sigmoid_gated(a: torch.Tensor, gate: torch.Tensor, q, scales, ze
     if _lanes(gate, K, "gate")[0] != M or gate.dim() != a.dim():
         raise ValueError("a and gate must have the same shape")
     y = torch.empty(shape(N), dtype=torch.float32, device=a.device) if y is None else y
-    _dev(y, "y", _F32)
+    _size(_dev(y, "y", _F32), M * N, "y")
     _check(lib.int4_matvec_sigmoid_gated(_ptr(a), _ptr(gate), M, _ptr(q), _ptr(scales),
                                          _ptr(zeros), N, K, gs, _ptr(y), _stream(stream)))
     return y
@@ -268,7 +279,7 @@ def int4_matvec_swiglu_gated(gate: torch.Tensor, up: torch.Tensor, q, scales, ze
     if _lanes(up, K, "up")[0] != M or up.dim() != gate.dim():
         raise ValueError("gate and up must have the same shape")
     y = torch.empty(shape(N), dtype=torch.float32, device=gate.device) if y is None else y
-    _dev(y, "y", _F32)
+    _size(_dev(y, "y", _F32), M * N, "y")
     _check(lib.int4_matvec_swiglu_gated(_ptr(gate), _ptr(up), M, _ptr(q), _ptr(scales),
                                         _ptr(zeros), N, K, gs, _ptr(y), _stream(stream)))
     return y
@@ -280,14 +291,14 @@ def int4_matvec_norm_swiglu(a_a: torch.Tensor, a_b: torch.Tensor, w_norm: torch.
     """h = silu(x . w_gate) * (x . w_up), x = RMSNorm(a_a + a_b) * w_norm -> (h, residual_out or None)."""
     N, K, gs = _pair(q_gate, s_gate, z_gate, q_up, s_up, z_up, "_gate", "_up")
     for t, name in ((a_a, "a_a"), (a_b, "a_b"), (w_norm, "w_norm")):
-        _dev(t, name, _F32)
+        _size(_dev(t, name, _F32), K, name)
     dev = a_a.device
     h = torch.empty(N, dtype=torch.float32, device=dev) if h is None else h
     if residual_out is None and want_residual:
         residual_out = torch.empty(K, dtype=torch.float32, device=dev)
-    for t, name in ((h, "h"), (residual_out, "residual_out")):
+    for t, name, n in ((h, "h", N), (residual_out, "residual_out", K)):
         if t is not None:
-            _dev(t, name, _F32)
+            _size(_dev(t, name, _F32), n, name)
     _check(lib.int4_matvec_norm_swiglu(_ptr(a_a), _ptr(a_b), _ptr(w_norm), float(eps),
                                        _ptr(q_gate), _ptr(s_gate), _ptr(z_gate), _ptr(q_up),
                                        _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(h) if N else None,
@@ -326,7 +337,7 @@ def int4_gemm(X: torch.Tensor, q, scales, zeros, Y=None, workspace=None, stream=
         raise ValueError(f"X must be [T, {K}]")
     T = X.shape[0]
     Y = torch.empty((T, N), dtype=torch.float32, device=X.device) if Y is None else Y
-    _dev(Y, "Y", _F32)
+    _size(_dev(Y, "Y", _F32), T * N, "Y")
     need = int4_gemm_workspace_bytes(T, N, K, gs)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
@@ -342,7 +353,7 @@ def int4_matvec_gated_lanes(X: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up,
     N, K, gs = _pair(q_gate, s_gate, z_gate, q_up, s_up, z_up, "_gate", "_up")
     M, shape = _lanes(X, K, "X")
     H = torch.empty(shape(N), dtype=torch.float32, device=X.device) if H is None else H
-    _dev(H, "H", _F32)
+    _size(_dev(H, "H", _F32), M * N, "H")
     _check(lib.int4_matvec_gated_lanes(_ptr(X), M, _ptr(q_gate), _ptr(s_gate), _ptr(z_gate),
                                        _ptr(q_up), _ptr(s_up), _ptr(z_up), N, K, gs, _ptr(H),
                                        _stream(stream)))
@@ -372,8 +383,8 @@ def int4_mlp(x: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, q_down, 
         raise ValueError(f"x must hold D = {D} floats")
     h = torch.empty(F, dtype=torch.float32, device=x.device) if h is None else h
     y = torch.empty(D, dtype=torch.float32, device=x.device) if y is None else y
-    _dev(h, "h", _F32)
-    _dev(y, "y", _F32)
+    _size(_dev(h, "h", _F32), F, "h")
+    _size(_dev(y, "y", _F32), D, "y")
     if workspace is None:
         workspace = torch.zeros(int4_mlp_workspace_bytes() // 4, dtype=torch.int32, device=x.device)
     _dev(workspace, "workspace", (torch.int32, torch.uint32, torch.uint8))

@@ -191,3 +191,47 @@ def test_mlp_default_workspace_and_shape_errors(q4):
     small = torch.zeros(1, dtype=torch.int32, device="cuda")
     with pytest.raises(q4.Int4Error):
         q4.int4_mlp(xd, *wg_d, *wu_d, *wd_d, workspace=small)
+
+
+def test_binding_rejects_short_buffers(q4):
+    """The C ABI takes bare pointers, so the binding checks every element
+    count: a short output or input raises before any launch."""
+    import torch
+    N, K, gs = 64, 256, 32
+    w = weights_dev(quantized(0x7160, N, K, gs))
+    w2 = weights_dev(quantized(0x7161, N, K, gs))
+    x = torch.zeros(K, device="cuda")
+    short = torch.zeros(N - 1, device="cuda")
+    shortK = torch.zeros(K - 4, device="cuda")
+    X2 = torch.zeros((2, K), device="cuda")
+    cases = [
+        lambda: q4.int4_matvec(x, *w, Y=short),
+        lambda: q4.int4_matvec(X2, *w, Y=torch.zeros(N, device="cuda")),
+        lambda: q4.int4_matvec_split4(shortK, *w, 16, 32, 48),
+        lambda: q4.int4_matvec_split4(x, *w, 16, 32, 48,
+                                      outs=[torch.zeros(n, device="cuda") for n in (16, 16, 16, 15)]),
+        lambda: q4.int4_matvec_gated(x, *w, *w2, h=short),
+        lambda: q4.int4_matvec_gated(shortK, *w, *w2),
+        lambda: q4.int4_matvec_norm(x, x, shortK, 1e-6, *w),
+        lambda: q4.int4_matvec_norm(x, x, x, 1e-6, *w, y=short),
+        lambda: q4.int4_matvec_norm(x, x, x, 1e-6, *w, residual_out=shortK),
+        lambda: q4.int4_matvec_dual(x, *w, *w2, y1=short),
+        lambda: q4.int4_matvec_sigmoid_gated(x, x, *w, y=short),
+        lambda: q4.int4_matvec_swiglu_gated(x, x, *w, y=short),
+        lambda: q4.int4_matvec_norm_swiglu(x, x, x, 1e-6, *w, *w2, h=short),
+        lambda: q4.int4_matvec_gated_lanes(X2, *w, *w2, H=torch.zeros(N, device="cuda")),
+        lambda: q4.int4_gemm(X2, *w, Y=torch.zeros((2, N - 1), device="cuda")),
+        lambda: q4.int4_quantize_pack(torch.zeros((N, K), device="cuda"), gs,
+                                      q=torch.zeros((N, K // 8 - 1), dtype=torch.int32, device="cuda")),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError):
+            case()
+        print(f"case {i} rejected", flush=True)
+    D, F = 256, 512
+    wm = [weights_dev(quantized(0x7162 + i, *shp, gs)) for i, shp in enumerate(((F, D), (F, D), (D, F)))]
+    with pytest.raises(ValueError):
+        q4.int4_mlp(torch.zeros(D, device="cuda"), *wm[0], *wm[1], *wm[2], y=torch.zeros(D - 1, device="cuda"))
+    with pytest.raises(ValueError):
+        q4.int4_mlp(torch.zeros(D, device="cuda"), *wm[0], *wm[1], *wm[2], h=torch.zeros(F - 1, device="cuda"))
+    torch.cuda.synchronize()
