@@ -25,7 +25,8 @@
  * Conventions shared by every entry point:
  *   - All array pointers are DEVICE pointers on the current HIP device, owned
  *     by the caller.  The library allocates nothing, keeps no pointer after
- *     the call returns and holds no per-call state.
+ *     the call returns and holds no state between calls (int4_mlp keeps its
+ *     call counter in the caller's workspace).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     asynchronously; the call never synchronizes.  A kernel fault surfaces at
  *     the caller's next synchronization.
