@@ -27,6 +27,11 @@ way and reported under "next_rows"; they are not part of the step:
   prefill  X[T, 4096] . W[4096, 4096]^T for T = 512 and 4096 (gs 128) on the matrix cores;
            reported as useful TFLOP/s (2 T N K flops per call, prep launch included)
 
+One GPU's share of every call of the step under an 8-way split (columns; K
+for the down projection; synth.SHARD8) is timed as well, each call alone and
+the eight together as one graph ("one_gpu_share_of_8"; --no-shards skips it):
+context for how the path would shard, not the metric.
+
 Each call also gets a warm number (the same buffers every call, labelled
 cache-resident: calls under 256 MB then run from the MALL), and the JSON
 carries torch's own read rate over 350 MB and 82 MB as context.
