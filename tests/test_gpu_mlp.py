@@ -18,10 +18,11 @@ pytestmark = pytest.mark.gpu
 
 # (D, F, gs, fused).  The first three run as one launch on this device (both
 # passes on the register kernel's one-block-per-CU grid, with 8/6/7/8-wave
-# rows and ragged column splits); the last two are small enough that the
-# passes' grids differ, so they run as two launches.
+# rows and ragged column splits); the next two are small enough that the
+# passes' grids differ, and in the last two one pass has more than 16384
+# inputs (the LDS kernel), so they run as two launches.
 SHAPES = [(1024, 2944, 128, True), (2048, 5632, 64, True), (4096, 1024, 32, True), (256, 512, 32, False),
-          (160, 96, 32, False)]
+          (160, 96, 32, False), (20480, 256, 128, False), (1024, 16896, 128, False)]
 
 
 @pytest.fixture(scope="module")
