@@ -1063,7 +1063,10 @@ hipError_t dispatch(Mode mode, const GemvArgs& a, const LaunchShape& s, hipStrea
 
 int max_ncol(Mode mode, int M, int variant) {
   if (variant == kVariantReg) {
-    if (mode_streams(mode) == 2) return 2;
+    // Measured per mode: two weight streams step one column at a time, the
+    // routed split4 call two, the other one-lane calls four.
+    if (mode_streams(mode) == 2) return 1;
+    if (mode == kSplit4) return 2;
     return M == 1 ? 4 : 2;
   }
   return mode == kPlain ? 2 : 1;
