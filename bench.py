@@ -711,7 +711,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3, 1),
                 "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3 / PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "gemv_reg_kernel<M=1,NCOL=4,kNorm,DEPTH=1> (int4_matvec_norm)",
+                "traffic": traffic, "kernel": "gemv_reg_kernel<M=1,NCOL=4,kNorm,short rows> (int4_matvec_norm)",
                 "alg_bytes_per_launch": dom["alg_bytes"], "us_per_launch": dom["us_per_call"]}
 
     cpu = None

@@ -131,7 +131,9 @@ hipError_t launch_or_query(Kern kern, std::atomic<bool>& raised, const GemvArgs&
   if (e != hipSuccess) return e;
   if (occupancy)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, kern, s.block_threads, s.lds_bytes);
-  hipLaunchKernelGGL(kern, dim3(s.grid), dim3(s.block_threads), s.lds_bytes, stream, a);
+  GemvArgs b = a;
+  b.block_threads = s.block_threads;
+  hipLaunchKernelGGL(kern, dim3(s.grid), dim3(s.block_threads), s.lds_bytes, stream, b);
   return hipGetLastError();
 }
 

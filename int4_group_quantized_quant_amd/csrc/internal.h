@@ -59,6 +59,9 @@ struct GemvArgs {
   int32_t mix24;        // matrix-core kernel: > 0 runs one slice per wave, this many
                         // waves of 24 units and the rest of 16 (whole cache lines)
   uint32_t g_recip;     // ceil(2^32 / G), 0 when G = 1 (matrix-core kernel's table copy)
+  int32_t block_threads;  // threads per block as launched, set by the launcher: the
+                          // kernels read it from their arguments, since blockDim.x
+                          // costs a vector load of the dispatch packet at entry
 };
 
 // Float offset of the staged activations in the register kernel's LDS: after

@@ -32,7 +32,7 @@
 // of at most 64 units.  A block holds P rows of nch waves (about 8 waves);
 // the block stages the activations once in LDS, then wave (p, c) keeps the
 // inputs of chunk c in registers, streams the columns of row p NCOL at a
-// time with the loads DEPTH steps ahead, and writes one partial per (column,
+// time with the loads one step ahead, and writes one partial per (column,
 // chunk) to an LDS table.  After one barrier the block sums each column's
 // partials in chunk order and runs the epilogue (routing, SiLU gate, norm
 // scale, plain store).  Blocks are persistent: one per CU.
@@ -364,7 +364,7 @@ struct InputsReady {
 // weight loads is issued before the call, so that they stream while it
 // waits, and the activations (written by other blocks of the launch) are
 // read at device scope.  kPublish stores the outputs at device scope.
-template <int M, int NCOL, int MODE, bool kPublish, class Ready>
+template <int M, int NCOL, int MODE, bool kPublish, bool kLongRows, class Ready>
 __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready inputs_ready) {
   constexpr int NSTREAM = mode_streams(MODE);
   constexpr int NSLOT = NCOL * NSTREAM;
@@ -372,6 +372,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   constexpr int NZ = (V + 3) / 4;
   constexpr bool kWaits = !__is_same(Ready, InputsReady);
 
+  const int bd = a.block_threads;  // threads per block, from the arguments
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_int(threadIdx.x >> 6);
   const int nch = a.nch;
@@ -398,10 +399,11 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   const int n4 = a.K >> 2;
   // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
   // before step i is computed.  With inputs at hand, the first weight loads
-  // go out after the activation loads (the memory counter is in order, so
-  // the staging would otherwise wait for them) and overlap the barrier;
-  // with inputs still being produced, they go out first and overlap the
-  // wait.  Every load is unconditional: steps past the wave's last column
+  // go out after the activation loads: after the whole staging for short
+  // rows (the memory counter is in order, so the staging would otherwise
+  // wait for them), between the loads and the LDS writes for long ones
+  // (kLongRows); with inputs still being produced, they go out first and
+  // overlap the wait.  Every load is unconditional: steps past the wave's last column
   // re-read that column, and a wave without columns has an empty buffer
   // range, whose loads return 0 without touching memory.
   const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
@@ -415,10 +417,35 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
     load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
     inputs_ready();
   }
-  if constexpr (mode_has_norm(MODE)) {
+  if constexpr (kLongRows) {
+    // A plain row of more than 4 float4s per thread (K > 8192 for a full
+    // block): each thread's float4s are loaded into registers, then the
+    // first weight loads are issued behind them, so waiting for the
+    // activations leaves the weights in flight.  A thread holds at most 8
+    // (K <= 2048 nch and the block has at least 64 nch threads); loads past
+    // the row return 0 without touching memory, and all 8 are issued so
+    // that the wait counts stay exact.  Shorter rows measured faster with
+    // the weights issued after the staging.
+    static_assert(M == 1 && MODE == kPlain && !kWaits, "long rows: one plain row with inputs at hand");
+    constexpr int kStageMax = 8;
+    const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, n4 * 16, kBufferWord3);
+    float4 v[kStageMax];
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j)
+      v[j] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(threadIdx.x + j * bd) * 16u, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+    load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j) {
+      const int i = (int)threadIdx.x + j * bd;
+      if (i < n4) xl[(i & 7) * a.U + (i >> 3)] = v[j];
+    }
+  } else if constexpr (mode_has_norm(MODE)) {
     // Per-thread share of sum_k r_k^2, then the wave's total in its slot.
     float ssq = 0.0f;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n4; i += bd) {
       float4 r, v;
       norm_in4(a, i, r, v);
       ssq = fmaf(r.x, r.x, ssq);
@@ -431,21 +458,21 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
     const float wsum = wave_sum(ssq);
     if (lane == 0) scratch[wave] = wsum;
   } else if constexpr (mode_gates_input(MODE)) {
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(i & 7) * a.U + (i >> 3)] = gated_in4<MODE>(a, i);
+    for (int i = threadIdx.x; i < n4; i += bd) xl[(i & 7) * a.U + (i >> 3)] = gated_in4<MODE>(a, i);
   } else if constexpr (kWaits) {
     static_assert(M == 1, "a waiting pass reads one activation row");
     const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, n4 * 16, kBufferWord3);
-    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+    for (int i = threadIdx.x; i < n4; i += bd)
       xl[(i & 7) * a.U + (i >> 3)] = __builtin_bit_cast(
           float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)i * 16u, 0, kLoadDeviceCoherent));
   } else {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K);
-      for (int i = threadIdx.x; i < n4; i += blockDim.x) xl[(m * 8 + (i & 7)) * a.U + (i >> 3)] = src[i];
+      for (int i = threadIdx.x; i < n4; i += bd) xl[(m * 8 + (i & 7)) * a.U + (i >> 3)] = src[i];
     }
   }
-  if constexpr (!kWaits) load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+  if constexpr (!kWaits && !kLongRows) load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
   __syncthreads();
   float x[M][32];
 #pragma unroll
@@ -509,10 +536,10 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   float inv = 1.0f;
   if constexpr (mode_has_norm(MODE)) {
     float ss = scratch[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) ss += scratch[w];
+    for (int w = 1; w < (bd >> 6); ++w) ss += scratch[w];
     inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
     if (blockIdx.x == 0 && a.norm_out) {
-      for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+      for (int i = threadIdx.x; i < n4; i += bd) {
         const float4 v = xl[(i & 7) * a.U + (i >> 3)];
         reinterpret_cast<float4*>(a.norm_out)[i] = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
       }
@@ -521,7 +548,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
 
   // Each column's chunk partials, summed in chunk order.
   const int64_t ncols = blk_end - blk_begin;
-  for (int64_t j = threadIdx.x; j < ncols; j += blockDim.x) {
+  for (int64_t j = threadIdx.x; j < ncols; j += bd) {
     float tot[NSTREAM][M];
 #pragma unroll
     for (int st = 0; st < NSTREAM; ++st)
@@ -536,11 +563,10 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   }
 }
 
-template <int M, int NCOL, int MODE, int DEPTH>
+template <int M, int NCOL, int MODE, bool kLongRows>
 __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
-  static_assert(DEPTH == 1, "the register pass keeps one step of loads in flight");
   extern __shared__ float part[];
-  reg_pass<M, NCOL, MODE, false>(a, part, InputsReady{});
+  reg_pass<M, NCOL, MODE, false, kLongRows>(a, part, InputsReady{});
 }
 
 // ------------------------------------------------------------ fused MLP
@@ -606,12 +632,12 @@ __global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs
   // Wave 0 publishes and polls; it alone needs the epoch.
   uint32_t epoch = 0;
   if (threadIdx.x < 64) epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  reg_pass<1, NCOL1, kGated, true>(gate_up, part, InputsReady{});
+  reg_pass<1, NCOL1, kGated, true, false>(gate_up, part, InputsReady{});
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores of h have completed
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_store(ws + kMlpFlags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  reg_pass<1, NCOL2, kPlain, false>(down, part, GridWait{ws, epoch});
+  reg_pass<1, NCOL2, kPlain, false, false>(down, part, GridWait{ws, epoch});
   if (blockIdx.x == 0 && threadIdx.x == 0)
     __hip_atomic_store(ws, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -982,7 +1008,17 @@ template <int MODE, int M, int NCOL>
 hipError_t launch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t stream, int* occupancy) {
   static std::atomic<bool> raised1{false};
   if (s.depth != 1) return hipErrorInvalidValue;  // one step ahead is the only form built
-  return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, 1>, raised1, a, s, stream, occupancy);
+  if constexpr (MODE == kPlain) {
+    // More than 4 float4s of the row per thread: the long-row staging, which
+    // holds at most 8.
+    const int64_t per_thread = ((int64_t)(a.K / 4) + s.block_threads - 1) / s.block_threads;
+    if (per_thread > 8) return hipErrorInvalidValue;
+    if (per_thread > 4) {
+      static std::atomic<bool> raised2{false};
+      return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, true>, raised2, a, s, stream, occupancy);
+    }
+  }
+  return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, false>, raised1, a, s, stream, occupancy);
 }
 
 template <int NCOL1, int NCOL2>
@@ -994,7 +1030,9 @@ hipError_t launch_mlp_t(const GemvArgs& gate_up, const GemvArgs& down, const Lau
   if (e != hipSuccess) return e;
   if (occupancy)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, kern, s.block_threads, s.lds_bytes);
-  hipLaunchKernelGGL(kern, dim3(s.grid), dim3(s.block_threads), s.lds_bytes, stream, gate_up, down, ws);
+  GemvArgs g = gate_up, d = down;
+  g.block_threads = d.block_threads = s.block_threads;
+  hipLaunchKernelGGL(kern, dim3(s.grid), dim3(s.block_threads), s.lds_bytes, stream, g, d, ws);
   return hipGetLastError();
 }
 

@@ -81,7 +81,7 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
   const int hi4 = lane >> 4;   // matrix layout: k group / D row group
   const int lo16 = lane & 15;  // matrix layout: column
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
+  const int W = a.block_threads >> 6;
   const int nbk = MODE == kDual ? (int)gridDim.x / 2 : (int)gridDim.x;
   const int stream = MODE == kDual && (int)blockIdx.x >= nbk ? 1 : 0;
   const int64_t bk = (int64_t)blockIdx.x - (int64_t)stream * nbk;
@@ -159,7 +159,7 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
     u32x4 tsv[NB], tzv[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint32_t off = (uint32_t)(threadIdx.x + b * blockDim.x) * 16u;
+      const uint32_t off = (uint32_t)(threadIdx.x + b * a.block_threads) * 16u;
       tsv[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadNonTemporal));
       tzv[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, kLoadNonTemporal));
     }
@@ -215,8 +215,8 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
         int tid = (int)threadIdx.x;
         asm volatile("" : "+v"(tid));
 #pragma unroll
-        for (int b = 0; b < NB; ++b) table_put(tid + b * (int)blockDim.x, tsv[b], tzv[b]);
-        for (int c = tid + NB * (int)blockDim.x; c < nchunk; c += (int)blockDim.x) {
+        for (int b = 0; b < NB; ++b) table_put(tid + b * a.block_threads, tsv[b], tzv[b]);
+        for (int c = tid + NB * a.block_threads; c < nchunk; c += a.block_threads) {
           const u32x4 sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)c * 16u, 0, kLoadNonTemporal));
           const u32x4 zv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)c * 16u, 0, kLoadNonTemporal));
           table_put(c, sv, zv);
@@ -224,7 +224,7 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
         if constexpr (NV == 2) {  // the up stream's table
           const auto rs1 = table_rsrc(sbase(1));
           const auto rz1 = table_rsrc(zbase(1));
-          for (int c = tid; c < nchunk; c += (int)blockDim.x) {
+          for (int c = tid; c < nchunk; c += a.block_threads) {
             const u32x4 sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs1, (uint32_t)c * 16u, 0, kLoadNonTemporal));
             const u32x4 zv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rz1, (uint32_t)c * 16u, 0, kLoadNonTemporal));
             table_put(c, sv, zv, 1);
@@ -416,7 +416,7 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
     __syncthreads();
     // Y for the round's tiles: the waves' partials added in wave order.
     const int nout = rn * M * 16;
-    for (int o = threadIdx.x; o < nout; o += blockDim.x) {
+    for (int o = threadIdx.x; o < nout; o += a.block_threads) {
       const int c = o & 15;
       const int tm = o >> 4;
       const int i = tm / M;
@@ -443,7 +443,7 @@ template <int SU, int GS, int DEPTH, int MODE>
 __global__ __launch_bounds__(64 * kSliceMaxWaves) void gemv_slice_kernel(GemvArgs a) {
   extern __shared__ float4 lds4[];
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int W = blockDim.x >> 6;
+  const int W = a.block_threads >> 6;
   slice_wave<SU, SU, GS, DEPTH, MODE>(a, lds4, SU * wave, SU * W);
 }
 
