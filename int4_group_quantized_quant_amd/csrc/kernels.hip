@@ -260,7 +260,7 @@ __device__ __forceinline__ float block_inv_rms(const GemvArgs& a, float* scratch
   const float4* aa = reinterpret_cast<const float4*>(a.x);
   const float4* ab = reinterpret_cast<const float4*>(a.x2);
   float ss = 0.0f;
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+  for (int i = threadIdx.x; i < n4; i += a.block_threads) {
     const float4 x1 = aa[i];
     const float4 x2 = ab[i];
     const float r0 = x1.x + x2.x, r1 = x1.y + x2.y, r2 = x1.z + x2.z, r3 = x1.w + x2.w;
@@ -273,7 +273,7 @@ __device__ __forceinline__ float block_inv_rms(const GemvArgs& a, float* scratch
   if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = wsum;
   __syncthreads();
   float total = scratch[0];
-  const int nw = blockDim.x >> 6;
+  const int nw = a.block_threads >> 6;
   for (int w = 1; w < nw; ++w) total += scratch[w];
   return 1.0f / sqrtf(total / (float)a.K + a.eps);
 }
@@ -295,7 +295,7 @@ __device__ __forceinline__ void write_norm_outputs(const GemvArgs& a, float inv)
   if (blockIdx.x != 0 || (a.residual_out == nullptr && a.norm_out == nullptr)) return;
   float4* res = reinterpret_cast<float4*>(a.residual_out);
   float4* nrm = reinterpret_cast<float4*>(a.norm_out);
-  for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
+  for (int i = threadIdx.x; i < (a.K >> 2); i += a.block_threads) {
     float4 r, x;
     norm_in4(a, i, r, x);
     if (res) res[i] = r;
@@ -647,11 +647,11 @@ __global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs
 // Activation row m is stored as float4 xl[m][j][u] = inputs 32u+4j .. 32u+4j+3,
 // pre-scaled like the register kernel's activations (prescale4).
 template <int M>
-__device__ __forceinline__ void stage_x(const float* __restrict__ X, int K, int U, float4* xl) {
+__device__ __forceinline__ void stage_x(const float* __restrict__ X, int K, int U, int bd, float4* xl) {
   const int n4 = K >> 2;
   for (int m = 0; m < M; ++m) {
     const float4* src = reinterpret_cast<const float4*>(X + (size_t)m * K);
-    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+    for (int i = threadIdx.x; i < n4; i += bd)
       xl[(m * 8 + (i & 7)) * U + (i >> 3)] = prescale4(src[i]);
   }
 }
@@ -666,23 +666,23 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   if constexpr (mode_has_norm(MODE)) {
     float* scratch = reinterpret_cast<float*>(xl + (size_t)8 * a.U);
     inv = block_inv_rms(a, scratch);
-    for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x) {
+    for (int i = threadIdx.x; i < (a.K >> 2); i += a.block_threads) {
       float4 r, v;
       norm_in4(a, i, r, v);
       xl[(i & 7) * a.U + (i >> 3)] = prescale4(v);
     }
     write_norm_outputs(a, inv);
   } else if constexpr (mode_gates_input(MODE)) {
-    for (int i = threadIdx.x; i < (a.K >> 2); i += blockDim.x)
+    for (int i = threadIdx.x; i < (a.K >> 2); i += a.block_threads)
       xl[(i & 7) * a.U + (i >> 3)] = prescale4(gated_in4<MODE>(a, i));
   } else {
-    stage_x<M>(a.x, a.K, a.U, xl);
+    stage_x<M>(a.x, a.K, a.U, a.block_threads, xl);
   }
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_int(threadIdx.x >> 6);
-  const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  const int64_t gw = (int64_t)blockIdx.x * (a.block_threads >> 6) + wave;
   const int64_t c_begin = uniform_i64(gw * a.N / a.total_waves);
   const int64_t c_end = uniform_i64((gw + 1) * a.N / a.total_waves);
   if (c_begin >= c_end) return;
@@ -776,20 +776,25 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
 
 // ------------------------------------------------------------ embedding gather
 
+// Threads per block of the embedding gather and the quantizers, a constant
+// in the kernels as well: blockDim.x would cost a load of the dispatch
+// packet before the first index is known.
+constexpr int kSmallBlock = 256;
+
 // out[t][k] = (code - zero) * scale of row ids[t] of a table stored like the
 // weight columns ([P1] EmbeddingInt4 and the per-layer-embedding row gather).
 // One lane per 32-bit code word: a 4-byte load, eight values, two 16-byte
 // stores, so a wave reads 256 contiguous bytes and writes 2 KiB.  The value
 // is rounded once, as the definition states.  Ids outside [0, N) write zeros.
-__global__ __launch_bounds__(256) void embedding_gather_kernel(const int32_t* __restrict__ ids, int64_t T,
+__global__ __launch_bounds__(kSmallBlock) void embedding_gather_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                                const uint32_t* __restrict__ q,
                                                                const float* __restrict__ scales,
                                                                const float* __restrict__ zeros, int64_t N,
                                                                int32_t K, int32_t gs, float* __restrict__ out) {
   const int64_t wpr = K >> 3;  // code words per row
   const int64_t total = T * wpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+  const int64_t stride = (int64_t)gridDim.x * kSmallBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kSmallBlock + threadIdx.x; i < total; i += stride) {
     const int64_t t = i / wpr;
     const int64_t w = i - t * wpr;
     const int64_t n = ids[t];
@@ -833,14 +838,14 @@ __device__ __forceinline__ float clamp_code(float v) {
 // batch's loads are issued before the current batch is quantized, so a wave
 // keeps two batches of inputs in flight.
 template <int WPT, int R>
-__global__ __launch_bounds__(256) void quantize_pack_wave_kernel(const float* __restrict__ W,
+__global__ __launch_bounds__(kSmallBlock) void quantize_pack_wave_kernel(const float* __restrict__ W,
                                                                  int64_t total_groups, int gs, int tpg,
                                                                  uint32_t* __restrict__ q,
                                                                  float* __restrict__ scales,
                                                                  float* __restrict__ zeros) {
   const int lane = threadIdx.x & 63;
   const int gpw = 64 / tpg;  // groups per wave and batch
-  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t wave_id = (int64_t)blockIdx.x * (kSmallBlock >> 6) + (threadIdx.x >> 6);
   const int64_t grp0 = wave_id * gpw * R + lane / tpg;
   const int part = lane & (tpg - 1);
   const int wpg = gs >> 3;
@@ -927,7 +932,7 @@ __global__ __launch_bounds__(256) void quantize_pack_wave_kernel(const float* __
   }
 }
 
-__global__ __launch_bounds__(256) void quantize_pack_kernel(const float* __restrict__ W,
+__global__ __launch_bounds__(kSmallBlock) void quantize_pack_kernel(const float* __restrict__ W,
                                                             int64_t total_groups, int gs, int tpg,
                                                             int gpb, uint32_t* __restrict__ q,
                                                             float* __restrict__ scales,
@@ -1137,9 +1142,9 @@ hipError_t launch_embedding(const int32_t* ids, int64_t T, const uint32_t* q, co
                             const float* zeros, int64_t N, int32_t K, int32_t gs, float* out,
                             hipStream_t stream) {
   const int64_t total = T * (K / 8);
-  int64_t grid = (total + 255) / 256;
+  int64_t grid = (total + kSmallBlock - 1) / kSmallBlock;
   if (grid > 65536) grid = 65536;  // grid-stride beyond this
-  hipLaunchKernelGGL(embedding_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ids, T, q,
+  hipLaunchKernelGGL(embedding_gather_kernel, dim3((unsigned)grid), dim3(kSmallBlock), 0, stream, ids, T, q,
                      scales, zeros, N, K, gs, out);
   return hipGetLastError();
 }
@@ -1157,19 +1162,19 @@ hipError_t launch_quantize(const float* W, int64_t total_groups, int32_t gs, uin
     const int64_t groups_per_block = 4 * (64 / tpg) * R;
     const int64_t grid = (total_groups + groups_per_block - 1) / groups_per_block;
     if (wpt == 1)
-      hipLaunchKernelGGL((quantize_pack_wave_kernel<1, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<1, R>), dim3((unsigned)grid), dim3(kSmallBlock), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     else if (wpt == 2)
-      hipLaunchKernelGGL((quantize_pack_wave_kernel<2, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<2, R>), dim3((unsigned)grid), dim3(kSmallBlock), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     else if (wpt <= 4)
-      hipLaunchKernelGGL((quantize_pack_wave_kernel<4, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<4, R>), dim3((unsigned)grid), dim3(kSmallBlock), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     else
-      hipLaunchKernelGGL((quantize_pack_wave_kernel<8, R>), dim3((unsigned)grid), dim3(256), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
+      hipLaunchKernelGGL((quantize_pack_wave_kernel<8, R>), dim3((unsigned)grid), dim3(kSmallBlock), 0, stream, W, total_groups, gs, tpg, q, scales, zeros);
     return hipGetLastError();
   }
   const int tpg = wpg < 256 ? wpg : 256;
   const int gpb = 256 / tpg < 64 ? 256 / tpg : 64;
   const int64_t grid = (total_groups + gpb - 1) / gpb;
-  hipLaunchKernelGGL(quantize_pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, W,
+  hipLaunchKernelGGL(quantize_pack_kernel, dim3((unsigned)grid), dim3(kSmallBlock), 0, stream, W,
                      total_groups, gs, tpg, gpb, q, scales, zeros);
   return hipGetLastError();
 }
