@@ -45,12 +45,20 @@ def test_worked_examples(q4):
     ex = json.load(open(GOLDEN))["examples"]
     rows = [np.array(e["w"], np.float32) for e in ex if "w" in e]
     rows += [np.full(32, e["w_const"], np.float32) for e in ex if "w_const" in e]
+    # Groups given in units of the smallest subnormal (the scale-underflow case).
+    sub = [e for e in ex if "w_units_of_min_subnormal" in e]
+    rows += [(np.array(e["w_units_of_min_subnormal"], np.float64) * 2.0 ** -149).astype(np.float32)
+             for e in sub]
     W = np.stack(rows)
     got = gpu_quantize(q4, W, 32)
     assert_bits_equal(W, 32, got, "worked examples")
-    for i, e in enumerate(x for x in ex if "w" in x):
+    with_words = [e for e in ex if "w" in e] + [None] * sum("w_const" in e for e in ex) + sub
+    for i, e in enumerate(with_words):
+        if e is None:
+            continue
         words = np.array([int(h, 16) for h in e["words"]], np.uint32)
-        np.testing.assert_array_equal(got[0][i], words)
+        np.testing.assert_array_equal(got[0][i], words, err_msg=e["name"])
+        np.testing.assert_array_equal(got[2][i], np.float32(e["zero"]), err_msg=e["name"])
 
 
 @pytest.mark.parametrize("gs", [32, 64, 96, 128, 256, 544])

@@ -39,7 +39,8 @@ def _scale_of(ex):
 
 
 @pytest.mark.parametrize("name", ["A_ties_to_even", "B_zero_clamped_at_0_code_clamped_at_15",
-                                  "C_zero_clamped_at_15"])
+                                  "C_zero_clamped_at_15", "E_zero_tie_rounds_down_to_even",
+                                  "F_zero_tie_rounds_up_to_even"])
 def test_worked_examples(name):
     ex = _example(name)
     W = np.array(ex["w"], np.float32).reshape(1, 32)
@@ -54,6 +55,36 @@ def test_ties_are_not_rounded_half_up():
     ex = _example("A_ties_to_even")
     q, _, _ = oracle.quantize_pack(np.array(ex["w"], np.float32).reshape(1, 32), 32)
     assert not np.array_equal(q[0], _words(ex["words_if_ties_rounded_half_up"]))
+
+
+@pytest.mark.parametrize("name,alt", [("E_zero_tie_rounds_down_to_even", "words_if_zero_rounded_half_up"),
+                                      ("F_zero_tie_rounds_up_to_even", "words_if_zero_truncated")])
+def test_zero_point_tie_rule(name, alt):
+    # -min/scale is exactly k + 1/2 in both groups: 4.5 -> 4 and 3.5 -> 4 under
+    # ties to even.  A half-up zero fails E, a truncated one fails F.
+    ex = _example(name)
+    q, s, z = oracle.quantize_pack(np.array(ex["w"], np.float32).reshape(1, 32), 32)
+    assert z[0, 0] == 4.0
+    np.testing.assert_array_equal(q[0], _words(ex["words"]))
+    assert not np.array_equal(q[0], _words(ex[alt]))
+    np.testing.assert_array_equal(_unpack(q[0], 32), np.array(ex["codes"]))
+
+
+def _min_subnormal_group(ex):
+    units = np.array(ex["w_units_of_min_subnormal"], np.float64)
+    return (units * 2.0 ** -149).astype(np.float32)
+
+
+def test_scale_underflow_group():
+    # max > min, but (max - min) / 15 underflows to 0: stored as an all-zero group.
+    ex = _example("G_scale_underflows_to_zero")
+    w = _min_subnormal_group(ex)
+    assert w.min() < 0 < w.max()
+    assert np.float32(w.max() - w.min()) / np.float32(15) == 0.0
+    q, s, z = oracle.quantize_pack(w.reshape(1, 32), 32)
+    assert s[0, 0] == 0.0 and z[0, 0] == 0.0 and z[0, 0] != ex["zero_if_underflow_not_handled"]
+    np.testing.assert_array_equal(q[0], _words(ex["words"]))
+    assert not np.any(np.isnan(oracle.dequant(q, s, z, 32, 32)))
 
 
 def test_example_a_dequantizes_onto_the_half_grid():
