@@ -19,6 +19,10 @@
  *   scales float  [N][K/gs]  scale of group g = k/gs of column n at [n*K/gs + g]
  *   zeros  float  [N][K/gs]  zero point, an integer value in [0, 15]
  *   w[n][k] = (code - zero) * scale            ([P4] WGSL_QUAD_MATVEC_INT4 dequant)
+ * Every kernel forms code - zero exactly, so a term whose code equals its
+ * zero point contributes exactly 0 (an output made only of such terms is 0),
+ * and each dot-product output is within 1e-4 * sum_k |x_k * w[n][k]| + 1e-6
+ * of the exact sum for any codes, any scales and any integer zero points.
  * Activations and outputs are fp32, row-major: X[m][k] at X[m*K + k],
  * Y[m][n] at Y[m*N + n].
  *

@@ -18,11 +18,12 @@
 //    v_fma_mix_f32 multiplies the fp32 activation by it.  Odd inputs use the
 //    nibble 4 bits higher (16 * code * 2^-24).  The activations are held
 //    pre-scaled by 2^24 (even inputs) and 2^20 (odd inputs), exact
-//    power-of-two scalings, so a unit's chain is sum x * code.  The zero
-//    point is constant over a unit, so sum x * (code - zero) is that chain
-//    minus zero * sum x, with the unit's activation sum computed once per
-//    lane.  Per 32 weights: 4 shifts, 16 AND, 32 mixed FMAs, then one FMA
-//    for the zero point and one multiply by the group's scale.
+//    power-of-two scalings.  The zero point, as an fp16 subnormal pair, is
+//    subtracted from each pair of masked codes with one packed fp16
+//    subtraction (exact), so each product is x * (code - zero) with one
+//    rounding, as the definition (code - zero) * scale gives it.  Per 32
+//    weights: 4 shifts, 16 AND, 16 packed subtractions, 32 mixed FMAs and
+//    one multiply by the group's scale.
 //  * Cross-lane sums are butterflies in the fixed order xor 32, xor 16 (lane
 //    swaps across wave halves / row pairs), then xor 8, 4, 2, 1 (DPP row
 //    rotations).  Several values are reduced at once by pairing them in the
@@ -126,31 +127,37 @@ struct Step {
   float z[NSLOT];
 };
 
-// The codes of the 32 inputs of one unit as 16 fp16 pairs, scaled by 2^-24
-// (even inputs) or 2^-20 (odd inputs): each nibble is masked in place into
-// the mantissa of a subnormal half, so the value is exact with no
-// conversion.  Pair 4i+t holds inputs 8i+t and 8i+t+4.
-__device__ __forceinline__ void unit_codes(u32x4 w, half2_t (&d)[16]) {
+// The zero point of a group as an fp16 subnormal pair (zero * 2^-24 in both
+// halves).  Zero points are integers in [0, 15], so the conversion is exact.
+__device__ __forceinline__ uint32_t zero_pair(float zero) { return (uint32_t)zero * 0x00010001u; }
+
+// The dequantized codes (code - zero) of the 32 inputs of one unit as 16
+// fp16 pairs, scaled by 2^-24 (even inputs) or 2^-20 (odd inputs): each
+// nibble is masked in place into the mantissa of a subnormal half (code *
+// 2^-24, or code * 2^-20 four bits up) and the zero point, shifted the same
+// way, is subtracted with one packed fp16 subtraction per pair.  Every
+// value is an integer multiple of 2^-24 below 2^-14 in magnitude, so all of
+// it is exact, as the definition (code - zero) * scale asks.  Pair 4i+t
+// holds inputs 8i+t and 8i+t+4.
+__device__ __forceinline__ void unit_codes(u32x4 w, uint32_t zh, half2_t (&d)[16]) {
+  const half2_t z0 = as_half2(zh), z1 = as_half2(zh << 4);
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t lo = words[i];
     const uint32_t hi = words[i] >> 8;
-    d[4 * i + 0] = as_half2(lo & 0x000F000Fu);
-    d[4 * i + 1] = as_half2(lo & 0x00F000F0u);
-    d[4 * i + 2] = as_half2(hi & 0x000F000Fu);
-    d[4 * i + 3] = as_half2(hi & 0x00F000F0u);
+    d[4 * i + 0] = as_half2(lo & 0x000F000Fu) - z0;
+    d[4 * i + 1] = as_half2(lo & 0x00F000F0u) - z1;
+    d[4 * i + 2] = as_half2(hi & 0x000F000Fu) - z0;
+    d[4 * i + 3] = as_half2(hi & 0x00F000F0u) - z1;
   }
 }
 
-// sum_k x[k] * (code_k - zero) over one unit (x pre-scaled, xs the unit's
-// activation sum from unit_xsum): the code products are accumulated k
-// ascending with one rounding each, then the zero point's term -zero * xs is
-// added with one fused rounding.  The zero point is constant over the unit
-// (a group spans whole units), so this is the dequantized dot product with
-// the subtraction moved out of the per-input work.
-__device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&d)[16], float xs,
-                                          float zero) {
+// sum_k x[k] * (code_k - zero) over one unit (x pre-scaled), accumulated k
+// ascending with one rounding per product: every product is of an fp32
+// activation and an exact small integer, so the only errors are the 32
+// roundings of the running sum.
+__device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&d)[16]) {
   float t = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -163,15 +170,6 @@ __device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&
     t = fmaf(x[8 * i + 6], (float)d[4 * i + 2].y, t);
     t = fmaf(x[8 * i + 7], (float)d[4 * i + 3].y, t);
   }
-  return fmaf(-zero, xs, t);
-}
-
-// Sum of one unit's 32 activations, k ascending, from the pre-scaled values
-// (multiplying by 2^-24 or 2^-20 undoes the scaling exactly).
-__device__ __forceinline__ float unit_xsum(const float (&x)[32]) {
-  float t = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) t += x[k] * ((k & 1) ? (1.0f / kOddScale) : (1.0f / kEvenScale));
   return t;
 }
 
@@ -480,19 +478,15 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
 #pragma unroll
     for (int j = 0; j < 8; ++j) put4(x[m], j, active ? xl[(m * 8 + j) * a.U + u] : make_float4(0.f, 0.f, 0.f, 0.f));
 
-  float xs[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) xs[m] = unit_xsum(x[m]);
-
   const bool writer = V >= 4 ? (lane & 15) == 0 : (V == 2 ? (lane & 31) == 0 : lane == 0);
   auto step = [&](int64_t n, const Step<NSLOT>& r) {
     float vals[V];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
       half2_t d[16];
-      unit_codes(r.q[sl], d);
+      unit_codes(r.q[sl], zero_pair(r.z[sl]), d);
 #pragma unroll
-      for (int m = 0; m < M; ++m) vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x[m], d, xs[m], r.z[sl]);
+      for (int m = 0; m < M; ++m) vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x[m], d);
     }
     float z[NZ];
     wave_reduce<V>(vals, z);
@@ -696,7 +690,7 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
     const bool active = lane < a.cw && u < a.U;
     half2_t d[NSLOT][16];
 #pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl) unit_codes(r.q[sl], d[sl]);
+    for (int sl = 0; sl < NSLOT; ++sl) unit_codes(r.q[sl], zero_pair(r.z[sl]), d[sl]);
     float vals[M * NSLOT];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -709,10 +703,8 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
         x[4 * j + 2] = v.z;
         x[4 * j + 3] = v.w;
       }
-      const float xs = unit_xsum(x);
 #pragma unroll
-      for (int sl = 0; sl < NSLOT; ++sl)
-        vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x, d[sl], xs, r.z[sl]);
+      for (int sl = 0; sl < NSLOT; ++sl) vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x, d[sl]);
     }
     float tot[M * NSLOT];
     wave_totals<M * NSLOT>(vals, tot);
