@@ -299,6 +299,26 @@ int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales,
               const float* zeros, int64_t N, int64_t K, int32_t group_size, float* Y,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The prefill GEMM for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): int4_gemm with its workspace taken from a scratch array that
+ * the library holds in device memory, INT4_GEMM_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) on each GPU it runs on, from the library's load until the
+ * process ends.  The call allocates nothing.  A problem whose workspace
+ * (int4_gemm_workspace_bytes(T, N, K, group_size)) exceeds that size
+ * returns INT4_ERR_SHAPE with nothing launched (e.g. at K = 4096 up to
+ * about T = 3968).  The scratch holds nothing across calls, but every call
+ * on one GPU uses the same array: two calls that overlap in time on one GPU
+ * (other streams or other host threads) race and give undefined results;
+ * calls ordered on one stream are safe.  Arguments, validation and
+ * results are those of int4_gemm, bit for bit.
+ */
+#define INT4_GEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int int4_gemm_noalloc(const float* X, int64_t T, const uint32_t* q, const float* scales,
+                      const float* zeros, int64_t N, int64_t K, int32_t group_size, float* Y,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ __all__ = [
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
     "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
     "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "int4_mlp", "int4_mlp_workspace_bytes",
-    "lib", "LIB_PATH",
+    "int4_gemm_noalloc", "INT4_GEMM_NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -61,6 +61,8 @@ lib.int4_matvec_gated_lanes.restype = ctypes.c_int
 lib.int4_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_gemm.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, ctypes.c_size_t, _vp]
+lib.int4_gemm_noalloc.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_gemm_noalloc.restype = ctypes.c_int
 lib.int4_mlp_workspace_bytes.argtypes = []
 lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_mlp.argtypes = [_vp] * 10 + [_i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -344,6 +346,30 @@ def int4_gemm(X: torch.Tensor, q, scales, zeros, Y=None, workspace=None, stream=
     _dev(workspace, "workspace", (torch.uint8,))
     _check(lib.int4_gemm(_ptr(X), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
                          _ptr(workspace), workspace.numel(), _stream(stream)))
+    return Y
+
+
+# Size of the scratch array int4_gemm_noalloc uses on each GPU (the header's
+# INT4_GEMM_NOALLOC_SCRATCH_BYTES).
+INT4_GEMM_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def int4_gemm_noalloc(X: torch.Tensor, q, scales, zeros, Y=None, stream=None) -> torch.Tensor:
+    """int4_gemm with the library's own scratch: the C call allocates nothing.
+
+    Pass Y to allocate nothing at all (otherwise torch allocates it here).
+    Problems whose workspace exceeds INT4_GEMM_NOALLOC_SCRATCH_BYTES raise
+    Int4Error (INT4_ERR_SHAPE); calls that overlap in time on one GPU race.
+    """
+    N, K, gs = _weights(q, scales, zeros)
+    _dev(X, "X", _F32)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError(f"X must be [T, {K}]")
+    T = X.shape[0]
+    Y = torch.empty((T, N), dtype=torch.float32, device=X.device) if Y is None else Y
+    _size(_dev(Y, "Y", _F32), T * N, "Y")
+    _check(lib.int4_gemm_noalloc(_ptr(X), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
+                                 _stream(stream)))
     return Y
 
 

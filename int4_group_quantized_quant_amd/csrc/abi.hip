@@ -17,6 +17,11 @@
 #include "int4gemv.h"
 #include "internal.h"
 
+// One copy per device of the allocation-free GEMM's workspace
+// (int4_gemm_noalloc), held from the code object's load until the process
+// ends.
+static __device__ __align__(256) unsigned char scratch[INT4_GEMM_NOALLOC_SCRATCH_BYTES];
+
 namespace int4gemv {
 namespace {
 
@@ -352,6 +357,80 @@ void fill_common(GemvArgs& a, int64_t N, int64_t K, int32_t gs) {
   a.g_magic = group_magic(gs);
 }
 
+// ------------------------------------------------------------ prefill GEMM
+
+// Checks shared by both GEMM entry points (everything but the workspace);
+// fills the workspace layout.
+int gemm_validate(const float* X, int64_t T, const uint32_t* q, const float* scales, const float* zeros,
+                  int64_t N, int64_t K, int32_t group_size, float* Y, GemmLayout* L) {
+  if (N < 0 || T < 0) return fail(INT4_ERR_SHAPE, "N and T must be >= 0 (N=%lld, T=%lld)", (long long)N,
+                                  (long long)T);
+  RETURN_IF(check_kgs(K, group_size));
+  if (N == 0 || T == 0) return INT4_OK;
+  if ((uint64_t)N * (uint64_t)K / 2 >= ((uint64_t)1 << 31))
+    return fail(INT4_ERR_SHAPE, "N*K/2 = %llu bytes of codes exceed 2^31", (unsigned long long)N * K / 2);
+  *L = gemm_layout(T, N, K, group_size);
+  if ((uint64_t)L->Tp * (uint64_t)L->Kp * 4 >= ((uint64_t)1 << 40) || L->Tp / 128 * (L->Np / 128) >= ((int64_t)1 << 30))
+    return fail(INT4_ERR_SHAPE, "T=%lld is larger than supported", (long long)T);
+  if (!X || !q || !scales || !zeros || !Y) return fail(INT4_ERR_NULL, "X, q, scales, zeros and Y are required");
+  RETURN_IF(check_align(X, 16, "X"));
+  RETURN_IF(check_align(q, 16, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(Y, 4, "Y"));
+  return INT4_OK;
+}
+
+// The prep and GEMM launches over a validated problem and a workspace of at
+// least L.bytes (256-byte aligned).
+int gemm_launch(const float* X, int64_t T, const uint32_t* q, const float* scales, const float* zeros,
+                int64_t N, int64_t K, int32_t group_size, float* Y, const GemmLayout& L, char* ws,
+                void* stream) {
+  GemmArgs a{};
+  a.X = X;
+  a.s = scales;
+  a.z = zeros;
+  a.q = q;
+  a.Y = Y;
+  a.xs = reinterpret_cast<uint32_t*>(ws + L.xs_off);
+  a.fac = reinterpret_cast<float*>(ws + L.fac_off);
+  a.st = reinterpret_cast<float*>(ws + L.st_off);
+  a.zt = reinterpret_cast<uint32_t*>(ws + L.zt_off);
+  a.T = T;
+  a.N = N;
+  a.Tp = L.Tp;
+  a.Np = L.Np;
+  a.Gp = L.Gp;
+  a.RB = L.Tp / 128;
+  // 128 x 256 tiles halve the activation bytes each CU loads per product
+  // (the activations are re-read once per column tile); they need enough
+  // row blocks to keep the CUs busy, so short prompts use 128 x 128.
+  a.BN = gemm_block_cols(L.Tp, group_size);
+  a.CB = (N + a.BN - 1) / a.BN;
+  a.qbytes = (int64_t)(N * K / 2);
+  a.K = (int32_t)K;
+  a.Kp = (int32_t)L.Kp;
+  a.gs = group_size;
+  a.G = (int32_t)(K / group_size);
+  // Split K in two when the 128 x 128 tiles alone would leave CUs idle.
+  DeviceInfo dev;
+  RETURN_IF(device_info(&dev));
+  a.S = (a.RB * a.CB < dev.cus && L.Kp / 64 >= 2) ? 2 : 1;
+  hipError_t e = launch_gemm(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Scratch of int4_gemm_noalloc.  `scratch` names the host-side stand-in of
+// the device array; its device address on each device comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is ever handed to a kernel.
+constexpr size_t kGemmScratchBytes = INT4_GEMM_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+std::array<char*, 64> g_scratch_ptr{};
+
+int gemm_scratch(char** out);
+
 int run(Mode mode, GemvArgs& a, void* stream) {
   LaunchShape s{};
   RETURN_IF(plan(mode, a, &s));
@@ -360,6 +439,23 @@ int run(Mode mode, GemvArgs& a, void* stream) {
   return ok();
 }
 
+
+int gemm_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= (int)g_scratch_ptr.size()) return fail(INT4_ERR_HIP, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(INT4_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return INT4_OK;
+}
 }  // namespace
 }  // namespace int4gemv
 
@@ -845,64 +941,40 @@ size_t int4_gemm_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t group_
 int int4_gemm(const float* X, int64_t T, const uint32_t* q, const float* scales, const float* zeros,
               int64_t N, int64_t K, int32_t group_size, float* Y, void* workspace,
               size_t workspace_bytes, void* stream) {
-  if (N < 0 || T < 0) return fail(INT4_ERR_SHAPE, "N and T must be >= 0 (N=%lld, T=%lld)", (long long)N,
-                                  (long long)T);
-  RETURN_IF(check_kgs(K, group_size));
+  GemmLayout L;
+  RETURN_IF(gemm_validate(X, T, q, scales, zeros, N, K, group_size, Y, &L));
   if (N == 0 || T == 0) return ok();
-  if ((uint64_t)N * (uint64_t)K / 2 >= ((uint64_t)1 << 31))
-    return fail(INT4_ERR_SHAPE, "N*K/2 = %llu bytes of codes exceed 2^31", (unsigned long long)N * K / 2);
-  const GemmLayout L = gemm_layout(T, N, K, group_size);
-  if ((uint64_t)L.Tp * (uint64_t)L.Kp * 4 >= ((uint64_t)1 << 40) || L.Tp / 128 * (L.Np / 128) >= ((int64_t)1 << 30))
-    return fail(INT4_ERR_SHAPE, "T=%lld is larger than supported", (long long)T);
-  if (!X || !q || !scales || !zeros || !Y) return fail(INT4_ERR_NULL, "X, q, scales, zeros and Y are required");
   if (!workspace) return fail(INT4_ERR_NULL, "workspace is required (int4_gemm_workspace_bytes)");
   if (workspace_bytes < L.bytes)
     return fail(INT4_ERR_SHAPE, "workspace holds %zu bytes; this call needs %zu", workspace_bytes, L.bytes);
-  RETURN_IF(check_align(X, 16, "X"));
-  RETURN_IF(check_align(q, 16, "q"));
-  RETURN_IF(check_align(scales, 4, "scales"));
-  RETURN_IF(check_align(zeros, 4, "zeros"));
-  RETURN_IF(check_align(Y, 4, "Y"));
   RETURN_IF(check_align(workspace, 256, "workspace"));
   const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
   const Span ins[] = {{X, (uint64_t)T * K * 4, "X"}, {q, (uint64_t)N * K / 2, "q"},
                       {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
   const Span outs[] = {{Y, (uint64_t)T * N * 4, "Y"}, {workspace, L.bytes, "workspace"}};
   RETURN_IF(check_alias(ins, 4, outs, 2));
-  char* ws = static_cast<char*>(workspace);
-  GemmArgs a{};
-  a.X = X;
-  a.s = scales;
-  a.z = zeros;
-  a.q = q;
-  a.Y = Y;
-  a.xs = reinterpret_cast<uint32_t*>(ws + L.xs_off);
-  a.fac = reinterpret_cast<float*>(ws + L.fac_off);
-  a.st = reinterpret_cast<float*>(ws + L.st_off);
-  a.zt = reinterpret_cast<uint32_t*>(ws + L.zt_off);
-  a.T = T;
-  a.N = N;
-  a.Tp = L.Tp;
-  a.Np = L.Np;
-  a.Gp = L.Gp;
-  a.RB = L.Tp / 128;
-  // 128 x 256 tiles halve the activation bytes each CU loads per product
-  // (the activations are re-read once per column tile); they need enough
-  // row blocks to keep the CUs busy, so short prompts use 128 x 128.
-  a.BN = gemm_block_cols(L.Tp, group_size);
-  a.CB = (N + a.BN - 1) / a.BN;
-  a.qbytes = (int64_t)(N * K / 2);
-  a.K = (int32_t)K;
-  a.Kp = (int32_t)L.Kp;
-  a.gs = group_size;
-  a.G = (int32_t)(K / group_size);
-  // Split K in two when the 128 x 128 tiles alone would leave CUs idle.
-  DeviceInfo dev;
-  RETURN_IF(device_info(&dev));
-  a.S = (a.RB * a.CB < dev.cus && L.Kp / 64 >= 2) ? 2 : 1;
-  hipError_t e = launch_gemm(a, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
-  return ok();
+  return gemm_launch(X, T, q, scales, zeros, N, K, group_size, Y, L, static_cast<char*>(workspace), stream);
+}
+
+int int4_gemm_noalloc(const float* X, int64_t T, const uint32_t* q, const float* scales,
+                      const float* zeros, int64_t N, int64_t K, int32_t group_size, float* Y,
+                      void* stream) {
+  GemmLayout L;
+  RETURN_IF(gemm_validate(X, T, q, scales, zeros, N, K, group_size, Y, &L));
+  if (N == 0 || T == 0) return ok();
+  if (L.bytes > kGemmScratchBytes)
+    return fail(INT4_ERR_SHAPE,
+                "T=%lld, N=%lld, K=%lld need %zu bytes of scratch; the allocation-free GEMM holds %zu "
+                "(use int4_gemm with a workspace)",
+                (long long)T, (long long)N, (long long)K, L.bytes, kGemmScratchBytes);
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{X, (uint64_t)T * K * 4, "X"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{Y, (uint64_t)T * N * 4, "Y"}};
+  RETURN_IF(check_alias(ins, 4, outs, 1));
+  char* ws = nullptr;
+  RETURN_IF(gemm_scratch(&ws));
+  return gemm_launch(X, T, q, scales, zeros, N, K, group_size, Y, L, ws, stream);
 }
 
 }  // extern "C"

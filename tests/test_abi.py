@@ -238,6 +238,28 @@ def test_gemm_workspace_and_validation(lib):
     assert "2^31" in _err(lib)
 
 
+def test_gemm_noalloc_validation(lib):
+    # Every case fails (or returns) before the library looks up its scratch
+    # array, so none of them touches a device.
+    lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.int4_gemm_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    T, N, K, gs = 5, 77, 96, 96
+    assert lib.int4_gemm_noalloc(None, 0, None, None, None, N, K, gs, None, None) == OK   # T == 0
+    assert lib.int4_gemm_noalloc(A, T, B, C, D, 0, K, gs, None, None) == OK               # N == 0
+    assert lib.int4_gemm_noalloc(A, -1, B, C, D, N, K, gs, E, None) == SHAPE
+    assert lib.int4_gemm_noalloc(A, T, B, C, D, N, K, 48, E, None) == SHAPE
+    assert lib.int4_gemm_noalloc(A, T, B, C, D, N, K, gs, None, None) == NULL
+    assert lib.int4_gemm_noalloc(None, T, B, C, D, N, K, gs, E, None) == NULL
+    assert lib.int4_gemm_noalloc(A + 4, T, B, C, D, N, K, gs, E, None) == ALIGN
+    assert lib.int4_gemm_noalloc(A, T, B, C, D, N, K, gs, A + 16, None) == ALIAS         # Y over X
+    # The scratch holds 64 MiB: T = 4096 at K = 4096 needs more and is refused.
+    big = lib.int4_gemm_workspace_bytes(4096, 4096, 4096, 128)
+    assert big > 64 << 20
+    assert lib.int4_gemm_noalloc(A, 4096, B, C, D, 4096, 4096, 128, E, None) == SHAPE
+    assert "scratch" in _err(lib)
+    assert lib.int4_gemm_workspace_bytes(3968, 4096, 4096, 128) <= 64 << 20
+
+
 def test_mlp_workspace_and_validation(lib):
     lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
     need = lib.int4_mlp_workspace_bytes()
