@@ -33,17 +33,24 @@ the eight together as one graph ("one_gpu_share_of_8"; --no-shards skips it):
 context for how the path would shard, not the metric.
 
 Each call also gets a warm number (the same buffers every call, labelled
-cache-resident: calls under 256 MB then run from the MALL), and the JSON
-carries torch's own read rate over 350 MB and 82 MB as context.
+cache-resident: calls under 256 MB then run from the MALL).  The single
+1024x1024 matvec (gs 128) is timed the same way as a row of its own, outside
+the step.
+
+stream_read_ceiling: a plain streaming read of each call's algorithmic bytes
+(the library's probe kernel, best of a few launch shapes, rotating >= 1 GiB)
+is timed too; each row's pct_of_stream_read is that read's time over the
+call's time.
 
 Per-call durations: each call is also timed alone, in a graph of back-to-back
 calls cycling over >= 1 GiB of device copies of its buffers, with HIP events
 on the stream the kernels run on.  The norm LM head call is the dominant
 kernel; its roofline entry uses that measured duration.
 
-cpu_baseline: the CPU oracle (plain C, one thread) timed on a bounded sample
-of the same step (the first fraction f of every call's columns), converted to
-GB/s over the sampled algorithmic bytes.
+cpu_baseline: the CPU oracle (plain C, fp64 dot products) over every column
+of every call of the step on all its OpenMP threads, and on one thread over a
+bounded sample (the first fraction f of every call's columns); each the
+median of three passes, in GB/s of algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -118,6 +125,19 @@ class Call:
         self.fn = fn            # fn(buffer_set) enqueues the call
         self.sets_fn = sets_fn  # sets_fn(r) -> list of r buffer sets (device copies)
         self.weight_bytes = weight_bytes
+
+
+def build_single(q4, torch, dev):
+    """The single 1024x1024 matvec (gs 128): a per-call row of its own, not part
+    of the step (it moves 0.6 MB, so it measures launch latency, not HBM)."""
+    c1 = synth.CONFIGS["c1"]
+    i1 = synth.c1_inputs()
+    w1 = q4.int4_quantize_pack(torch.from_numpy(i1["W"]).to(dev), c1["gs"])
+    x1 = torch.from_numpy(i1["x"]).to(dev)
+    y1 = torch.empty(c1["N"], device=dev)
+    sets = lambda r: [tuple(w1)] + [tuple(t.clone() for t in w1) for _ in range(r - 1)]
+    return Call(f"single {c1['N']}x{c1['K']}", alg_bytes(c1["N"], c1["K"], c1["gs"], c1["K"], c1["N"]),
+                lambda s: q4.int4_matvec(x1, *s, Y=y1), sets, sum(t.numel() * 4 for t in w1))
 
 
 def build_workload(q4, torch, dev):
@@ -467,32 +487,54 @@ def time_call_warm(torch, call, n=32, replays=6):
     return e0.elapsed_time(e1) * 1e3 / (replays * n)
 
 
-def streaming_read_context(torch, dev):
-    """Read rate of torch's own sum over fp32 buffers of the LM-head and lanes
-    sizes (rotating copies past the MALL), timed eagerly: context for the
-    per-call rates, not a bound of this library."""
+# Launch shapes tried for the streaming-read ceiling: (blocks per CU, waves
+# per block, 16-byte loads in flight per lane); the fastest is reported.
+STREAM_SHAPES = ((1, 8, 4), (1, 16, 2), (2, 8, 2), (1, 8, 2), (2, 4, 4))
+
+
+def stream_read_ceiling(q4, torch, dev, sizes, cus):
+    """Time of one plain streaming read of each size (the library's probe
+    kernel: buffer loads, XOR checksum, persistent grid), over rotating
+    slices of >= 1 GiB so the MALL cannot serve it, best over STREAM_SHAPES."""
     out = {}
-    for label, nbytes, copies in (("350MB", 350750208, 2), ("82MB", 82042880, 4)):
-        bufs = [torch.ones(nbytes // 4, device=dev) for _ in range(copies)]
-        for b in bufs:
-            b.sum()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 8
-        e0.record()
-        for i in range(reps * copies):
-            bufs[i % copies].sum()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-        out[label] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
-        del bufs
+    sink = torch.empty(2 * cus, dtype=torch.int32, device=dev)
+    for nbytes in sorted(set(sizes)):
+        n16 = -(-nbytes // 16) * 16
+        r = max(2, min(64, -(-MALL_ROTATE_BYTES // n16)))
+        buf = torch.ones(r * n16 // 4, dtype=torch.float32, device=dev)
+        best = None
+        for bpc, waves, unroll in STREAM_SHAPES:
+            blocks = bpc * cus
+
+            def reads():
+                for i in range(r):
+                    q4.int4_probe_stream_read(buf[i * n16 // 4:(i + 1) * n16 // 4], sink[:blocks], blocks,
+                                              waves, unroll)
+            g = capture(torch, reads)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(4):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (4 * r)
+            if best is None or us < best[0]:
+                best = (us, bpc, waves, unroll)
+            del g
+        out[nbytes] = {"us": round(best[0], 3), "GBps": round(nbytes / best[0] / 1e3, 1),
+                       "shape": f"{best[1]} block(s)/CU x {best[2]} waves, {best[3]} loads in flight per lane"}
+        log(f"streaming read {nbytes / 1e6:9.1f} MB {best[0]:9.2f} us {nbytes / best[0] / 1e3:8.1f} GB/s")
+        del buf
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(calls_meta, budget_s=12.0):
-    """Time the oracle on the first fraction f of every call's columns."""
+def cpu_baseline(single_budget_s=3.0):
+    """The oracle (plain C, fp64 dot products) on the step's calls: all of every
+    call on all the threads OpenMP gives it, and a bounded sample on one
+    thread; each the median of three passes."""
     import oracle
     c2, c3, c4, c5 = (synth.CONFIGS[k] for k in ("c2", "c3", "c4", "c5"))
 
@@ -510,6 +552,7 @@ def cpu_baseline(calls_meta, budget_s=12.0):
                       c3["Kd"], 128, 1))
         W = synth.weights(0x404, max(1, int(c4["N"] * frac)), c4["K"])
         items.append(("norm", None, oracle.quantize_pack(W, 128), c4["K"], 128, 1))
+        del W
         W = synth.weights(0x502, max(1, int(c5["N"] * frac)), c5["K"])
         w5 = oracle.quantize_pack(W, 64)
         for M in c5["Ms"]:
@@ -531,21 +574,38 @@ def cpu_baseline(calls_meta, budget_s=12.0):
                 nbytes += alg_bytes(N, K, gs, M * K, M * N)
         return nbytes, time.perf_counter() - t0
 
-    probe = 0.002
-    nb, dt = run(prep(probe))
-    frac = min(1.0, probe * budget_s / max(dt, 1e-6))
-    log(f"cpu baseline: probe f={probe} took {dt:.2f}s, timing the oracle on f={frac:.4f}")
-    items = prep(frac)
-    nb, dt, passes = 0, 0.0, 0
-    # The whole step may take less than the budget: then time repeated passes.
-    while passes == 0 or (frac >= 1.0 and dt < budget_s):
-        b, t = run(items)
-        nb, dt, passes = nb + b, dt + t, passes + 1
-    return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"first {frac:.4f} of the columns of every call of the step, "
-                       f"{passes} pass(es) ({nb / 1e6:.1f} MB algorithmic), one thread, plain C "
-                       f"oracle with fp64 dot products; {dt:.1f} s"),
-            "seconds": dt}
+    def median3(items):
+        runs = sorted((run(items) for _ in range(3)), key=lambda bt: bt[0] / bt[1])
+        return runs[1]
+
+    threads = oracle.max_threads()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    full = prep(1.0)
+    nb_all, dt_all = median3(full)
+    del full
+    log(f"cpu baseline: whole step on {threads} threads, {dt_all:.2f}s per pass (median of 3)")
+    oracle.set_threads(1)
+    try:
+        probe = 0.002
+        nb, dt = run(prep(probe))
+        frac = min(1.0, probe * single_budget_s / max(dt, 1e-6))
+        items = prep(frac)
+        nb_one, dt_one = median3(items)
+    finally:
+        oracle.set_threads(threads)
+    log(f"cpu baseline: f={frac:.4f} of the step on one thread, {dt_one:.2f}s per pass (median of 3)")
+    return {"value": round(nb_all / dt_all / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"every column of every call of the step ({nb_all / 1e6:.1f} MB algorithmic), "
+                       f"median of 3 passes of {dt_all:.2f} s, {threads} OpenMP threads over output columns; "
+                       "plain C oracle, fp64 dot products"),
+            "host_cpus": os.cpu_count(), "host_cpus_usable": affinity,
+            "single_thread": {"value": round(nb_one / dt_one / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "sample": (f"first {frac:.4f} of the columns of every call of the step "
+                                         f"({nb_one / 1e6:.1f} MB algorithmic), median of 3 passes "
+                                         f"of {dt_one:.2f} s")}}
 
 
 def counter_probe(q4, torch, dev):
@@ -613,15 +673,18 @@ def main():
     calls, quant, keep = build_workload(q4, torch, dev)
     step_bytes = sum(c.nbytes for c in calls)
 
-    # Per-call durations (rotating copies, graphs of back-to-back calls).
+    # Per-call durations (rotating copies, graphs of back-to-back calls); the
+    # single small matvec is timed the same way but is not part of the step.
     per_call = {}
-    for c in calls:
+    for c in [build_single(q4, torch, dev)] + calls:
         us, r = time_call(torch, c)
         warm = time_call_warm(torch, c)
         per_call[c.name] = {"us_per_call": round(us, 3), "GBps": round(c.nbytes / us / 1e3, 1),
                             "pct_peak": round(100 * c.nbytes / us / 1e3 / PEAK_GBS, 1),
                             "alg_bytes": c.nbytes, "rotating_copies": r,
-                            "warm_us_per_call": round(warm, 3)}
+                            "warm_us_per_call": round(warm, 3),
+                            "dtype": ("f32 activations split into fp16 hi + lo on the matrix cores, "
+                                      "fp32 accumulation" if re.search(r"M=[2-8]", c.name) else "f32")}
         log(f"{c.name:28s} {us:9.2f} us  {c.nbytes / us / 1e3:8.1f} GB/s  "
             f"({100 * c.nbytes / us / 1e3 / PEAK_GBS:5.1f}% of 8 TB/s)")
 
@@ -714,15 +777,26 @@ def main():
                 "traffic": traffic, "kernel": "gemv_reg_kernel<M=1,NCOL=4,kNorm,short rows> (int4_matvec_norm)",
                 "alg_bytes_per_launch": dom["alg_bytes"], "us_per_launch": dom["us_per_call"]}
 
+    # The streaming-read ceiling at every call's size, and each call's share of it.
+    ceiling = stream_read_ceiling(q4, torch, dev, [v["alg_bytes"] for v in per_call.values()]
+                                  + [v["alg_bytes"] for v in next_rows.values() if "TFLOPs" not in v],
+                                  props.multi_processor_count)
+    for rows in (per_call, next_rows):
+        for v in rows.values():
+            if v["alg_bytes"] in ceiling and "TFLOPs" not in v:
+                v["stream_read_us"] = ceiling[v["alg_bytes"]]["us"]
+                v["pct_of_stream_read"] = round(100 * ceiling[v["alg_bytes"]]["us"] / v["us_per_call"], 1)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(calls)
+        cpu = cpu_baseline()
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 (lanes M=2,4,8: f32 activations split into fp16 hi + lo, fp32 accumulation)",
         "data": "synthetic",
         "config": {"workload": ("decode step: split4 6656x4096 + gated MLP 2x14336x4096 + "
                                 "down 4096x14336 + norm LM head 151936x4096 (gs 128) + "
@@ -734,7 +808,7 @@ def main():
         "per_call": per_call,
         "next_rows": next_rows,
         "one_gpu_share_of_8": shard,
-        "streaming_read_context": streaming_read_context(torch, dev),
+        "stream_read_ceiling": {str(k): v for k, v in ceiling.items()},
         "quantize_pack": {"elements": quant["elements"], "seconds": round(quant["seconds"], 5),
                           "GBps_fp32_in": round(4 * quant["elements"] / quant["seconds"] / 1e9, 1),
                           "GBps_alg": round((4.5 * quant["elements"] + 8 * quant["groups"])

@@ -319,6 +319,19 @@ int int4_gemm_noalloc(const float* X, int64_t T, const uint32_t* q, const float*
                       const float* zeros, int64_t N, int64_t K, int32_t group_size, float* Y,
                       void* stream);
 
+/*
+ * Measurement, not part of the method: one plain streaming read of `bytes`
+ * bytes of `buf` (16-byte aligned, a multiple of 16), the ceiling that the
+ * matvec calls' effective bandwidth is compared with.  `blocks` blocks of
+ * `waves` waves (1..16) each read one contiguous slice with `unroll` (1, 2
+ * or 4) 16-byte loads per lane in flight, and write the XOR of every 32-bit
+ * word of their slice to sink[block] (`blocks` words).  Returns INT4_ERR_NULL,
+ * _ALIGN, _SHAPE (a slice of 2 GiB or more) or _ARG (unroll) on bad
+ * arguments, _HIP on a launch failure; asynchronous on `stream`.
+ */
+int int4_probe_stream_read(const void* buf, size_t bytes, int32_t blocks, int32_t waves,
+                           int32_t unroll, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

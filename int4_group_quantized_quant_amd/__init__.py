@@ -24,7 +24,7 @@ __all__ = [
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
     "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
     "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "int4_mlp", "int4_mlp_workspace_bytes",
-    "int4_gemm_noalloc", "INT4_GEMM_NOALLOC_SCRATCH_BYTES", "lib", "LIB_PATH",
+    "int4_gemm_noalloc", "INT4_GEMM_NOALLOC_SCRATCH_BYTES", "int4_probe_stream_read", "lib", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint4gemv.so")
@@ -63,6 +63,8 @@ lib.int4_gemm_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_gemm.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, ctypes.c_size_t, _vp]
 lib.int4_gemm_noalloc.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 lib.int4_gemm_noalloc.restype = ctypes.c_int
+lib.int4_probe_stream_read.argtypes = [_vp, ctypes.c_size_t, _i32, _i32, _i32, _vp, _vp]
+lib.int4_probe_stream_read.restype = ctypes.c_int
 lib.int4_mlp_workspace_bytes.argtypes = []
 lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_mlp.argtypes = [_vp] * 10 + [_i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -371,6 +373,17 @@ def int4_gemm_noalloc(X: torch.Tensor, q, scales, zeros, Y=None, stream=None) ->
     _check(lib.int4_gemm_noalloc(_ptr(X), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs, _ptr(Y),
                                  _stream(stream)))
     return Y
+
+
+def int4_probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int, waves: int = 8,
+                           unroll: int = 4, stream=None) -> None:
+    """Measurement only: one streaming read of all of `buf` (any dtype, 16-byte
+    multiple), XOR checksum of each block's slice into the int32 `sink`."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda or sink.dtype not in _CODES:
+        raise ValueError("buf must be a contiguous device tensor and sink a device int32 tensor")
+    _size(sink, blocks, "sink")
+    _check(lib.int4_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), blocks, waves, unroll,
+                                      _ptr(sink), _stream(stream)))
 
 
 def int4_matvec_gated_lanes(X: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, H=None,

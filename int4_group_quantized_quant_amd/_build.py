@@ -20,7 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libint4gemv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "slice.hip", "gemm.hip", "abi.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "slice.hip", "gemm.hip", "abi.hip",
+                                                   "probe.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -21,7 +21,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-             "-fno-fast-math", "-Wall", "-Wextra"]
+             "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra"]
 
 
 def build(verbose: bool = False) -> str:
@@ -51,6 +51,10 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_set_threads.argtypes = [_i32]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = _i32
     lib.oracle_quantize_pack.argtypes = [_f32p, _i64, _i64, _i32, _u32p, _f32p, _f32p]
     lib.oracle_dequant.argtypes = [_u32p, _f32p, _f32p, _i64, _i64, _i32, _f32p]
     lib.oracle_matvec.argtypes = [_f32p, _i32, _u32p, _f32p, _f32p, _i64, _i64, _i32, _f64p, _f64p]
@@ -244,6 +248,16 @@ def embedding(ids, q, scales, zeros, K: int, group_size: int) -> np.ndarray:
     _load().oracle_embedding(ids, ids.shape[0], q, _c(scales, np.float32), _c(zeros, np.float32),
                              N, K, group_size, out)
     return out
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's column loops use (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    """Threads the oracle's column loops use now."""
+    return int(_load().oracle_max_threads())
 
 
 def tolerance(B):

@@ -26,13 +26,22 @@
  * the exact IEEE binary32 sequence written below.
  *
  * Parity pins live in tests/test_oracle_*.py; no function here is unpinned.
+ * Loops over independent output columns (or groups, or rows) are shared out
+ * over OpenMP threads; nothing within one output depends on the thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include "oracle.h"
+
+/* Output columns are independent, so the loops over them run on OpenMP
+ * threads; each column is still computed by one thread in exactly the order
+ * written, so the results do not depend on the thread count. */
+void oracle_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
+int32_t oracle_max_threads(void) { return (int32_t)omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- helpers */
 
@@ -79,7 +88,10 @@ static float clamp_0_15(float v) {
 void oracle_quantize_pack(const float* W, int64_t N, int64_t K, int32_t gs,
                           uint32_t* q, float* scales, float* zeros) {
     int64_t groups = K / gs;
+#pragma omp parallel
+    {
     unsigned* cbuf = (unsigned*)malloc(sizeof(unsigned) * (size_t)gs);
+#pragma omp for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t g = 0; g < groups; ++g) {
             const float* w = W + n * K + g * gs;
@@ -119,11 +131,13 @@ void oracle_quantize_pack(const float* W, int64_t N, int64_t K, int32_t gs,
         }
     }
     free(cbuf);
+    }
 }
 
 /* Dequantized matrix, binary32 [N][K]: dq[n][k] = (code - zero) * scale. */
 void oracle_dequant(const uint32_t* q, const float* scales, const float* zeros,
                     int64_t N, int64_t K, int32_t gs, float* dq) {
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k)
             dq[n * K + k] = dq_at(q, scales, zeros, K, gs, n, k);
@@ -142,6 +156,7 @@ void oracle_matvec(const float* X, int32_t M, const uint32_t* q, const float* sc
                    double* Y, double* B) {
     for (int32_t m = 0; m < M; ++m) {
         const float* x = X + (int64_t)m * K;
+#pragma omp parallel for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0, mag = 0.0;
             for (int64_t k = 0; k < K; ++k) {
@@ -163,6 +178,7 @@ void oracle_matvec_f32(const float* X, int32_t M, const uint32_t* q, const float
                        const float* zeros, int64_t N, int64_t K, int32_t gs, float* Y) {
     for (int32_t m = 0; m < M; ++m) {
         const float* x = X + (int64_t)m * K;
+#pragma omp parallel for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
             float acc = 0.0f;
             for (int64_t k = 0; k < K; ++k) {
@@ -239,6 +255,7 @@ void oracle_norm(const float* a_a, const float* a_b, const float* w_norm, float 
     double inv_rms = 1.0 / sqrt(ss / (double)K + (double)eps);
     for (int64_t k = 0; k < K; ++k)
         normed[k] = (double)residual[k] * inv_rms * (double)w_norm[k];
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         double acc = 0.0, mag = 0.0;
         for (int64_t k = 0; k < K; ++k) {
@@ -290,6 +307,7 @@ void oracle_input_gated(int32_t kind, const float* a, const float* b,
         else
             xg[k] = (ak / (1.0 + exp(-ak))) * bk;
     }
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         double acc = 0.0, mag = 0.0;
         for (int64_t k = 0; k < K; ++k) {
@@ -335,6 +353,7 @@ void oracle_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm,
  */
 void oracle_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
                       const float* zeros, int64_t N, int64_t K, int32_t gs, float* out) {
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         int64_t n = ids[t];
         for (int64_t k = 0; k < K; ++k)

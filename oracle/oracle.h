@@ -51,6 +51,10 @@ void oracle_norm_swiglu(const float* a_a, const float* a_b, const float* w_norm,
 void oracle_embedding(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
                       const float* zeros, int64_t N, int64_t K, int32_t gs, float* out);
 
+/* Threads the column loops use (OpenMP); results do not depend on it. */
+void oracle_set_threads(int32_t n);
+int32_t oracle_max_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -260,6 +260,18 @@ def test_gemm_noalloc_validation(lib):
     assert lib.int4_gemm_workspace_bytes(3968, 4096, 4096, 128) <= 64 << 20
 
 
+def test_probe_validation(lib):
+    sz = ctypes.c_size_t
+    assert lib.int4_probe_stream_read(None, sz(1024), 4, 8, 4, B, None) == NULL
+    assert lib.int4_probe_stream_read(A, sz(1024), 4, 8, 4, None, None) == NULL
+    assert lib.int4_probe_stream_read(A + 8, sz(1024), 4, 8, 4, B, None) == ALIGN
+    assert lib.int4_probe_stream_read(A, sz(1000), 4, 8, 4, B, None) == ALIGN
+    assert lib.int4_probe_stream_read(A, sz(1024), 0, 8, 4, B, None) == SHAPE
+    assert lib.int4_probe_stream_read(A, sz(1024), 4, 17, 4, B, None) == SHAPE
+    assert lib.int4_probe_stream_read(A, sz(1 << 32), 1, 8, 4, B, None) == SHAPE  # a 4 GiB slice
+    assert lib.int4_probe_stream_read(A, sz(1024), 4, 8, 3, B, None) == ARG
+
+
 def test_mlp_workspace_and_validation(lib):
     lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
     need = lib.int4_mlp_workspace_bytes()

@@ -119,8 +119,7 @@ def test_lanes_table_limit(q4):
 def test_lanes_many_rounds(q4):
     """More tiles per block than the LDS partial table holds (70000 columns at
     K = 16416: two rounds per block).  Random packed codes, integer zero
-    points; a contiguous run of columns across blocks and rounds, a random
-    sample and the last columns are checked."""
+    points; every output is checked."""
     rng = np.random.default_rng(0xB700)
     N, K, gs, M = 70000, 16416, 32, 3
     q = rng.integers(0, 2**32, (N, K // 8), dtype=np.uint32)
@@ -128,10 +127,8 @@ def test_lanes_many_rounds(q4):
     z = rng.integers(0, 16, (N, K // gs)).astype(np.float32)
     X = synth.lanes(0xB701, M, K)
     Y = run_matvec(q4, X, q, s, z)
-    cols = np.unique(np.concatenate([np.arange(800), rng.choice(N, 300, replace=False),
-                                     np.arange(N - 8, N)]))
-    Y_ref, B = oracle.matvec(X, q[cols], s[cols], z[cols], K, gs)
-    assert_dot_close(Y[:, cols], Y_ref, B, "lanes, two rounds")
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    assert_dot_close(Y, Y_ref, B, "lanes, two rounds")
 
 
 @pytest.mark.parametrize("K,gs", [(256, 32), (1024, 128), (2080, 32), (5120, 64)])

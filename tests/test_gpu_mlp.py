@@ -112,7 +112,7 @@ def test_mlp_matches_oracle_and_separate_calls(q4, D, F, gs, fused):
 def test_mlp_full_size(q4):
     """The SiLU-gated MLP at its workload size (gate/up 14336 x 4096, down
     4096 x 14336, gs 128), the launch the bench times; the down projection
-    is checked on sampled columns against the oracle on the GPU's h."""
+    is checked over every column against the oracle on the GPU's h."""
     import torch
     c = synth.CONFIGS["c3"]
     inp = synth.c3_inputs()
@@ -130,11 +130,9 @@ def test_mlp_full_size(q4):
                        D, gs)
     hh = host(h)
     assert np.all(np.abs(hh.astype(np.float64) - ref["h"]) <= gated_tolerance(ref)), "h"
-    rng = np.random.default_rng(0x7110)
-    cols = np.unique(np.concatenate([rng.choice(D, 256, replace=False), np.arange(8), np.arange(D - 8, D)]))
-    qd, sd, zd = (host(t[torch.from_numpy(cols).cuda()]) for t in wd_d)
+    qd, sd, zd = (host(t) for t in wd_d)
     y_ref, B = oracle.matvec(hh, qd.view(np.uint32), sd, zd, F, gs)
-    assert_dot_close(host(y)[cols], y_ref, B, "y")
+    assert_dot_close(host(y), y_ref, B, "y")
     check_separate(q4, xd, wg_d, wu_d, wd_d, h, y)
     check_workspace(ws, 1)
 

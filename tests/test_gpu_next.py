@@ -219,21 +219,13 @@ def test_embedding_gather_empty_cases(q4):
 
 # ------------------------------------------------------------------ full workload sizes
 
-def sample_cols(N, seed):
-    rng = np.random.default_rng(seed)
-    cols = set(rng.choice(N, size=min(N, 384), replace=False).tolist())
-    cols |= set(range(min(N, 8))) | set(range(max(0, N - 8), N))
-    return np.array(sorted(cols))
-
-
-def gpu_quantized(q4, W, gs, cols):
-    """GPU codes for all of W, oracle codes for the sampled rows (compared bitwise)."""
+def gpu_quantized(q4, W, gs):
+    """GPU and oracle codes of all of W, compared bit for bit over every row."""
     import torch
     qd, sd, zd = q4.int4_quantize_pack(torch.from_numpy(W).cuda(), gs)
-    ref = oracle.quantize_pack(W[cols], gs)
-    idx = torch.from_numpy(cols).cuda()
+    ref = oracle.quantize_pack(W, gs)
     for got, want in zip((qd, sd, zd), ref):
-        np.testing.assert_array_equal(bits(host(got[idx])), bits(want))
+        np.testing.assert_array_equal(bits(host(got)), bits(want))
     return (qd, sd, zd), ref
 
 
@@ -241,47 +233,43 @@ def test_n1_dual_full(q4):
     import torch
     c = synth.NEXT["n1"]
     inp = synth.n1_inputs()
-    cols = sample_cols(c["N"], 0x61)
-    (w0, r0) = gpu_quantized(q4, inp["W0"], c["gs"], cols)
-    (w1, r1) = gpu_quantized(q4, inp["W1"], c["gs"], cols)
+    (w0, r0) = gpu_quantized(q4, inp["W0"], c["gs"])
+    (w1, r1) = gpu_quantized(q4, inp["W1"], c["gs"])
     y0, y1 = q4.int4_matvec_dual(torch.from_numpy(inp["x"]).cuda(), *w0, *w1)
     ref = oracle.dual(inp["x"], *r0, *r1, c["K"], c["gs"])
-    assert_dot_close(host(y0)[cols], ref["y0"], ref["b0"], "n1 y0")
-    assert_dot_close(host(y1)[cols], ref["y1"], ref["b1"], "n1 y1")
+    assert_dot_close(host(y0), ref["y0"], ref["b0"], "n1 y0")
+    assert_dot_close(host(y1), ref["y1"], ref["b1"], "n1 y1")
 
 
 def test_n2_sigmoid_gated_full(q4):
     import torch
     c = synth.NEXT["n2"]
     inp = synth.n2_inputs()
-    cols = sample_cols(c["N"], 0x62)
-    w, r = gpu_quantized(q4, inp["W"], c["gs"], cols)
+    w, r = gpu_quantized(q4, inp["W"], c["gs"])
     y = q4.int4_matvec_sigmoid_gated(*to_dev(inp["a"], inp["gate"]), *w)
     ref = oracle.sigmoid_gated(inp["a"], inp["gate"], *r, c["K"], c["gs"])
-    assert_dot_close(host(y)[cols], ref["y"], ref["B"], "n2")
+    assert_dot_close(host(y), ref["y"], ref["B"], "n2")
 
 
 def test_n3_swiglu_gated_full(q4):
     c = synth.NEXT["n3"]
     inp = synth.n3_inputs()
-    cols = sample_cols(c["N"], 0x63)
-    w, r = gpu_quantized(q4, inp["W"], c["gs"], cols)
+    w, r = gpu_quantized(q4, inp["W"], c["gs"])
     y = q4.int4_matvec_swiglu_gated(*to_dev(inp["gate"], inp["up"]), *w)
     ref = oracle.swiglu_gated(inp["gate"], inp["up"], *r, c["K"], c["gs"])
-    assert_dot_close(host(y)[cols], ref["y"], ref["B"], "n3")
+    assert_dot_close(host(y), ref["y"], ref["B"], "n3")
 
 
 def test_n4_norm_swiglu_full(q4):
     c = synth.NEXT["n4"]
     inp = synth.n4_inputs()
-    cols = sample_cols(c["N"], 0x64)
-    wg, rg = gpu_quantized(q4, inp["Wg"], c["gs"], cols)
-    wu, ru = gpu_quantized(q4, inp["Wu"], c["gs"], cols)
+    wg, rg = gpu_quantized(q4, inp["Wg"], c["gs"])
+    wu, ru = gpu_quantized(q4, inp["Wu"], c["gs"])
     dev = to_dev(inp["a_a"], inp["a_b"], inp["w_norm"])
     h, r = q4.int4_matvec_norm_swiglu(*dev, inp["eps"], *wg, *wu)
     ref = oracle.norm_swiglu(inp["a_a"], inp["a_b"], inp["w_norm"], inp["eps"], *rg, *ru,
                              c["K"], c["gs"])
-    hh = host(h)[cols].astype(np.float64)
+    hh = host(h).astype(np.float64)
     assert np.all(np.abs(hh - ref["h"]) <= gated_tolerance(ref)), "n4"
     np.testing.assert_array_equal(host(r), ref["residual"])
 
@@ -290,17 +278,14 @@ def test_n5_embedding_gather_full(q4):
     import torch
     c = synth.NEXT["n5"]
     inp = synth.n5_inputs()
-    rows = sample_cols(c["N"], 0x65)
-    w, r = gpu_quantized(q4, inp["W"], c["gs"], rows)
+    w, r = gpu_quantized(q4, inp["W"], c["gs"])
     del inp["W"]
-    # Gather T ids drawn from the sampled rows (so the oracle holds their codes),
-    # in the order and multiplicity of the workload's id stream.
+    # The workload's id stream over the whole table, every row compared.
     T = max(c["Ts"])
-    ids = rows[inp["ids"] % len(rows)].astype(np.int32)
+    ids = inp["ids"].astype(np.int32)
+    assert ids.shape == (T,)
     out = host(q4.int4_embedding_gather(torch.from_numpy(ids).cuda(), *w))
-    # The oracle table holds the sampled rows only: map each id to its position there.
-    pos = np.searchsorted(rows, ids).astype(np.int32)
-    ref = oracle.embedding(pos, *r, c["K"], c["gs"])
+    ref = oracle.embedding(ids, *r, c["K"], c["gs"])
     assert out.shape == (T, c["K"])
     np.testing.assert_array_equal(bits(out), bits(ref))
 
