@@ -608,33 +608,80 @@ def cpu_baseline(single_budget_s=3.0):
                                          f"of {dt_one:.2f} s")}}
 
 
+# Calls the counter probe launches, in this order, each PROBE_REPS times on
+# rotating weight copies: (label, kind, N, K, gs, M).  The labels name the
+# rows of the counter summaries in profiles/.
+PROBE_CALLS = (
+    ("split4 6656x4096", "split4", 6656, 4096, 128, 1),
+    ("gated 2x14336x4096", "gated", 14336, 4096, 128, 1),
+    ("down 4096x14336", "plain", 4096, 14336, 128, 1),
+    ("norm LM head 151936x4096", "norm", 151936, 4096, 128, 1),
+    ("lanes M=1 25600x5120", "plain", 25600, 5120, 64, 1),
+    ("lanes M=2 25600x5120", "plain", 25600, 5120, 64, 2),
+    ("lanes M=4 25600x5120", "plain", 25600, 5120, 64, 4),
+    ("lanes M=8 25600x5120", "plain", 25600, 5120, 64, 8),
+    ("MLP fused 2x14336x4096 + 4096x14336", "mlp", 14336, 4096, 128, 1),
+)
+PROBE_REPS = 5
+PROBE_COPY_BYTES = 1 << 28
+
+
 def counter_probe(q4, torch, dev):
-    """Launches for hardware-counter runs: the LM-head norm call on four
-    rotating weight copies (random codes and groups: the bytes a launch moves
-    do not depend on the values), then a plain device copy of 256 MiB whose
-    bytes are known, used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
-    c4 = synth.CONFIGS["c4"]
-    N, K, gs = c4["N"], c4["K"], c4["gs"]
+    """Launches for hardware-counter runs: every call of the step and the fused
+    MLP block, PROBE_REPS times each on rotating weight copies (random codes:
+    the bytes a launch moves do not depend on the values), then PROBE_REPS
+    plain elementwise copies of PROBE_COPY_BYTES whose bytes are known, used
+    to calibrate the FETCH_SIZE / WRITE_SIZE counters.  Prints the dispatch
+    order on stderr."""
     g = torch.Generator(device=dev)
     g.manual_seed(4)
-    sets = []
-    for _ in range(4):
+
+    def triplet(N, K, gs):
         q = torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, device=dev, generator=g)
-        s = torch.rand((N, K // gs), device=dev, generator=g) * 1e-2
+        s_ = torch.rand((N, K // gs), device=dev, generator=g) * 1e-2
         z = torch.randint(0, 16, (N, K // gs), device=dev, generator=g).float()
-        sets.append((q, s, z))
-    a = [torch.randn(K, device=dev, generator=g) for _ in range(3)]
-    y, r, n = (torch.empty(m, device=dev) for m in (N, K, K))
-    for i in range(5):
-        q, s, z = sets[i % 4]
-        q4.int4_matvec_norm(*a, c4["eps"], q, s, z, y=y, residual_out=r, norm_out=n)
-    torch.cuda.synchronize()
-    src = torch.empty(1 << 26, dtype=torch.float32, device=dev).fill_(1.0)
+        return q, s_, z
+
+    def vec(*shape):
+        return torch.randn(*shape, device=dev, generator=g)
+
+    copies = 2
+    for label, kind, N, K, gs, M in PROBE_CALLS:
+        if kind == "gated":
+            sets = [(*triplet(N, K, gs), *triplet(N, K, gs)) for _ in range(copies)]
+            x, h = vec(K), torch.empty(N, device=dev)
+            fn = lambda w: q4.int4_matvec_gated(x, *w, h=h)
+        elif kind == "mlp":
+            sets = [(*triplet(N, K, gs), *triplet(N, K, gs), *triplet(K, N, gs)) for _ in range(copies)]
+            x, h, y = vec(K), torch.empty(N, device=dev), torch.empty(K, device=dev)
+            ws = torch.zeros(q4.int4_mlp_workspace_bytes() // 4, dtype=torch.int32, device=dev)
+            fn = lambda w: q4.int4_mlp(x, *w, h=h, y=y, workspace=ws)
+        elif kind == "norm":
+            sets = [triplet(N, K, gs) for _ in range(copies)]
+            a = [vec(K) for _ in range(3)]
+            y, r, n = (torch.empty(m, device=dev) for m in (N, K, K))
+            fn = lambda w: q4.int4_matvec_norm(*a, 1e-6, *w, y=y, residual_out=r, norm_out=n)
+        elif kind == "split4":
+            sets = [triplet(N, K, gs) for _ in range(copies)]
+            x = vec(K)
+            outs = tuple(torch.empty(m, device=dev) for m in (4096, 1024, 1024, 512))
+            fn = lambda w: q4.int4_matvec_split4(x, *w, 4096, 5120, 6144, outs=outs)
+        else:
+            sets = [triplet(N, K, gs) for _ in range(copies)]
+            X, Y = vec(M, K), torch.empty((M, N), device=dev)
+            fn = lambda w: q4.int4_matvec(X, *w, Y=Y)
+        for i in range(PROBE_REPS):
+            fn(sets[i % copies])
+        torch.cuda.synchronize()
+        log(f"counter probe: {PROBE_REPS} x {label}")
+        del sets
+        torch.cuda.empty_cache()
+    src = torch.empty(PROBE_COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(5):
-        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes 256 MiB
+    for _ in range(PROBE_REPS):
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes PROBE_COPY_BYTES
     torch.cuda.synchronize()
-    log(f"counter probe: 5 norm launches {N}x{K} gs {gs}, 5 copies of {src.numel() * 4} bytes")
+    log(f"counter probe: {PROBE_REPS} x elementwise copy of {PROBE_COPY_BYTES} bytes")
 
 
 def main():
@@ -648,8 +695,8 @@ def main():
                     help="skip the 1/8-share calls (the JSON then carries one_gpu_share_of_8 null); "
                          "a kernel trace then holds only the full-size launches of each kernel")
     ap.add_argument("--counter-probe", action="store_true",
-                    help="only launch the LM-head norm call and a plain 256 MiB device copy, "
-                         "5 times each, for rocprofv3 --pmc runs (prints no JSON)")
+                    help="only launch every call of the step and the fused MLP block, then a plain "
+                         "256 MiB device copy, 5 times each, for rocprofv3 --pmc runs (prints no JSON)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the int4 matvec path here has no multi-GPU "

@@ -173,8 +173,9 @@ int cached_occupancy(Mode mode, const GemvArgs& a, const LaunchShape& s, int* bp
 //
 // Register kernel (M = 1, K <= 16384): nch = ceil(K/2048) chunks of cw units,
 // P = 8/nch rows of nch waves per block (about 8 waves: two per SIMD, which
-// streams best), columns split evenly over the B*P rows, one LDS partial per
-// (column, stream, lane, chunk), the activations staged once per block.
+// streams best), the columns split evenly over the blocks (the P waves of a
+// chunk share the block's columns), one LDS partial per (column, stream,
+// lane, chunk), the activations staged once per block.
 //
 // Matrix-core kernel (plain, M >= 2): blocks of W <= 8 waves, each wave one
 // slice of 16, 20 or 24 units of K per pass, 8 / W blocks per CU, the

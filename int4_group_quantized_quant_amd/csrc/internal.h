@@ -65,9 +65,10 @@ struct GemvArgs {
 };
 
 // Float offset of the staged activations in the register kernel's LDS: after
-// the partial table and one float per wave (at most 16 waves), rounded up to
-// a float4.  The register kernel's LDS holds x_lds_offset + M*K floats.
-__host__ __device__ inline int x_lds_offset(int part_floats) { return (part_floats + 16 + 3) & ~3; }
+// the partial table, one float per wave (at most 16 waves) and one column
+// group counter per chunk (at most 8), rounded up to a float4.  The
+// register kernel's LDS holds x_lds_offset + M*K floats.
+__host__ __device__ inline int x_lds_offset(int part_floats) { return (part_floats + 24 + 3) & ~3; }
 
 enum Variant : int {
   kVariantLds = 0,   // activations staged in LDS, one wave per column group

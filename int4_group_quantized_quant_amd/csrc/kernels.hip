@@ -127,29 +127,32 @@ struct Step {
   float z[NSLOT];
 };
 
-// The zero point of a group as an fp16 subnormal pair (zero * 2^-24 in both
-// halves).  Zero points are integers in [0, 15], so the conversion is exact.
-__device__ __forceinline__ uint32_t zero_pair(float zero) { return (uint32_t)zero * 0x00010001u; }
+// The zero point of a group as the fp16 subnormal pair (zero * 2^-24,
+// 16 * zero * 2^-24).  Zero points are integers in [0, 15], so the
+// conversion is exact.
+__device__ __forceinline__ uint32_t zero_pair(float zero) { return (uint32_t)zero * 0x00100001u; }
 
 // The dequantized codes (code - zero) of the 32 inputs of one unit as 16
-// fp16 pairs, scaled by 2^-24 (even inputs) or 2^-20 (odd inputs): each
-// nibble is masked in place into the mantissa of a subnormal half (code *
-// 2^-24, or code * 2^-20 four bits up) and the zero point, shifted the same
-// way, is subtracted with one packed fp16 subtraction per pair.  Every
-// value is an integer multiple of 2^-24 below 2^-14 in magnitude, so all of
-// it is exact, as the definition (code - zero) * scale asks.  Pair 4i+t
-// holds inputs 8i+t and 8i+t+4.
+// fp16 pairs.  A nibble masked in place into an fp16 half is the exact
+// subnormal code * 2^-24 (bits 0-3 of the half) or 16 * code * 2^-24 (bits
+// 4-7).  Word i gives the pairs (c0, 16 c5), (16 c1, c4), (c2, 16 c7) and
+// (16 c3, c6) of its inputs 8i..8i+7, so one zero pair (z, 16 z) and its
+// half swap (taken for free by the packed subtraction) serve all four; one
+// packed fp16 subtraction per pair is exact (integers times 2^-24 below
+// 2^-14), as the definition (code - zero) * scale asks.  Even inputs come
+// out scaled by 2^-24 and odd ones by 2^-20.
 __device__ __forceinline__ void unit_codes(u32x4 w, uint32_t zh, half2_t (&d)[16]) {
-  const half2_t z0 = as_half2(zh), z1 = as_half2(zh << 4);
+  const half2_t za = as_half2(zh);
+  const half2_t zb = __builtin_shufflevector(za, za, 1, 0);
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t lo = words[i];
     const uint32_t hi = words[i] >> 8;
-    d[4 * i + 0] = as_half2(lo & 0x000F000Fu) - z0;
-    d[4 * i + 1] = as_half2(lo & 0x00F000F0u) - z1;
-    d[4 * i + 2] = as_half2(hi & 0x000F000Fu) - z0;
-    d[4 * i + 3] = as_half2(hi & 0x00F000F0u) - z1;
+    d[4 * i + 0] = as_half2(lo & 0x00F0000Fu) - za;
+    d[4 * i + 1] = as_half2(lo & 0x000F00F0u) - zb;
+    d[4 * i + 2] = as_half2(hi & 0x00F0000Fu) - za;
+    d[4 * i + 3] = as_half2(hi & 0x000F00F0u) - zb;
   }
 }
 
@@ -165,10 +168,10 @@ __device__ __forceinline__ float unit_dot(const float (&x)[32], const half2_t (&
     t = fmaf(x[8 * i + 1], (float)d[4 * i + 1].x, t);
     t = fmaf(x[8 * i + 2], (float)d[4 * i + 2].x, t);
     t = fmaf(x[8 * i + 3], (float)d[4 * i + 3].x, t);
-    t = fmaf(x[8 * i + 4], (float)d[4 * i + 0].y, t);
-    t = fmaf(x[8 * i + 5], (float)d[4 * i + 1].y, t);
-    t = fmaf(x[8 * i + 6], (float)d[4 * i + 2].y, t);
-    t = fmaf(x[8 * i + 7], (float)d[4 * i + 3].y, t);
+    t = fmaf(x[8 * i + 4], (float)d[4 * i + 1].y, t);
+    t = fmaf(x[8 * i + 5], (float)d[4 * i + 0].y, t);
+    t = fmaf(x[8 * i + 6], (float)d[4 * i + 3].y, t);
+    t = fmaf(x[8 * i + 7], (float)d[4 * i + 2].y, t);
   }
   return t;
 }
@@ -354,21 +357,36 @@ struct InputsReady {
 };
 
 // One pass of the register kernel over its columns.  `part` is the block's
-// LDS: [cols of the block][NSTREAM][M][nch] partials, one float per wave,
-// then the staged activations (x_lds_offset).  The block may hold more waves
-// than the pass's P rows of nch waves; the extra waves own no columns.
-// `inputs_ready` is called by every thread before the activations are read:
-// with InputsReady the staging goes first; otherwise the first step of
-// weight loads is issued before the call, so that they stream while it
-// waits, and the activations (written by other blocks of the launch) are
-// read at device scope.  kPublish stores the outputs at device scope.
-template <int M, int NCOL, int MODE, bool kPublish, bool kLongRows, class Ready>
+// LDS: [cols of the block][NSTREAM][M][nch] partials, 16 floats of per-wave
+// sums, 8 column-group counters (one per chunk), then the staged
+// activations (x_lds_offset).  The block may hold more waves than the pass's
+// P rows of nch waves; the extra waves own no columns.
+//
+// Activations: the block loads its rows coalesced into registers, issues
+// the first step of weight loads behind them, then writes the rows to LDS
+// (for the norm, x = (a_a + a_b) * w_norm and block 0 writes residual_out;
+// for a gated input, the gated vector); after one barrier each lane keeps
+// its unit's 32 inputs in registers for the sweep.  `inputs_ready` is called
+// by every thread before the activations are loaded: with InputsReady they
+// are a kernel input; otherwise the first step of weight loads is issued
+// before the call, so that they stream while it waits, and the activations
+// (written by other blocks of the launch) are read at device scope.
+//
+// Columns: the block owns [blk_begin, blk_end), in groups of NCOL.  The P
+// waves of chunk c share that chunk's column groups: wave p starts with
+// group p and then claims the next free group from the chunk's LDS counter,
+// two groups ahead, so the waves of a chunk finish together whatever order
+// the SIMDs run them in.  A (column, chunk) partial does not depend on which
+// wave computes it, so the results do not depend on the claiming order.
+// kPublish stores the outputs at device scope.
+template <int M, int NCOL, int MODE, bool kPublish, class Ready>
 __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready inputs_ready) {
   constexpr int NSTREAM = mode_streams(MODE);
   constexpr int NSLOT = NCOL * NSTREAM;
   constexpr int V = M * NSLOT;
   constexpr int NZ = (V + 3) / 4;
   constexpr bool kWaits = !__is_same(Ready, InputsReady);
+  static_assert(M == 1, "the register kernel runs one lane");
 
   const int bd = a.block_threads;  // threads per block, from the arguments
   const int lane = threadIdx.x & (kWave - 1);
@@ -380,113 +398,129 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   const int64_t R = (int64_t)gridDim.x * P;
   const int64_t blk_begin = uniform_i64((int64_t)blockIdx.x * P * a.N / R);
   const int64_t blk_end = uniform_i64(((int64_t)blockIdx.x * P + P) * a.N / R);
-  const int64_t row = (int64_t)blockIdx.x * P + (p < P ? p : 0);
-  const int64_t c_begin = uniform_i64(row * a.N / R);
-  const int64_t c_end = p < P ? uniform_i64((row + 1) * a.N / R) : c_begin;
+  const int ncols = (int)(blk_end - blk_begin);
+  const int ngroups = (ncols + NCOL - 1) / NCOL;
   const int u = c * a.cw + lane;
   const bool active = lane < a.cw && u < a.U;
   const uint32_t qoff = (uint32_t)(active ? u : 0) * 16u;
   const uint32_t soff = (uint32_t)(active ? unit_group(a, u) : 0) * 4u;
   float* scratch = part + a.part_floats;
-
-  // Activations: the block stages the M rows once in LDS (coalesced; for
-  // the norm, x = (a_a + a_b) * w_norm and block 0 writes residual_out; for
-  // a gated input, the gated vector), then each lane keeps its unit's 32
-  // inputs in registers for the sweep.
+  uint32_t* claims = reinterpret_cast<uint32_t*>(scratch + 16);
   float4* xl = reinterpret_cast<float4*>(part + x_lds_offset(a.part_floats));
   const int n4 = a.K >> 2;
-  // Ring of DEPTH + 1 register sets: the loads of step i + DEPTH are issued
-  // before step i is computed.  With inputs at hand, the first weight loads
-  // go out after the activation loads: after the whole staging for short
-  // rows (the memory counter is in order, so the staging would otherwise
-  // wait for them), between the loads and the LDS writes for long ones
-  // (kLongRows); with inputs still being produced, they go out first and
-  // overlap the wait.  Every load is unconditional: steps past the wave's last column
-  // re-read that column, and a wave without columns has an empty buffer
-  // range, whose loads return 0 without touching memory.
-  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, c_begin, c_end);
-  const uint32_t last = c_end > c_begin ? (uint32_t)(c_end - c_begin - 1) : 0u;
+
+  // The block's weight streams (scalar buffer resources from its first
+  // column, so every offset is 32-bit).  Every load is unconditional: a
+  // group past the block's last column re-reads that column (its result is
+  // never stored), and a block without columns has an empty range, whose
+  // loads return 0 without touching memory.
+  const StreamBufs bufs = make_stream_bufs<NSTREAM>(a, blk_begin, blk_end);
+  const uint32_t last = ncols > 0 ? (uint32_t)(ncols - 1) : 0u;
   // One step of loads in flight ahead of the arithmetic: two or three
   // measured slower on every call shape (more requests outstanding per CU
   // only add contention for the memory pipeline).
-  constexpr int DEPTH = 1;
   Step<NSLOT> s0, s1;
+  const int g_first = p < P ? p : ngroups;  // waves past the P rows own nothing
+  if (threadIdx.x < (unsigned)nch) claims[threadIdx.x] = (uint32_t)P;
+
+  // Activation float4 i = threadIdx.x + j * bd of a row, for j < nper (at
+  // most 8: the planner keeps K <= 16384 and blocks of at least 64 * nch
+  // threads).
+  const int nper = (n4 + bd - 1) / bd;
+  auto row_rsrc = [&](const float* src) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, a.K * 4, kBufferWord3);
+  };
+  auto ld4 = [&](__amdgpu_buffer_rsrc_t r, int j) {
+    return __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(threadIdx.x + j * bd) * 16u, 0, 0));
+  };
+  auto put_lds = [&](int j, float4 v) {
+    const int i = (int)threadIdx.x + j * bd;
+    if (i < n4) xl[(i & 7) * a.U + (i >> 3)] = v;
+  };
+  constexpr int kStageMax = 8;
   if constexpr (kWaits) {
-    load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(g_first * NCOL), last, qoff, soff, s0);
     inputs_ready();
-  }
-  if constexpr (kLongRows) {
-    // A plain row of more than 4 float4s per thread (K > 8192 for a full
-    // block): each thread's float4s are loaded into registers, then the
-    // first weight loads are issued behind them, so waiting for the
-    // activations leaves the weights in flight.  A thread holds at most 8
-    // (K <= 2048 nch and the block has at least 64 nch threads); loads past
-    // the row return 0 without touching memory, and all 8 are issued so
-    // that the wait counts stay exact.  Shorter rows measured faster with
-    // the weights issued after the staging.
-    static_assert(M == 1 && MODE == kPlain && !kWaits, "long rows: one plain row with inputs at hand");
-    constexpr int kStageMax = 8;
-    const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, n4 * 16, kBufferWord3);
-    float4 v[kStageMax];
-#pragma unroll
-    for (int j = 0; j < kStageMax; ++j)
-      v[j] = __builtin_bit_cast(
-          float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(threadIdx.x + j * bd) * 16u, 0, 0));
-    __builtin_amdgcn_sched_barrier(0);
-    load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-      const int i = (int)threadIdx.x + j * bd;
-      if (i < n4) xl[(i & 7) * a.U + (i >> 3)] = v[j];
-    }
-  } else if constexpr (mode_has_norm(MODE)) {
-    // Per-thread share of sum_k r_k^2, then the wave's total in its slot.
-    float ssq = 0.0f;
-    for (int i = threadIdx.x; i < n4; i += bd) {
-      float4 r, v;
-      norm_in4(a, i, r, v);
-      ssq = fmaf(r.x, r.x, ssq);
-      ssq = fmaf(r.y, r.y, ssq);
-      ssq = fmaf(r.z, r.z, ssq);
-      ssq = fmaf(r.w, r.w, ssq);
-      if (blockIdx.x == 0 && a.residual_out) reinterpret_cast<float4*>(a.residual_out)[i] = r;
-      xl[(i & 7) * a.U + (i >> 3)] = v;
-    }
-    const float wsum = wave_sum(ssq);
-    if (lane == 0) scratch[wave] = wsum;
-  } else if constexpr (mode_gates_input(MODE)) {
-    for (int i = threadIdx.x; i < n4; i += bd) xl[(i & 7) * a.U + (i >> 3)] = gated_in4<MODE>(a, i);
-  } else if constexpr (kWaits) {
-    static_assert(M == 1, "a waiting pass reads one activation row");
-    const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, n4 * 16, kBufferWord3);
+    const auto rx = row_rsrc(a.x);
     for (int i = threadIdx.x; i < n4; i += bd)
       xl[(i & 7) * a.U + (i >> 3)] = __builtin_bit_cast(
           float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)i * 16u, 0, kLoadDeviceCoherent));
+  } else if constexpr (mode_has_norm(MODE)) {
+    const auto ra = row_rsrc(a.x), rb = row_rsrc(a.x2), rg = row_rsrc(a.w_norm);
+    float4 va[kStageMax], vb[kStageMax], vg[kStageMax];
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j)
+      if (j < nper) {
+        va[j] = ld4(ra, j);
+        vb[j] = ld4(rb, j);
+        vg[j] = ld4(rg, j);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(g_first * NCOL), last, qoff, soff, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Per-thread share of sum_k r_k^2 (its float4s in order), then the
+    // wave's total in its slot.
+    float ssq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j)
+      if (j < nper) {
+        const int i = (int)threadIdx.x + j * bd;
+        if (i < n4) {
+          const float4 r = make_float4(va[j].x + vb[j].x, va[j].y + vb[j].y, va[j].z + vb[j].z, va[j].w + vb[j].w);
+          ssq = fmaf(r.x, r.x, ssq);
+          ssq = fmaf(r.y, r.y, ssq);
+          ssq = fmaf(r.z, r.z, ssq);
+          ssq = fmaf(r.w, r.w, ssq);
+          if (blockIdx.x == 0 && a.residual_out) reinterpret_cast<float4*>(a.residual_out)[i] = r;
+          xl[(i & 7) * a.U + (i >> 3)] =
+              make_float4(r.x * vg[j].x, r.y * vg[j].y, r.z * vg[j].z, r.w * vg[j].w);
+        }
+      }
+    const float wsum = wave_sum(ssq);
+    if (lane == 0) scratch[wave] = wsum;
+  } else if constexpr (mode_gates_input(MODE)) {
+    const auto rp = row_rsrc(a.x), rr = row_rsrc(a.x2);
+    float4 vp[kStageMax], vr[kStageMax];
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j)
+      if (j < nper) {
+        vp[j] = ld4(rp, j);
+        vr[j] = ld4(rr, j);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(g_first * NCOL), last, qoff, soff, s0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j)
+      if (j < nper) put_lds(j, gate4<MODE>(vp[j], vr[j]));
   } else {
+    const auto rx = row_rsrc(a.x);
+    float4 v[kStageMax];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.K);
-      for (int i = threadIdx.x; i < n4; i += bd) xl[(m * 8 + (i & 7)) * a.U + (i >> 3)] = src[i];
-    }
+    for (int j = 0; j < kStageMax; ++j)
+      if (j < nper) v[j] = ld4(rx, j);
+    __builtin_amdgcn_sched_barrier(0);
+    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(g_first * NCOL), last, qoff, soff, s0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j)
+      if (j < nper) put_lds(j, v[j]);
   }
-  if constexpr (!kWaits && !kLongRows) load_units<NCOL, NSTREAM>(a, bufs, 0u, last, qoff, soff, s0);
   __syncthreads();
-  float x[M][32];
+  float x[32];
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) put4(x[m], j, active ? xl[(m * 8 + j) * a.U + u] : make_float4(0.f, 0.f, 0.f, 0.f));
+  for (int j = 0; j < 8; ++j) put4(x, j, active ? xl[j * a.U + u] : make_float4(0.f, 0.f, 0.f, 0.f));
 
   const bool writer = V >= 4 ? (lane & 15) == 0 : (V == 2 ? (lane & 31) == 0 : lane == 0);
-  auto step = [&](int64_t n, const Step<NSLOT>& r) {
+  // Compute the group starting at block column n0 from the loaded step r.
+  auto step = [&](int n0, const Step<NSLOT>& r) {
     float vals[V];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
       half2_t d[16];
       unit_codes(r.q[sl], zero_pair(r.z[sl]), d);
-#pragma unroll
-      for (int m = 0; m < M; ++m) vals[m * NSLOT + sl] = r.s[sl] * unit_dot(x[m], d);
+      vals[sl] = r.s[sl] * unit_dot(x, d);
     }
     float z[NZ];
     wave_reduce<V>(vals, z);
@@ -495,31 +529,51 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
 #pragma unroll
       for (int j = 0; j < NZ; ++j) {
         const int vi = reduced_index<V>(j, rrow);
-        const int m = vi / NSLOT;
-        const int sl = vi - m * NSLOT;
-        const int64_t col = n + sl / NSTREAM;
-        if (col < c_end)
-          part[(((col - blk_begin) * NSTREAM + sl % NSTREAM) * M + m) * nch + c] = z[j];
+        const int col = n0 + vi / NSTREAM;
+        if (col < ncols) part[((col * NSTREAM + vi % NSTREAM) * M) * nch + c] = z[j];
       }
     }
   };
-
-  // One pipeline stage: issue the loads DEPTH steps ahead into `far` (past
-  // the last column they re-read it), then compute `cur` (columns n..).  No
-  // load sits behind a branch, so the compiler's wait counts stay exact and
-  // every step, the last ones included, overlaps the next loads.
-  auto stage = [&](int64_t n, const Step<NSLOT>& cur, Step<NSLOT>& far) {
-    load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(n - c_begin) + DEPTH * NCOL, last, qoff, soff, far);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
-    step(n, cur);
+  // The next free group of this wave's chunk, claimed by lane 0 from the
+  // chunk's LDS counter with one increment (ds_inc_rtn, which the compiler
+  // keeps as a single-lane atomic).  It is read out (wave-uniform) only
+  // where the next loads need it, one step later, so the atomic's latency
+  // hides behind that step.
+  auto claim = [&]() -> uint32_t {
+    uint32_t g = 0;
+    if (lane == 0) g = __builtin_amdgcn_atomic_inc32(claims + c, 0xFFFFFFFFu, __ATOMIC_RELAXED, "workgroup");
+    return g;
   };
-  if (c_begin < c_end) {
-    int64_t n = c_begin;
+  // The empty asm takes the claimed value as an operand at this point, after
+  // the step's stores, so the compiler cannot move the read-out (and its wait
+  // for the atomic) up into the step.
+  auto group = [](uint32_t claimed) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(claimed));
+    return (int)__builtin_amdgcn_readfirstlane(claimed);
+  };
+
+  // Pipeline: s0 holds the loads of group g; the loads of the next group are
+  // issued before g is computed, and the group after it is claimed
+  // meanwhile.
+  if (g_first < ngroups) {
+    int g = g_first;
+    uint32_t next = claim();
     while (true) {
-      stage(n, s0, s1);
-      if ((n += NCOL) >= c_end) break;
-      stage(n, s1, s0);
-      if ((n += NCOL) >= c_end) break;
+      const int g1 = group(next);
+      load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(g1 * NCOL), last, qoff, soff, s1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the arithmetic
+      next = claim();
+      step(g * NCOL, s0);
+      if (g1 >= ngroups) break;
+      g = g1;
+      const int g2 = group(next);
+      load_units<NCOL, NSTREAM>(a, bufs, (uint32_t)(g2 * NCOL), last, qoff, soff, s0);
+      __builtin_amdgcn_sched_barrier(0);
+      next = claim();
+      step(g * NCOL, s1);
+      if (g2 >= ngroups) break;
+      g = g2;
     }
   }
   __syncthreads();
@@ -541,26 +595,23 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   }
 
   // Each column's chunk partials, summed in chunk order.
-  const int64_t ncols = blk_end - blk_begin;
-  for (int64_t j = threadIdx.x; j < ncols; j += bd) {
+  for (int j = threadIdx.x; j < ncols; j += bd) {
     float tot[NSTREAM][M];
 #pragma unroll
-    for (int st = 0; st < NSTREAM; ++st)
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float* pp = part + ((j * NSTREAM + st) * M + m) * nch;
-        float s = pp[0];
-        for (int cc = 1; cc < nch; ++cc) s += pp[cc];
-        tot[st][m] = s;
-      }
+    for (int st = 0; st < NSTREAM; ++st) {
+      const float* pp = part + (j * NSTREAM + st) * M * nch;
+      float sum = pp[0];
+      for (int cc = 1; cc < nch; ++cc) sum += pp[cc];
+      tot[st][0] = sum;
+    }
     store_column<M, MODE, kPublish>(a, blk_begin + j, tot, inv);
   }
 }
 
-template <int M, int NCOL, int MODE, bool kLongRows>
+template <int M, int NCOL, int MODE>
 __global__ __launch_bounds__(512) void gemv_reg_kernel(GemvArgs a) {
   extern __shared__ float part[];
-  reg_pass<M, NCOL, MODE, false, kLongRows>(a, part, InputsReady{});
+  reg_pass<M, NCOL, MODE, false>(a, part, InputsReady{});
 }
 
 // ------------------------------------------------------------ fused MLP
@@ -626,12 +677,12 @@ __global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs
   // Wave 0 publishes and polls; it alone needs the epoch.
   uint32_t epoch = 0;
   if (threadIdx.x < 64) epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  reg_pass<1, NCOL1, kGated, true, false>(gate_up, part, InputsReady{});
+  reg_pass<1, NCOL1, kGated, true>(gate_up, part, InputsReady{});
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores of h have completed
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_store(ws + kMlpFlags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  reg_pass<1, NCOL2, kPlain, false, false>(down, part, GridWait{ws, epoch});
+  reg_pass<1, NCOL2, kPlain, false>(down, part, GridWait{ws, epoch});
   if (blockIdx.x == 0 && threadIdx.x == 0)
     __hip_atomic_store(ws, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1003,19 +1054,11 @@ __global__ __launch_bounds__(kSmallBlock) void quantize_pack_kernel(const float*
 
 template <int MODE, int M, int NCOL>
 hipError_t launch_reg(const GemvArgs& a, const LaunchShape& s, hipStream_t stream, int* occupancy) {
-  static std::atomic<bool> raised1{false};
+  static std::atomic<bool> raised{false};
   if (s.depth != 1) return hipErrorInvalidValue;  // one step ahead is the only form built
-  if constexpr (MODE == kPlain) {
-    // More than 4 float4s of the row per thread: the long-row staging, which
-    // holds at most 8.
-    const int64_t per_thread = ((int64_t)(a.K / 4) + s.block_threads - 1) / s.block_threads;
-    if (per_thread > 8) return hipErrorInvalidValue;
-    if (per_thread > 4) {
-      static std::atomic<bool> raised2{false};
-      return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, true>, raised2, a, s, stream, occupancy);
-    }
-  }
-  return launch_or_query(gemv_reg_kernel<M, NCOL, MODE, false>, raised1, a, s, stream, occupancy);
+  // The staging holds at most 8 float4s of a row per thread.
+  if ((a.K / 4 + s.block_threads - 1) / s.block_threads > 8) return hipErrorInvalidValue;
+  return launch_or_query(gemv_reg_kernel<M, NCOL, MODE>, raised, a, s, stream, occupancy);
 }
 
 template <int NCOL1, int NCOL2>
