@@ -162,15 +162,19 @@ int int4_matvec_gated_lanes(const float* X, int32_t M,
  *
  * workspace: at least int4_mlp_workspace_bytes() bytes of device memory,
  * 16-byte aligned, owned by the caller, all ZERO before its first use and
- * then left as the calls leave it: it holds a call counter and one flag per
- * block, through which the down projection waits until every part of h is
- * written.  Calls that share a workspace must not overlap in time.  The
- * wait assumes the launch's blocks are all resident at once (the grid is
- * one block per compute unit); a block that waits about a second gives up
- * and sets word 1 of the workspace to 1, and the outputs are then
- * undefined.  Shapes the fused launch does not cover (very small F or D, or
- * K beyond the one-lane register kernel) run as the two separate calls,
- * with the same results, and leave the workspace untouched.
+ * then left as the calls leave it: word 0 counts the completed fused calls,
+ * word 1 is the timeout flag, and one flag per block follows, through which
+ * the down projection waits until every part of h is written.  Calls that
+ * share a workspace must not overlap in time.  The wait assumes the
+ * launch's blocks are all resident at once (the grid is one block per
+ * compute unit, and nothing else may occupy the device meanwhile); a block
+ * that waits about a second gives up and sets word 1.  The outputs of that
+ * call are then undefined, and every later fused call with that workspace
+ * writes NaN to all of h and y and does nothing else, until the caller
+ * zeroes the workspace again; int4_mlp_timed_out reads word 1.  Shapes the
+ * fused launch does not cover (very small F or D, or K beyond the one-lane
+ * register kernel) run as the two separate calls, with the same results,
+ * and neither read nor write the workspace.
  */
 size_t int4_mlp_workspace_bytes(void);
 int int4_mlp(const float* x,
@@ -179,6 +183,15 @@ int int4_mlp(const float* x,
              const uint32_t* q_down, const float* s_down, const float* z_down,
              int64_t D, int64_t F, int32_t group_size, float* h, float* y,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Whether a fused int4_mlp wait on `workspace` has timed out (word 1 of the
+ * workspace is set): *timed_out = 1 if so, else 0.  Waits for `stream`
+ * (every call enqueued on it before this one) to finish, then reads the
+ * word; allocates nothing.  After a timeout, zero the workspace before
+ * using it again.
+ */
+int int4_mlp_timed_out(const void* workspace, int32_t* timed_out, void* stream);
 
 /*
  * Residual-add + RMSNorm prefixed matvec ([P4] WGSL_NORM_MATVEC_INT4,

@@ -24,6 +24,7 @@ __all__ = [
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
     "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
     "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "int4_mlp", "int4_mlp_workspace_bytes",
+    "int4_mlp_timed_out",
     "int4_gemm_noalloc", "INT4_GEMM_NOALLOC_SCRATCH_BYTES", "int4_probe_stream_read", "lib", "LIB_PATH",
 ]
 
@@ -69,6 +70,8 @@ lib.int4_mlp_workspace_bytes.argtypes = []
 lib.int4_mlp_workspace_bytes.restype = ctypes.c_size_t
 lib.int4_mlp.argtypes = [_vp] * 10 + [_i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.int4_mlp.restype = ctypes.c_int
+lib.int4_mlp_timed_out.argtypes = [_vp, ctypes.POINTER(ctypes.c_int32), _vp]
+lib.int4_mlp_timed_out.restype = ctypes.c_int
 for _fn in (lib.int4_gemm, lib.int4_embedding_gather, lib.int4_quantize_pack, lib.int4_matvec, lib.int4_matvec_split4,
             lib.int4_matvec_gated, lib.int4_matvec_norm, lib.int4_matvec_dual,
             lib.int4_matvec_sigmoid_gated, lib.int4_matvec_swiglu_gated,
@@ -404,6 +407,17 @@ def int4_mlp_workspace_bytes() -> int:
     return int(lib.int4_mlp_workspace_bytes())
 
 
+def int4_mlp_timed_out(workspace: torch.Tensor, stream=None) -> bool:
+    """Whether a fused int4_mlp wait on `workspace` has timed out (its word 1
+    is set).  Waits for the stream's earlier work."""
+    _dev(workspace, "workspace", (torch.int32, torch.uint32, torch.uint8))
+    if workspace.numel() * workspace.element_size() < 8:
+        raise ValueError("workspace must hold at least two 32-bit words")
+    out = ctypes.c_int32(0)
+    _check(lib.int4_mlp_timed_out(_ptr(workspace), ctypes.byref(out), _stream(stream)))
+    return bool(out.value)
+
+
 def int4_mlp(x: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, q_down, s_down, z_down,
              h=None, y=None, workspace=None, stream=None):
     """(h, y): h = silu(x . w_gate^T) * (x . w_up^T) [F], y = h . w_down^T [D], one launch.
@@ -411,7 +425,9 @@ def int4_mlp(x: torch.Tensor, q_gate, s_gate, z_gate, q_up, s_up, z_up, q_down, 
     workspace: an int32 device tensor of at least int4_mlp_workspace_bytes()
     bytes, zeroed before its first use and then kept as the calls leave it
     (calls sharing it must not overlap).  A fresh zeroed one is made when
-    not given.
+    not given.  If a fused call's wait on its blocks times out
+    (int4_mlp_timed_out), its h and y are undefined and every later call
+    with that workspace writes NaN, until the workspace is zeroed again.
     """
     F, D, gs = _pair(q_gate, s_gate, z_gate, q_up, s_up, z_up, "_gate", "_up")
     D2, F2, gs2 = _weights(q_down, s_down, z_down, "_down")

@@ -607,6 +607,19 @@ int int4_matvec_gated(const float* x, const uint32_t* q_gate, const float* s_gat
 
 size_t int4_mlp_workspace_bytes(void) { return kMlpWorkspaceBytes; }
 
+int int4_mlp_timed_out(const void* workspace, int32_t* timed_out, void* stream) {
+  if (!workspace || !timed_out) return fail(INT4_ERR_NULL, "workspace and timed_out are required");
+  RETURN_IF(check_align(workspace, 16, "workspace"));
+  uint32_t word = 0;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&word, static_cast<const uint32_t*>(workspace) + 1, sizeof(word),
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "reading the workspace: %s", hipGetErrorString(e));
+  *timed_out = word != 0u;
+  return ok();
+}
+
 int int4_mlp(const float* x, const uint32_t* q_gate, const float* s_gate, const float* z_gate,
              const uint32_t* q_up, const float* s_up, const float* z_up, const uint32_t* q_down,
              const float* s_down, const float* z_down, int64_t D, int64_t F, int32_t group_size, float* h,

@@ -239,7 +239,9 @@ __device__ __forceinline__ void load_units(const GemvArgs& a, const StreamBufs& 
   for (int c = 0; c < NCOL * NSTREAM; ++c) {
     const int st = c % NSTREAM;
     const uint32_t col0 = rel + (uint32_t)(c / NSTREAM);
-    const uint32_t col = col0 < last ? col0 : last;
+    // Wave-uniform by contract; stated so that the offset is a scalar operand
+    // and never a per-lane loop over the distinct values.
+    const uint32_t col = __builtin_amdgcn_readfirstlane(col0 < last ? col0 : last);
     r.q[c] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.q[st], qoff, col * qbytes, kLoadNonTemporal));
     r.s[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.s[st], soff, col * gbytes, 0));
@@ -669,11 +671,26 @@ struct GridWait {
 // in its flag; its first step of down-projection weights is loaded while it
 // waits for every flag, and the down pass then stages the whole of h.
 // Block 0 advances the stored epoch once it has seen every flag (by then
-// every block has read it).  No read-modify-write: all blocks' atomics on
-// one word would be serialized at the memory.
+// every block has read it), unless a wait has timed out.  No
+// read-modify-write: all blocks' atomics on one word would be serialized at
+// the memory.  Once the timeout flag is set (by this call's or an earlier
+// call's wait), a call only writes NaN to h and y, and leaves the
+// workspace as it is.
 template <int NCOL1, int NCOL2>
 __global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs down, uint32_t* ws) {
   extern __shared__ float part[];
+  __shared__ uint32_t stuck;
+  if (threadIdx.x == 0) stuck = __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (stuck != 0u) {
+    // Block b of B fills its share [b n / B, (b + 1) n / B) of each output.
+    const int64_t B = gridDim.x, b = blockIdx.x;
+    const float nan = __builtin_nanf("");
+    for (int64_t i = b * gate_up.N / B + threadIdx.x; i < (b + 1) * gate_up.N / B; i += blockDim.x)
+      gate_up.out[0][i] = nan;
+    for (int64_t i = b * down.N / B + threadIdx.x; i < (b + 1) * down.N / B; i += blockDim.x) down.out[0][i] = nan;
+    return;
+  }
   // Wave 0 publishes and polls; it alone needs the epoch.
   uint32_t epoch = 0;
   if (threadIdx.x < 64) epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
@@ -683,7 +700,7 @@ __global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs
   if (threadIdx.x == 0)
     __hip_atomic_store(ws + kMlpFlags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   reg_pass<1, NCOL2, kPlain, false>(down, part, GridWait{ws, epoch});
-  if (blockIdx.x == 0 && threadIdx.x == 0)
+  if (blockIdx.x == 0 && threadIdx.x == 0 && __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
     __hip_atomic_store(ws, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

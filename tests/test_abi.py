@@ -305,3 +305,11 @@ def test_mlp_workspace_and_validation(lib):
     assert call(h=qd) == ALIAS               # h over the down codes
     assert call(ws=h + 16) == ALIAS          # workspace inside h
     assert call(y=h + 64) == ALIAS           # y inside h
+
+
+def test_mlp_timed_out_validation(lib):
+    out = ctypes.c_int32(7)
+    assert lib.int4_mlp_timed_out(None, ctypes.byref(out), None) == NULL
+    assert lib.int4_mlp_timed_out(0x100000000, None, None) == NULL
+    assert lib.int4_mlp_timed_out(0x100000004, ctypes.byref(out), None) == ALIGN
+    assert out.value == 7                    # untouched on an error

@@ -176,6 +176,34 @@ def test_mlp_calls_in_a_row_and_graph_replays(q4):
     check_workspace(ws, 3 + 1 + 3)  # eager calls, the warm-up, the replays (capture runs nothing)
 
 
+def test_mlp_timeout_flag_is_reported_and_sticky(q4):
+    """The timeout flag, set here from the host (no wait is made to time
+    out): the call writes NaN to all of h and y and leaves the call count,
+    int4_mlp_timed_out reports the flag, and a zeroed workspace works again."""
+    import torch
+    D, F, gs = 1024, 2944, 128
+    wg_d = weights_dev(quantized(0x7170, F, D, gs))
+    wu_d = weights_dev(quantized(0x7171, F, D, gs))
+    wd_d = weights_dev(quantized(0x7172, D, F, gs))
+    xd, = to_dev(synth.normal_f32(0x7173, D))
+    ws = workspace(q4)
+    h, y = mlp(q4, xd, wg_d, wu_d, wd_d, ws, D, F)
+    check_separate(q4, xd, wg_d, wu_d, wd_d, h, y)
+    assert not q4.int4_mlp_timed_out(ws)
+    ws[1] = 1
+    h = torch.zeros(F, device="cuda")
+    y = torch.zeros(D, device="cuda")
+    q4.int4_mlp(xd, *wg_d, *wu_d, *wd_d, h=h, y=y, workspace=ws)
+    assert np.isnan(host(h)).all() and np.isnan(host(y)).all()
+    assert q4.int4_mlp_timed_out(ws)
+    assert host(ws).view(np.uint32)[0] == 1
+    ws.zero_()
+    h, y = mlp(q4, xd, wg_d, wu_d, wd_d, ws, D, F)
+    check_separate(q4, xd, wg_d, wu_d, wd_d, h, y)
+    assert not q4.int4_mlp_timed_out(ws)
+    check_workspace(ws, 1)
+
+
 def test_mlp_default_workspace_and_shape_errors(q4):
     import torch
     D, F, gs = 256, 512, 32
