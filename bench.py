@@ -684,6 +684,93 @@ def counter_probe(q4, torch, dev):
     log(f"counter probe: {PROBE_REPS} x elementwise copy of {PROBE_COPY_BYTES} bytes")
 
 
+# Shapes of the fixed-cost sweep: (label, kind, K, gs, column counts).  The
+# split4 rows keep the 6656-column call's routing proportions.
+FIXED_COST_SWEEPS = (
+    ("one-lane matvec K=5120 gs64 (the lanes M=1 kernel)", "plain", 5120, 64,
+     (256, 1024, 2048, 4096, 8192, 12800, 19200, 25600)),
+    ("split4 K=4096 gs128", "split4", 4096, 128, (256, 832, 1664, 3328, 4992, 6656)),
+)
+FIXED_COST_K = (1024, 2048, 4096, 8192, 16384)  # one-lane K sweep at 256 columns, gs 128
+
+
+def fit_line(xs, ys):
+    """Least-squares y = a + b x."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    return my - b * mx, b
+
+
+def fixed_cost(q4, torch, dev, cus):
+    """Splits a call's time into a part that does not grow with the bytes it
+    streams and a part that does: each sweep times the call at several column
+    counts (rotating copies, as the per-call rows) and the streaming-read probe
+    at the same byte counts, and fits t = a + b * bytes to both.  The probe's
+    intercept is the fixed cost of any launch that reads memory (dispatch,
+    first round trip to HBM, drain); the call's intercept minus the probe's is
+    what the call adds once per launch (activation staging, the partial-sum
+    epilogue).  A K sweep at 256 columns shows how the staging grows with K."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def triplet(N, K, gs):
+        q = torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, device=dev, generator=g)
+        s_ = torch.rand((N, K // gs), device=dev, generator=g) * 1e-2
+        z = torch.randint(0, 16, (N, K // gs), device=dev, generator=g).float()
+        return q, s_, z
+
+    def call_for(kind, N, K, gs):
+        w = triplet(N, K, gs)
+        x = torch.randn(K, device=dev, generator=g)
+        nbytes = alg_bytes(N, K, gs, K, N)
+        sets = lambda r: [w] + [tuple(t.clone() for t in w) for _ in range(r - 1)]
+        wb = sum(t.numel() * 4 for t in w)
+        if kind == "split4":
+            n0, n1, n2 = (N * 4096) // 6656, (N * 5120) // 6656, (N * 6144) // 6656
+            outs = tuple(torch.empty(m, device=dev) for m in (n0, n1 - n0, n2 - n1, N - n2))
+            return Call(f"split4 {N}x{K}", nbytes, lambda s: q4.int4_matvec_split4(x, *s, n0, n1, n2, outs=outs),
+                        sets, wb)
+        y = torch.empty(N, device=dev)
+        return Call(f"matvec {N}x{K}", nbytes, lambda s: q4.int4_matvec(x, *s, Y=y), sets, wb)
+
+    out = {"method": "t = a + b * bytes fitted to the call and to the streaming-read probe at the "
+                     "same byte counts; a_call - a_probe is what the call adds once per launch",
+           "sweeps": {}, "k_sweep": {}}
+    for label, kind, K, gs, Ns in FIXED_COST_SWEEPS:
+        rows = []
+        for N in Ns:
+            c = call_for(kind, N, K, gs)
+            us, _ = time_call(torch, c)
+            rows.append((N, c.nbytes, us))
+            log(f"fixed-cost sweep {label}: N={N} {us:.2f} us")
+            del c
+            torch.cuda.empty_cache()
+        probe = stream_read_ceiling(q4, torch, dev, [b for _, b, _ in rows], cus)
+        xs = [b for _, b, _ in rows]
+        a_k, b_k = fit_line(xs, [us for _, _, us in rows])
+        a_p, b_p = fit_line(xs, [probe[b]["us"] for b in xs])
+        out["sweeps"][label] = {
+            "rows": [{"N": N, "alg_bytes": b, "us": round(us, 3), "probe_us": probe[b]["us"]}
+                     for N, b, us in rows],
+            "call_intercept_us": round(a_k, 3), "call_slope_GBps": round(1e-3 / b_k, 1),
+            "probe_intercept_us": round(a_p, 3), "probe_slope_GBps": round(1e-3 / b_p, 1),
+            "call_adds_per_launch_us": round(a_k - a_p, 3)}
+        log(f"fixed-cost {label}: call {a_k:.2f} us + bytes at {1e-3 / b_k:.0f} GB/s; probe {a_p:.2f} us "
+            f"+ bytes at {1e-3 / b_p:.0f} GB/s")
+    for K in FIXED_COST_K:
+        c = call_for("plain", 256, K, 128)
+        us, _ = time_call(torch, c)
+        out["k_sweep"][str(K)] = {"N": 256, "alg_bytes": c.nbytes, "us": round(us, 3)}
+        log(f"fixed-cost K sweep: 256x{K} {us:.2f} us")
+        del c
+        torch.cuda.empty_cache()
+    probe = stream_read_ceiling(q4, torch, dev, [v["alg_bytes"] for v in out["k_sweep"].values()], cus)
+    for v in out["k_sweep"].values():
+        v["probe_us"] = probe[v["alg_bytes"]]["us"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -697,6 +784,9 @@ def main():
     ap.add_argument("--counter-probe", action="store_true",
                     help="only launch every call of the step and the fused MLP block, then a plain "
                          "256 MiB device copy, 5 times each, for rocprofv3 --pmc runs (prints no JSON)")
+    ap.add_argument("--fixed-cost", action="store_true",
+                    help="only run the fixed-cost sweeps (calls and the streaming-read probe at several "
+                         "sizes, fitted to a + b * bytes) and print them as one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the int4 matvec path here has no multi-GPU "
@@ -715,6 +805,9 @@ def main():
 
     if args.counter_probe:
         counter_probe(q4, torch, dev)
+        return
+    if args.fixed_cost:
+        print(json.dumps({"fixed_cost": fixed_cost(q4, torch, dev, props.multi_processor_count)}), flush=True)
         return
 
     calls, quant, keep = build_workload(q4, torch, dev)
@@ -821,7 +914,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3, 1),
                 "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["alg_bytes"] / dom["us_per_call"] / 1e3 / PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "gemv_reg_kernel<M=1,NCOL=4,kNorm,short rows> (int4_matvec_norm)",
+                "traffic": traffic, "kernel": "gemv_reg_kernel<M=1,NCOL=4,kNorm> (int4_matvec_norm)",
                 "alg_bytes_per_launch": dom["alg_bytes"], "us_per_launch": dom["us_per_call"]}
 
     # The streaming-read ceiling at every call's size, and each call's share of it.
