@@ -680,23 +680,31 @@ template <int NCOL1, int NCOL2>
 __global__ __launch_bounds__(512) void mlp_reg_kernel(GemvArgs gate_up, GemvArgs down, uint32_t* ws) {
   extern __shared__ float part[];
   __shared__ uint32_t stuck;
-  if (threadIdx.x == 0) stuck = __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (stuck != 0u) {
-    // Block b of B fills its share [b n / B, (b + 1) n / B) of each output.
-    const int64_t B = gridDim.x, b = blockIdx.x;
-    const float nan = __builtin_nanf("");
-    for (int64_t i = b * gate_up.N / B + threadIdx.x; i < (b + 1) * gate_up.N / B; i += blockDim.x)
-      gate_up.out[0][i] = nan;
-    for (int64_t i = b * down.N / B + threadIdx.x; i < (b + 1) * down.N / B; i += blockDim.x) down.out[0][i] = nan;
-    return;
+  // Wave 0 publishes and polls; it alone needs the epoch.  The timeout word
+  // is loaded with it at the start but examined only after the gated pass,
+  // so the pass does not wait for the load.
+  uint32_t epoch = 0, stuck_word = 0;
+  if (threadIdx.x < 64) {
+    epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    stuck_word = __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // Wave 0 publishes and polls; it alone needs the epoch.
-  uint32_t epoch = 0;
-  if (threadIdx.x < 64) epoch = __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   reg_pass<1, NCOL1, kGated, true>(gate_up, part, InputsReady{});
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores of h have completed
+  if (threadIdx.x == 0) stuck = stuck_word;
   __syncthreads();
+  if (stuck != 0u) {
+    // A wait timed out in an earlier call: no waiting; this block's own
+    // columns of h and of y (the two passes' static column ranges) become
+    // NaN.
+    const float nan = __builtin_nanf("");
+    for (const GemvArgs* a : {&gate_up, &down}) {
+      const int64_t R = (int64_t)gridDim.x * a->rows_per_block;
+      const int64_t b0 = (int64_t)blockIdx.x * a->rows_per_block * a->N / R;
+      const int64_t b1 = ((int64_t)blockIdx.x * a->rows_per_block + a->rows_per_block) * a->N / R;
+      for (int64_t i = b0 + threadIdx.x; i < b1; i += blockDim.x) a->out[0][i] = nan;
+    }
+    return;
+  }
   if (threadIdx.x == 0)
     __hip_atomic_store(ws + kMlpFlags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   reg_pass<1, NCOL2, kPlain, false>(down, part, GridWait{ws, epoch});
