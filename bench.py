@@ -338,6 +338,22 @@ def build_next(q4, torch, dev):
                           lambda s, ids=ids, out=out: q4.int4_embedding_gather(ids, *s, out=out),
                           lambda r: clones(w5, r), wbytes(w5)))
 
+    # Per-layer-embedding rows gathered from a page-locked host table: the
+    # table never enters HBM, so its copies are not rotated; the rows of
+    # every call are different tokens (rotating id sets), and the bytes are
+    # the T rows read over the host link plus ids and output.
+    n7 = synth.NEXT["n7"]
+    i7 = synth.n7_inputs()
+    t7 = i7["table"]
+    for T in n7["Ts"]:
+        out = torch.empty((T, n7["K"]), device=dev)
+        b7 = 4 * T + T * (n7["K"] // 2 + (n7["K"] // n7["gs"]) * 8) + 4 * T * n7["K"]
+        id_sets = lambda r, T=T: [(torch.from_numpy(synth.token_ids(0xC10 + i, T, n7["N"])).to(dev),)
+                                  for i in range(r)]
+        calls.append(Call(f"PLE gather from a pinned host table T={T} {n7['N']}x{n7['K']}", b7,
+                          lambda s, t7=t7, out=out: q4.int4_embedding_gather_host(s[0], *t7, out=out),
+                          id_sets, 16 * 1024 * 1024))
+
     n6 = synth.NEXT["n6"]
     i6 = synth.n6_inputs(max(n6["Ts"]))
     w6 = quantize(i6["W"], n6["gs"])
@@ -621,14 +637,17 @@ PROBE_CALLS = (
     ("lanes M=4 25600x5120", "plain", 25600, 5120, 64, 4),
     ("lanes M=8 25600x5120", "plain", 25600, 5120, 64, 8),
     ("MLP fused 2x14336x4096 + 4096x14336", "mlp", 14336, 4096, 128, 1),
+    ("prefill GEMM T=512 4096x4096", "gemm", 4096, 4096, 128, 512),
+    ("prefill GEMM T=4096 4096x4096", "gemm", 4096, 4096, 128, 4096),
 )
 PROBE_REPS = 5
 PROBE_COPY_BYTES = 1 << 28
 
 
 def counter_probe(q4, torch, dev):
-    """Launches for hardware-counter runs: every call of the step and the fused
-    MLP block, PROBE_REPS times each on rotating weight copies (random codes:
+    """Launches for hardware-counter runs: every call of the step, the fused
+    MLP block and the prefill GEMM (whose prep launch comes first each time),
+    PROBE_REPS times each on rotating weight copies (random codes:
     the bytes a launch moves do not depend on the values), then PROBE_REPS
     plain elementwise copies of PROBE_COPY_BYTES whose bytes are known, used
     to calibrate the FETCH_SIZE / WRITE_SIZE counters.  Prints the dispatch
@@ -661,6 +680,11 @@ def counter_probe(q4, torch, dev):
             a = [vec(K) for _ in range(3)]
             y, r, n = (torch.empty(m, device=dev) for m in (N, K, K))
             fn = lambda w: q4.int4_matvec_norm(*a, 1e-6, *w, y=y, residual_out=r, norm_out=n)
+        elif kind == "gemm":
+            sets = [triplet(N, K, gs) for _ in range(copies)]
+            X, Y = vec(M, K), torch.empty((M, N), device=dev)
+            ws = torch.empty(q4.int4_gemm_workspace_bytes(M, N, K, gs), dtype=torch.uint8, device=dev)
+            fn = lambda w: q4.int4_gemm(X, *w, Y=Y, workspace=ws)
         elif kind == "split4":
             sets = [triplet(N, K, gs) for _ in range(copies)]
             x = vec(K)
@@ -918,12 +942,16 @@ def main():
                 "alg_bytes_per_launch": dom["alg_bytes"], "us_per_launch": dom["us_per_call"]}
 
     # The streaming-read ceiling at every call's size, and each call's share of it.
+    # (Not for the GEMM, bound by the matrix cores, nor for the host-table
+    # gather, whose bytes cross the host link.)
+    def hbm_row(name, v):
+        return "TFLOPs" not in v and "host table" not in name
     ceiling = stream_read_ceiling(q4, torch, dev, [v["alg_bytes"] for v in per_call.values()]
-                                  + [v["alg_bytes"] for v in next_rows.values() if "TFLOPs" not in v],
+                                  + [v["alg_bytes"] for k, v in next_rows.items() if hbm_row(k, v)],
                                   props.multi_processor_count)
     for rows in (per_call, next_rows):
-        for v in rows.values():
-            if v["alg_bytes"] in ceiling and "TFLOPs" not in v:
+        for k, v in rows.items():
+            if v["alg_bytes"] in ceiling and hbm_row(k, v):
                 v["stream_read_us"] = ceiling[v["alg_bytes"]]["us"]
                 v["pct_of_stream_read"] = round(100 * ceiling[v["alg_bytes"]]["us"] / v["us_per_call"], 1)
 

@@ -295,6 +295,24 @@ int int4_embedding_gather(const int32_t* ids, int64_t T, const uint32_t* q, cons
                           float* out, void* stream);
 
 /*
+ * The same gather with the table kept in page-locked host memory
+ * ([P1] setPleSource / streamPleRows: the per-layer-embedding table,
+ * [vocab, L*256] int4 and about 1.2 GB for its model, stays off the GPU, and
+ * each step only the rows of the input tokens are gathered and dequantized).
+ * q, scales and zeros are host pointers into memory allocated with
+ * hipHostMalloc (mapped for the device); the kernel reads the T rows over
+ * the host link and dequantizes them on the GPU, so only T * (K/2 +
+ * (K/gs) * 8) bytes cross it, and no host thread dequantizes anything.
+ * ids (int32, T) and out ([T][K] fp32, 16-byte aligned) are device memory.
+ * Results are bit-identical to int4_embedding_gather on the same table.
+ * Table pointers that are not page-locked host memory are refused with
+ * INT4_ERR_ARG before any launch (a kernel cannot read pageable memory).
+ */
+int int4_embedding_gather_host(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                               const float* zeros, int64_t N, int64_t K, int32_t group_size, float* out,
+                               void* stream);
+
+/*
  * Prefill GEMM: Y[t][n] = sum_k X[t][k] * w[n][k] for T tokens at once
  * ([P1] the prefill path runs a tiled matmul for any number of rows, decode
  * the K-parallel matvec).  Same weights, layouts and tolerance as

@@ -24,7 +24,7 @@ __all__ = [
     "int4_matvec_gated", "int4_matvec_norm", "int4_matvec_dual", "int4_matvec_sigmoid_gated",
     "int4_matvec_swiglu_gated", "int4_matvec_norm_swiglu", "int4_embedding_gather", "int4_gemm",
     "int4_gemm_workspace_bytes", "int4_matvec_gated_lanes", "int4_mlp", "int4_mlp_workspace_bytes",
-    "int4_mlp_timed_out",
+    "int4_mlp_timed_out", "int4_embedding_gather_host",
     "int4_gemm_noalloc", "INT4_GEMM_NOALLOC_SCRATCH_BYTES", "int4_probe_stream_read", "lib", "LIB_PATH",
 ]
 
@@ -57,6 +57,8 @@ lib.int4_matvec_swiglu_gated.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i64, _i
 lib.int4_matvec_norm_swiglu.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i64, _i64, _i32, _vp, _vp, _vp]
 lib.int4_embedding_gather.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_embedding_gather_host.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+lib.int4_embedding_gather_host.restype = ctypes.c_int
 lib.int4_matvec_gated_lanes.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
 lib.int4_matvec_gated_lanes.restype = ctypes.c_int
 lib.int4_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
@@ -324,6 +326,43 @@ def int4_embedding_gather(ids: torch.Tensor, q, scales, zeros, out=None, stream=
         raise ValueError(f"out must hold T*K = {T * K} floats")
     _check(lib.int4_embedding_gather(_ptr(ids), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs,
                                      _ptr(out), _stream(stream)))
+    return out
+
+
+def _pinned(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError(f"{name} must be a page-locked host tensor (pin_memory=True)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def int4_embedding_gather_host(ids: torch.Tensor, q, scales, zeros, out=None, stream=None) -> torch.Tensor:
+    """As int4_embedding_gather, with the table (q, scales, zeros) in page-locked
+    host memory: only the T gathered rows cross the host link, and the GPU
+    dequantizes them.  ids int32 [T] and out float32 [T, K] are device tensors."""
+    _pinned(q, "q", _CODES)
+    _pinned(scales, "scales", _F32)
+    _pinned(zeros, "zeros", _F32)
+    if q.dim() != 2 or scales.dim() != 2 or scales.shape != zeros.shape or scales.shape[0] != q.shape[0]:
+        raise ValueError("q must be [N, K/8] and scales/zeros [N, K/gs]")
+    N, K = q.shape[0], q.shape[1] * 8
+    G = scales.shape[1]
+    if G == 0 or K % G:
+        raise ValueError(f"K={K} is not a multiple of the group count {G}")
+    gs = K // G
+    _dev(ids, "ids", (torch.int32,))
+    T = ids.numel()
+    out = torch.empty((T, K), dtype=torch.float32, device=ids.device) if out is None else out
+    _dev(out, "out", _F32)
+    if out.numel() != T * K:
+        raise ValueError(f"out must hold T*K = {T * K} floats")
+    _check(lib.int4_embedding_gather_host(_ptr(ids), T, _ptr(q), _ptr(scales), _ptr(zeros), N, K, gs,
+                                          _ptr(out), _stream(stream)))
     return out
 
 

@@ -947,6 +947,56 @@ int int4_embedding_gather(const int32_t* ids, int64_t T, const uint32_t* q, cons
   return ok();
 }
 
+// The device-side address of a table in page-locked host memory (hipHostMalloc,
+// mapped into the device's address space); anything else (pageable or device
+// memory) is refused, because a kernel reading pageable memory faults.
+static int host_table_ptr(const void* p, const char* name, const void** dev) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the next call
+    return fail(INT4_ERR_ARG, "%s is not page-locked host memory (allocate it with hipHostMalloc)", name);
+  }
+  if (at.type != hipMemoryTypeHost || !at.devicePointer || !at.hostPointer)
+    return fail(INT4_ERR_ARG, "%s is not page-locked host memory mapped for the device", name);
+  *dev = static_cast<const char*>(at.devicePointer) +
+         (static_cast<const char*>(p) - static_cast<const char*>(at.hostPointer));
+  return INT4_OK;
+}
+
+int int4_embedding_gather_host(const int32_t* ids, int64_t T, const uint32_t* q, const float* scales,
+                               const float* zeros, int64_t N, int64_t K, int32_t group_size, float* out,
+                               void* stream) {
+  if (N < 0 || T < 0) return fail(INT4_ERR_SHAPE, "N and T must be >= 0 (N=%lld, T=%lld)", (long long)N,
+                                  (long long)T);
+  RETURN_IF(check_kgs(K, group_size));
+  if (T == 0) return ok();
+  if (!ids || !out) return fail(INT4_ERR_NULL, "ids and out are required");
+  if (N > 0 && (!q || !scales || !zeros)) return fail(INT4_ERR_NULL, "q, scales and zeros are required when N > 0");
+  RETURN_IF(check_align(ids, 4, "ids"));
+  RETURN_IF(check_align(q, 4, "q"));
+  RETURN_IF(check_align(scales, 4, "scales"));
+  RETURN_IF(check_align(zeros, 4, "zeros"));
+  RETURN_IF(check_align(out, 16, "out"));
+  if ((uint64_t)T * (uint64_t)K > ((uint64_t)1 << 40))
+    return fail(INT4_ERR_SHAPE, "T*K=%llu is larger than supported", (unsigned long long)T * K);
+  const uint64_t G = (uint64_t)N * (uint64_t)(K / group_size);
+  const Span ins[] = {{ids, (uint64_t)T * 4, "ids"}, {q, (uint64_t)N * K / 2, "q"},
+                      {scales, G * 4, "scales"}, {zeros, G * 4, "zeros"}};
+  const Span outs[] = {{out, (uint64_t)T * K * 4, "out"}};
+  RETURN_IF(check_alias(ins, 4, outs, 1));
+  const void *dq = nullptr, *ds = nullptr, *dz = nullptr;
+  if (N > 0) {
+    RETURN_IF(host_table_ptr(q, "q", &dq));
+    RETURN_IF(host_table_ptr(scales, "scales", &ds));
+    RETURN_IF(host_table_ptr(zeros, "zeros", &dz));
+  }
+  hipError_t e = launch_embedding(ids, T, static_cast<const uint32_t*>(dq), static_cast<const float*>(ds),
+                                  static_cast<const float*>(dz), N, (int32_t)K, group_size, out,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return fail(INT4_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t int4_gemm_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t group_size) {
   if (T <= 0 || N <= 0 || K <= 0 || group_size <= 0) return 0;
   return gemm_layout(T, N, K, group_size).bytes;

@@ -157,6 +157,9 @@ NEXT = {
                N=151936, K=4096, gs=128, Ts=(1, 4096)),
     "n6": dict(name="prefill GEMM T=512 (and 4096) N=4096 K=4096 gs=128", T=512, Ts=(512, 4096),
                N=4096, K=4096, gs=128),
+    "n7": dict(name="per-layer-embedding gather from a page-locked host table [262144, 8960] gs=64 "
+                    "(random codes), T = 1 and 64",
+               N=262144, K=8960, gs=64, Ts=(1, 64)),
 }
 
 
@@ -220,6 +223,29 @@ def token_ids(seed: int, T: int, N: int) -> np.ndarray:
 def n5_inputs(N: int | None = None):
     c = NEXT["n5"]
     return dict(ids=token_ids(0xA01, max(c["Ts"]), c["N"]), W=weights(0xA02, N or c["N"], c["K"]))
+
+
+def ple_table(seed: int, N: int, K: int, group_size: int, pin: bool = True):
+    """A random int4 table (q int32 [N, K/8] of uniform 32-bit words, scales
+    U(1e-3, 1.1e-2) and integer zero points U{0..15} as fp32 [N, K/gs]) drawn
+    from torch's seeded CPU generator straight into page-locked host tensors
+    (pin=True): the per-layer-embedding table's shape without its values,
+    which a gather does not depend on.  Returns (q, scales, zeros)."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    G = K // group_size
+    q = torch.empty((N, K // 8), dtype=torch.int32, pin_memory=pin)
+    s = torch.empty((N, G), dtype=torch.float32, pin_memory=pin)
+    z = torch.empty((N, G), dtype=torch.float32, pin_memory=pin)
+    q.copy_(torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, generator=g))
+    s.copy_(torch.rand((N, G), generator=g) * 1e-2 + 1e-3)
+    z.copy_(torch.randint(0, 16, (N, G), generator=g).to(torch.float32))
+    return q, s, z
+
+
+def n7_inputs():
+    c = NEXT["n7"]
+    return dict(ids=token_ids(0xC01, max(c["Ts"]), c["N"]), table=ple_table(0xC02, c["N"], c["K"], c["gs"]))
 
 
 def n6_inputs(T: int | None = None):

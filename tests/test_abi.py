@@ -313,3 +313,17 @@ def test_mlp_timed_out_validation(lib):
     assert lib.int4_mlp_timed_out(0x100000000, None, None) == NULL
     assert lib.int4_mlp_timed_out(0x100000004, ctypes.byref(out), None) == ALIGN
     assert out.value == 7                    # untouched on an error
+
+
+def test_embedding_gather_host_validation(lib):
+    # Every error below is found before the table pointers are examined (no
+    # runtime call is made).
+    q, s, z, ids, out = (0x100000000 + i * 0x10000000 for i in range(5))
+    N, K, gs, T = 64, 512, 64, 3
+    assert lib.int4_embedding_gather_host(ids, 0, q, s, z, N, K, gs, out, None) == OK        # T == 0
+    assert lib.int4_embedding_gather_host(ids, T, q, s, z, N, K, 48, out, None) == SHAPE
+    assert lib.int4_embedding_gather_host(ids, -1, q, s, z, N, K, gs, out, None) == SHAPE
+    assert lib.int4_embedding_gather_host(None, T, q, s, z, N, K, gs, out, None) == NULL
+    assert lib.int4_embedding_gather_host(ids, T, None, s, z, N, K, gs, out, None) == NULL
+    assert lib.int4_embedding_gather_host(ids, T, q, s, z, N, K, gs, out + 4, None) == ALIGN
+    assert lib.int4_embedding_gather_host(ids, T, q, s, z, N, K, gs, q + 64, None) == ALIAS   # out over q
