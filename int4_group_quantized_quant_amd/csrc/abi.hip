@@ -201,7 +201,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     auto lds_for = [&](int64_t blocks) -> size_t {
       const int64_t t = table(blocks);
       if (t > ((int64_t)1 << 28)) return (size_t)-1;
-      return ((size_t)x_lds_offset((int)t) + (size_t)rows * (size_t)a.K) * sizeof(float);
+      return ((size_t)x_lds_offset((int)t) + (size_t)rows * 32 * (size_t)x_plane_stride(a.U)) * sizeof(float);
     };
     if (lds_for(dev.cus) <= dev.lds_block) {
       a.rows_per_block = P;

@@ -66,9 +66,17 @@ struct GemvArgs {
 
 // Float offset of the staged activations in the register kernel's LDS: after
 // the partial table, one float per wave (at most 16 waves) and one column
-// group counter per chunk (at most 8), rounded up to a float4.  The
-// register kernel's LDS holds x_lds_offset + M*K floats.
+// group counter per chunk (at most 8), rounded up to a float4.
 __host__ __device__ inline int x_lds_offset(int part_floats) { return (part_floats + 24 + 3) & ~3; }
+// The register kernel stages activation float4 i at plane i % 8, position
+// i / 8 (so that lane u later reads its 32 inputs as 8 contiguous-across-
+// lanes float4s).  Planes are x_plane_stride(U) float4s apart, U rounded up
+// to 9 mod 16: the 8 planes a group of consecutive staging writes touches
+// then start in distinct 16-byte bank groups (with 32 or 64 four-byte
+// banks), where a stride of U (a multiple of 16 for U = 128, 160 or 448)
+// would put them all in one.  The LDS after x_lds_offset holds
+// 32 * x_plane_stride(U) floats.
+__host__ __device__ inline int x_plane_stride(int U) { return U + ((9 - U) & 15); }
 
 enum Variant : int {
   kVariantLds = 0,   // activations staged in LDS, one wave per column group

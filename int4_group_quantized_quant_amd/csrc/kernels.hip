@@ -409,6 +409,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   float* scratch = part + a.part_floats;
   uint32_t* claims = reinterpret_cast<uint32_t*>(scratch + 16);
   float4* xl = reinterpret_cast<float4*>(part + x_lds_offset(a.part_floats));
+  const int xs = x_plane_stride(a.U);  // float4s between staging planes
   const int n4 = a.K >> 2;
 
   // The block's weight streams (scalar buffer resources from its first
@@ -438,7 +439,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   };
   auto put_lds = [&](int j, float4 v) {
     const int i = (int)threadIdx.x + j * bd;
-    if (i < n4) xl[(i & 7) * a.U + (i >> 3)] = v;
+    if (i < n4) xl[(i & 7) * xs + (i >> 3)] = v;
   };
   constexpr int kStageMax = 8;
   if constexpr (kWaits) {
@@ -446,7 +447,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
     inputs_ready();
     const auto rx = row_rsrc(a.x);
     for (int i = threadIdx.x; i < n4; i += bd)
-      xl[(i & 7) * a.U + (i >> 3)] = __builtin_bit_cast(
+      xl[(i & 7) * xs + (i >> 3)] = __builtin_bit_cast(
           float4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)i * 16u, 0, kLoadDeviceCoherent));
   } else if constexpr (mode_has_norm(MODE)) {
     const auto ra = row_rsrc(a.x), rb = row_rsrc(a.x2), rg = row_rsrc(a.w_norm);
@@ -475,7 +476,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
           ssq = fmaf(r.z, r.z, ssq);
           ssq = fmaf(r.w, r.w, ssq);
           if (blockIdx.x == 0 && a.residual_out) reinterpret_cast<float4*>(a.residual_out)[i] = r;
-          xl[(i & 7) * a.U + (i >> 3)] =
+          xl[(i & 7) * xs + (i >> 3)] =
               make_float4(r.x * vg[j].x, r.y * vg[j].y, r.z * vg[j].z, r.w * vg[j].w);
         }
       }
@@ -512,7 +513,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
   __syncthreads();
   float x[32];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) put4(x, j, active ? xl[j * a.U + u] : make_float4(0.f, 0.f, 0.f, 0.f));
+  for (int j = 0; j < 8; ++j) put4(x, j, active ? xl[j * xs + u] : make_float4(0.f, 0.f, 0.f, 0.f));
 
   const bool writer = V >= 4 ? (lane & 15) == 0 : (V == 2 ? (lane & 31) == 0 : lane == 0);
   // Compute the group starting at block column n0 from the loaded step r.
@@ -590,7 +591,7 @@ __device__ __forceinline__ void reg_pass(const GemvArgs& a, float* part, Ready i
     inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
     if (blockIdx.x == 0 && a.norm_out) {
       for (int i = threadIdx.x; i < n4; i += bd) {
-        const float4 v = xl[(i & 7) * a.U + (i >> 3)];
+        const float4 v = xl[(i & 7) * xs + (i >> 3)];
         reinterpret_cast<float4*>(a.norm_out)[i] = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
       }
     }
