@@ -37,15 +37,35 @@ namespace {
 
 constexpr int kTile = 128;      // rows of a block tile
 constexpr int kStageK = 64;     // inputs per LDS stage
-// LDS stage layout: planes of 128 rows (or columns) x 16 bytes, plane stride
-// 516 dwords (4 pad).  A fragment read (16 consecutive rows of one plane per
-// quarter-wave) is contiguous; a plane-crossing write of 8 lanes lands on
-// 8 distinct bank quads.
-constexpr int kPlane = kTile * 4 + 4;
-constexpr int kAPlanes = 16;    // 8-input block b of the stage: plane 2b (hi), 2b + 1 (lo)
+// LDS stage layout: planes of 128 rows (or BN columns) x 16 bytes.  A
+// 16-byte LDS access of a wave runs in 16-lane cycles over the 64 banks (16
+// quads of 16 bytes); by the bank-conflict counter on this chip, lanes 0-7
+// share a cycle with lanes 24-31 and lanes 8-15 with lanes 16-23 (likewise
+// in the upper half), and a cycle whose 16 lanes hit 16 distinct quads costs
+// no extra cycle.  A fragment read has each quarter-wave read 16 consecutive
+// rows of its own plane, and a stage write has 8 lanes write 8 planes of one
+// row (activations) or 2-4 planes of a few columns (B).  Two devices keep
+// both kinds on distinct quads:
+//  * some planes start 128 bytes (8 quads) past a 256-byte boundary: the lo
+//    activation plane of each 8-input block, and the B planes of the
+//    stage's second 32-input step;
+//  * within an aligned run of 16 rows (columns) the slots are permuted by an
+//    XOR with a constant below 8 that depends only on the quarter-wave that
+//    reads the plane (a_slot, b_slot), so each lane's read address is one
+//    per-lane base plus compile-time offsets.
+// Activation block b (planes 2b = hi, 2b + 1 = lo) takes kAPair dwords: hi
+// at 0, lo at kALo (2176 bytes, 128 past a 256-byte boundary).
+constexpr int kAPair = 2 * kTile * 4 + 64;
+constexpr int kALo = kTile * 4 + 32;
+constexpr int kABlocks = 8;     // 8-input blocks of a stage (planes 2b = hi, 2b + 1 = lo)
 constexpr int kBPlanes = 8;     // B fragment of code word w of the stage: plane w
-constexpr int kAWords = kAPlanes * kPlane;
+constexpr int kAWords = kABlocks * kAPair;
 constexpr int kThreads = 512;   // 8 waves, 2 per SIMD
+
+// Dword offset of row r of activation plane (block b, half hl) in a stage.
+__device__ __forceinline__ int a_slot(int b, int hl, int r) {
+  return b * kAPair + hl * kALo + (r ^ (2 * (b & 3))) * 4;
+}
 
 // hi and lo of two binary32 values as fp16 pairs, both rounded toward zero.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
@@ -170,8 +190,12 @@ struct TileShape {
   static constexpr int WC = BN / 64;
   static constexpr int WR = 8 / WC;
   static constexpr int RW = 128 / WR / 16;         // 16-row MFMA tiles per wave
-  static constexpr int BPlane = BN * 4 + 4;        // dwords per B-fragment plane
-  static constexpr int BWords = kBPlanes * BPlane;
+  static constexpr int BPlane = BN * 4;            // dwords per B-fragment plane
+  static constexpr int BWords = kBPlanes * BPlane + 32;
+  // Dword offset of column c of B plane p (planes 4-7 shifted 128 bytes).
+  static __device__ __forceinline__ int b_slot(int p, int c) {
+    return p * BPlane + 32 * (p >> 2) + (c ^ (4 * ((p >> 1) & 1))) * 4;
+  }
   static constexpr int SCWords = 2 * BN;           // scales, 2 steps x BN columns
   static constexpr int StageWords = kAWords + BWords + SCWords;
   static constexpr int WPT = BN / 64;              // code words per thread per stage (2 or 4)
@@ -241,6 +265,20 @@ void gemm_int4_kernel(GemmArgs a) {
       (void*)a.q, (short)0, (int)a.qbytes, kBufferWord3);
   const uint32_t qcol_off = (uint32_t)(n0 + wcol) * (uint32_t)(a.K / 2) + (uint32_t)(wrun * TS::WPT * 4);
   const int scstep = (tid / BN) & 1, sccol = tid % BN;
+  // Per-lane parts of the LDS offsets; every access adds only compile-time
+  // (or wave-uniform) terms to them.  The XOR constants are below 8 and the
+  // added row / column terms are multiples of 16, so the terms commute with
+  // the XOR; the plane terms stay the same across the planes an access
+  // spans (b_slot's shift and XOR depend on p >> 2 and (p >> 1) & 1 only).
+  //  * activation store of piece tid & 15 of row tid >> 4 (+ 32 rows per i);
+  const int a_st = a_slot((tid & 15) >> 1, tid & 1, tid >> 4);
+  //  * B stores of words h and h + 1 (h even) of the lane's run;
+  const int b_st0 = TS::b_slot(wrun * TS::WPT, wcol);
+  const int b_st2 = TS::b_slot(wrun * TS::WPT + (TS::WPT > 2 ? 2 : 0), wcol);
+  //  * fragment reads of block 4 ks + q4: rows 16 RW wr + 16 i + l16 and
+  //    columns 64 wc + 16 j + l16.
+  const int a_rd = a_slot(q4, 0, 16 * RW * wr + l16);
+  const int b_rd = TS::b_slot(q4, 64 * wc + l16);
   auto group_of = [&](int kk) -> int64_t {
     if constexpr (GSTEPS == 1) return kk;
     else if constexpr (GSTEPS == 2) return kk >> 1;
@@ -277,11 +315,8 @@ void gemm_int4_kernel(GemmArgs a) {
     uint32_t* sb = sa + kAWords;
     uint32_t* ss = sb + TS::BWords;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c >> 4, piece = c & 15;
-      *reinterpret_cast<u32x4*>(sa + piece * kPlane + row * 4) = p.a[i];
-    }
+    for (int i = 0; i < 4; ++i)  // piece c & 15 of row c >> 4, c = tid + 512 i
+      *reinterpret_cast<u32x4*>(sa + a_st + i * (kThreads / 16) * 4) = p.a[i];
     const half2_t z0 = as_half2(p.zh), z1 = as_half2(p.zh << 4);
 #pragma unroll
     for (int h = 0; h < TS::WPT; ++h) {
@@ -291,7 +326,7 @@ void gemm_int4_kernel(GemmArgs a) {
       bw[1] = __builtin_bit_cast(uint32_t, as_half2(w & 0x00F000F0u) - z1);
       bw[2] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x000F000Fu) - z0);
       bw[3] = __builtin_bit_cast(uint32_t, as_half2(w8 & 0x00F000F0u) - z1);
-      *reinterpret_cast<u32x4*>(sb + (wrun * TS::WPT + h) * TS::BPlane + wcol * 4) = bw;
+      *reinterpret_cast<u32x4*>(sb + (h < 2 ? b_st0 : b_st2) + (h & 1) * TS::BPlane) = bw;
     }
     if (tid < TS::SCWords) ss[tid] = p.sc;
   };
@@ -313,11 +348,10 @@ void gemm_int4_kernel(GemmArgs a) {
     u32x4 bf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const u32x4*>(sb + (ks * 4 + q4) * TS::BPlane + (64 * wc + 16 * j + l16) * 4);
+      bf[j] = *reinterpret_cast<const u32x4*>(sb + b_rd + ks * (4 * TS::BPlane + 32) + 64 * j);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const uint32_t* pa = sa + 2 * (ks * 4 + q4) * kPlane + (16 * RW * wr + 16 * i + l16) * 4;
-      const u32x4 ah = *reinterpret_cast<const u32x4*>(pa);
+      const u32x4 ah = *reinterpret_cast<const u32x4*>(sa + a_rd + 4 * ks * kAPair + 64 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ah),
@@ -326,8 +360,7 @@ void gemm_int4_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const uint32_t* pa = sa + 2 * (ks * 4 + q4) * kPlane + (16 * RW * wr + 16 * i + l16) * 4;
-      const u32x4 al = *reinterpret_cast<const u32x4*>(pa + kPlane);
+      const u32x4 al = *reinterpret_cast<const u32x4*>(sa + a_rd + 4 * ks * kAPair + kALo + 64 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al),
