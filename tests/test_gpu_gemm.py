@@ -1,7 +1,8 @@
 """GPU parity of the prefill GEMM (int4_gemm) against the oracle's matvec of
 all T rows: ragged T, N and K (a pad half-stage when K % 64 == 32), group
 sizes 32 to 128 and 96, integer problems that must come out exact, rows of
-very different magnitudes, and the full workload size on sampled outputs."""
+very different magnitudes, rows longer than 4096 inputs, and the full
+workload size on sampled outputs."""
 import numpy as np
 import pytest
 
@@ -131,6 +132,27 @@ def test_gemm_wide_tiles(q4, T, N, K, gs):
     Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
     Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
     assert_dot_close(Y, Y_ref, B, f"gemm wide T={T} N={N} K={K} gs={gs}")
+
+
+@pytest.mark.parametrize("T,N,K,gs", [(300, 260, 14336, 128), (1030, 130, 5120, 64)])
+def test_gemm_long_rows(q4, T, N, K, gs):
+    # K > 4096: the prep reads a row twice (its maximum, then the split)
+    # instead of holding it in registers; the first case runs 128 x 128
+    # tiles over 224 stages, the second 128 x 256 tiles over 80.
+    q, s, z = quantized(0x6700 + T, N, K, gs)
+    X = synth.lanes(0x6701 + T, T, K)
+    Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
+    Y_ref, B = oracle.matvec(X, q, s, z, K, gs)
+    assert_dot_close(Y, Y_ref, B, f"gemm long rows T={T} N={N} K={K} gs={gs}")
+
+
+def test_gemm_long_rows_integer_exact(q4):
+    # Partial sums stay below 2^24 (K * 8 * 15 < 2^24), so any order is exact.
+    rng = np.random.default_rng(0x6800)
+    T, N, K, gs = 130, 70, 8192, 128
+    q, s, z, X, exact = integer_problem(rng, N, K, gs, M=T)
+    Y = host(q4.int4_gemm(*to_dev(X, q.view(np.int32), s, z)))
+    np.testing.assert_array_equal(Y, exact.astype(np.float32))
 
 
 def test_gemm_wide_tiles_integer_exact(q4):
