@@ -235,10 +235,9 @@ void gemm_int4_kernel(GemmArgs a) {
   const int part = (int)(rem - cb * a.S);
   const int64_t m0 = rb * kTile, n0 = cb * BN;
   const int nst_all = a.Kp / kStageK;
-  // Sums are closed once per stage when a stage never straddles a group
-  // (GSTEPS 2, and GSTEPS 4 on the wide tile, where the second register
-  // set of a group spanning two stages would not fit); otherwise per group.
-  constexpr bool kStageFlush = GSTEPS == 2 || (GSTEPS == 4 && BN == 256);
+  // Sums are closed once per stage when a group is one stage (GSTEPS 2);
+  // otherwise once per group.
+  constexpr bool kStageFlush = GSTEPS == 2;
   // K parts cover whole groups when a group's sums span two stages.
   int per = (nst_all + a.S - 1) / a.S;
   if (GSTEPS == 4 && !kStageFlush) per = (per + 1) & ~1;
@@ -379,15 +378,16 @@ void gemm_int4_kernel(GemmArgs a) {
     }
   };
   // A stage is two steps.  For GSTEPS 1 and 2 the group ends are fixed per
-  // step; GSTEPS 4 spans a stage pair (PHASE: the stage's place in it); the
-  // general case tests the step index, and every case closes the sums at
-  // the part's last step.
-  auto compute = [&](int slot, int st, int phase) {
+  // step; GSTEPS 4 spans a stage pair (PHASE: the stage's place in it, the
+  // parity of its index in the part); the general case tests the step index,
+  // and every case closes the sums at the part's last step.  With GSTEPS 4,
+  // K is a multiple of 128 and a part an even number of stages, so a part
+  // ends on phase 1.  Inlined: as a call it spills.
+  auto compute = [&](int slot, int st, int phase) __attribute__((always_inline)) {
     const uint32_t* sa = lds + slot * TS::StageWords;
     const uint32_t* sb = sa + kAWords;
     const uint32_t* ss = sb + TS::BWords;
     const int kk = 2 * st;
-    const bool end_part = kk + 1 == last_step;
     if constexpr (GSTEPS == 1) {
       step(sa, sb, ss, 0, true, true);
       step(sa, sb, ss, 1, true, true);
@@ -397,8 +397,7 @@ void gemm_int4_kernel(GemmArgs a) {
     } else if constexpr (GSTEPS == 4) {
       if (phase == 0) {
         step(sa, sb, ss, 0, true, false);
-        if (end_part) step(sa, sb, ss, 1, false, true);
-        else step(sa, sb, ss, 1, false, false);
+        step(sa, sb, ss, 1, false, false);
       } else {
         step(sa, sb, ss, 0, false, false);
         step(sa, sb, ss, 1, false, true);
