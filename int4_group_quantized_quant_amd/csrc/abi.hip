@@ -264,7 +264,7 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
     int64_t B = (int64_t)dev.cus * bpc / nstreams;
     if (B > tiles) B = tiles;
     if (B < 1) B = 1;
-    const int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
+    int64_t tiles_per_block = ((N + B - 1) / B + 15) / 16;
     const size_t budget = dev.lds_cu / (size_t)bpc < dev.lds_block ? dev.lds_cu / (size_t)bpc : dev.lds_block;
     const int nv = mode == kGated ? 2 : 1;  // both streams of a tile in one block
     const size_t fixed = slice_lds_bytes(su, cls, a.G, W, 0, nv);
@@ -273,6 +273,12 @@ int plan(Mode mode, GemvArgs& a, LaunchShape* s) {
       return fail(INT4_ERR_SHAPE, "matrix-core lanes need %zu bytes of LDS per block; %zu available",
                   fixed + per_tile, budget);
     int64_t rt = (int64_t)((budget - fixed) / per_tile);
+    if (rt < tiles_per_block) {
+      // A block runs its tiles in one round: more blocks, of at most 16 * rt
+      // columns each, which then take turns on the CUs.
+      B = (N + 16 * rt - 1) / (16 * rt);
+      tiles_per_block = ((N + B - 1) / B + 15) / 16;
+    }
     if (rt > tiles_per_block) rt = tiles_per_block;
     a.rt = (int32_t)rt;
     a.su = su;

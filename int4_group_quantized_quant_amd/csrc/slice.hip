@@ -38,10 +38,10 @@ namespace {
 // layout (lane (g, col) reads word g of every unit of column col).  Each
 // unit's D is scaled by its group's scale into four accumulators; at the end
 // of the tile the lo rows are added to the hi rows, multiplied by 2^(24 - e)
-// and written to the block's partial table.  After a round of tiles, the
-// block adds the waves' partials in wave order and stores Y.  Every row's
-// arithmetic reads only that row's activations, so a lane's outputs never
-// depend on the other lanes.
+// and written to the block's partial table.  After its tiles (at most RT, a
+// round), the block adds the waves' partials in wave order and stores Y.
+// Every row's arithmetic reads only that row's activations, so a lane's
+// outputs never depend on the other lanes.
 
 
 // One tile of one slice in flight: SU/4 x 16 bytes of codes.
@@ -56,11 +56,10 @@ struct SliceTile {
 // runs both streams over its columns: a round's tiles of stream 0, then of
 // stream 1, and the round's outputs are silu(g) * u).
 // One wave's share of the kernel: slices of SU units starting at units
-// u_first, u_first + u_step, ... below U, over every round of the block's
-// tiles.  SUS is the largest slice size of the launch: it sets the per-wave
-// LDS stage and the table stride, which all waves of a block share.  Every
-// wave runs the same rounds and reaches the same barriers in each, whatever
-// its SU.
+// u_first, u_first + u_step, ... below U, over the block's round of tiles.
+// SUS is the largest slice size of the launch: it sets the per-wave LDS
+// stage and the table stride, which all waves of a block share.  Every wave
+// reaches the same barriers, whatever its SU.
 template <int SU, int SUS, int GS, int DEPTH, int MODE>
 __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int u_first, int u_step) {
   constexpr int NJ = SU / 4;  // load instructions per tile
@@ -113,8 +112,14 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
     st_off[j] = (uint32_t)(col * CS + 4 * t);
   }
 
-  for (int r0 = 0; r0 < ntile; r0 += RT) {
-    const int rn = ntile - r0 < RT ? ntile - r0 : RT;
+  // One round of tiles per block: the planner gives a block at most RT
+  // tiles, with more blocks than the device holds at once where the columns
+  // need more (a loop over rounds here made every launch slower, through
+  // the code it generates, even with one round).  The clamp only keeps the
+  // tables inside the LDS should a launch break that rule.
+  {
+    const int r0 = 0;
+    const int rn = ntile < RT ? ntile : RT;
 
     // The round's scales and zero points.  Its columns [c_lo, c_lo + ncr)
     // are consecutive rows of the [N][G] arrays, so each array is one
@@ -435,7 +440,6 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
         yout[(int64_t)mm * N + col] = y;
       }
     }
-    __syncthreads();
   }
 }
 

@@ -116,10 +116,11 @@ def test_lanes_table_limit(q4):
         q4.int4_matvec(X, qd, sd, zd)
 
 
-def test_lanes_many_rounds(q4):
-    """More tiles per block than the LDS partial table holds (70000 columns at
-    K = 16416: two rounds per block).  Random packed codes, integer zero
-    points; every output is checked."""
+def test_lanes_more_blocks_than_resident(q4):
+    """More tiles than one block per CU can hold in its LDS tables (70000
+    columns at K = 16416): the grid then has more blocks than the device runs
+    at once, each with the tiles its tables hold.  Random packed codes,
+    integer zero points; every output is checked."""
     rng = np.random.default_rng(0xB700)
     N, K, gs, M = 70000, 16416, 32, 3
     q = rng.integers(0, 2**32, (N, K // 8), dtype=np.uint32)
