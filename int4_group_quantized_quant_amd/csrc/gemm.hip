@@ -419,47 +419,27 @@ void gemm_int4_kernel(GemmArgs a) {
   // Two register prefetch sets: the loads of stage st + 2 are issued while
   // stage st is computed, and stage st + 1 (loaded one iteration earlier)
   // is written to the other LDS slot after it.  Past the part's last stage
-  // the loads re-read it, so the count in flight is fixed.
+  // the loads re-read it, so the count in flight is fixed.  (The wide tile
+  // once kept one set, loading one stage ahead, for register room; with its
+  // sums closed once per group both sets fit, and it runs 5% faster.)
   auto clamp = [&](int x) { return x < st_end ? x : st_end - 1; };
-  if constexpr (BN == 128) {
-    Prefetch<BN> p0, p1;
-    load_stage(st_begin, p0);
-    load_stage(clamp(st_begin + 1), p1);
+  Prefetch<BN> p0, p1;
+  load_stage(st_begin, p0);
+  load_stage(clamp(st_begin + 1), p1);
+  store_stage(0, p0);
+  __syncthreads();
+  int st = st_begin;
+  while (true) {
+    load_stage(clamp(st + 2), p0);
+    compute(0, st, 0);
+    store_stage(1, p1);
+    __syncthreads();
+    if (++st >= st_end) break;
+    load_stage(clamp(st + 2), p1);
+    compute(1, st, 1);
     store_stage(0, p0);
     __syncthreads();
-    int st = st_begin;
-    while (true) {
-      load_stage(clamp(st + 2), p0);
-      compute(0, st, 0);
-      store_stage(1, p1);
-      __syncthreads();
-      if (++st >= st_end) break;
-      load_stage(clamp(st + 2), p1);
-      compute(1, st, 1);
-      store_stage(0, p0);
-      __syncthreads();
-      if (++st >= st_end) break;
-    }
-  } else {
-    // The wide tile holds twice the accumulators: one register set, loads
-    // one stage ahead (a stage's products take twice as long to hide them).
-    Prefetch<BN> p0;
-    load_stage(st_begin, p0);
-    store_stage(0, p0);
-    __syncthreads();
-    int st = st_begin;
-    while (true) {
-      load_stage(clamp(st + 1), p0);
-      compute(0, st, 0);
-      store_stage(1, p0);
-      __syncthreads();
-      if (++st >= st_end) break;
-      load_stage(clamp(st + 1), p0);
-      compute(1, st, 1);
-      store_stage(0, p0);
-      __syncthreads();
-      if (++st >= st_end) break;
-    }
+    if (++st >= st_end) break;
   }
 
   // Y = total * 2^(24 - e_t); with K split in two, the two halves are added
