@@ -386,3 +386,33 @@ def test_gated_lanes_table_limit(q4):
     assert_dot_close(Y, Y_ref, B, "plain lanes at 512 groups")
     with pytest.raises(q4.Int4Error):
         q4.int4_matvec_gated_lanes(Xd, qd, sd, zd, qd, sd, zd)
+
+
+def test_lanes_variants_more_blocks_than_resident(q4):
+    """Dual and gated lanes whose columns need more tiles than one block per
+    CU holds in its LDS tables (9000 columns, 256 groups of 32 per column):
+    the grid then has more blocks than the device runs at once.  Every
+    output is checked against the oracle, and each stream's sums against
+    int4_matvec at the same M."""
+    N, K, gs, M = 9000, 8192, 32, 3
+    q0, s0, z0 = quantized(0xFC00, N, K, gs)
+    q1, s1, z1 = quantized(0xFC01, N, K, gs)
+    X = synth.lanes(0xFC02, M, K)
+    Xd, *w = to_dev(X, q0.view(np.int32), s0, z0, q1.view(np.int32), s1, z1)
+    y0, y1 = q4.int4_matvec_dual(Xd, *w)
+    y0, y1 = host(y0), host(y1)
+    H = host(q4.int4_matvec_gated_lanes(Xd, *w))
+    for m in range(M):
+        ref = oracle.dual(X[m], q0, s0, z0, q1, s1, z1, K, gs)
+        assert_dot_close(y0[m], ref["y0"], ref["b0"], f"dual lanes y0 m={m}")
+        assert_dot_close(y1[m], ref["y1"], ref["b1"], f"dual lanes y1 m={m}")
+        rg = oracle.gated(X[m], q0, s0, z0, q1, s1, z1, K, gs)
+        err = np.abs(H[m].astype(np.float64) - rg["h"])
+        assert np.all(err <= gated_tolerance(rg)), f"gated lanes m={m}"
+    g = host(q4.int4_matvec(Xd, *w[:3]))
+    u = host(q4.int4_matvec(Xd, *w[3:]))
+    np.testing.assert_array_equal(bits(y0), bits(g))
+    np.testing.assert_array_equal(bits(y1), bits(u))
+    g = g.astype(np.float64)
+    u = u.astype(np.float64)
+    assert close_ulps(H, g / (1.0 + np.exp(-g)) * u)
