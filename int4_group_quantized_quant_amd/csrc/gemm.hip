@@ -419,9 +419,9 @@ void gemm_int4_kernel(GemmArgs a) {
   // Two register prefetch sets: the loads of stage st + 2 are issued while
   // stage st is computed, and stage st + 1 (loaded one iteration earlier)
   // is written to the other LDS slot after it.  Past the part's last stage
-  // the loads re-read it, so the count in flight is fixed.  (The wide tile
-  // once kept one set, loading one stage ahead, for register room; with its
-  // sums closed once per group both sets fit, and it runs 5% faster.)
+  // the loads re-read it, so the count in flight is fixed.  Both tile widths
+  // hold the two sets: closing the sums once per group (not per stage)
+  // leaves the wide tile the registers for them (252 VGPRs, no scratch).
   auto clamp = [&](int x) { return x < st_end ? x : st_end - 1; };
   Prefetch<BN> p0, p1;
   load_stage(st_begin, p0);

@@ -114,9 +114,9 @@ __device__ __forceinline__ void slice_wave(const GemvArgs& a, float4* lds4, int 
 
   // One round of tiles per block: the planner gives a block at most RT
   // tiles, with more blocks than the device holds at once where the columns
-  // need more (a loop over rounds here made every launch slower, through
-  // the code it generates, even with one round).  The clamp only keeps the
-  // tables inside the LDS should a launch break that rule.
+  // need more (a loop over rounds here costs every launch time, through the
+  // code generated around it, even when it runs once).  The clamp only keeps
+  // the tables inside the LDS should a launch break that rule.
   {
     const int r0 = 0;
     const int rn = ntile < RT ? ntile : RT;
